@@ -1,0 +1,212 @@
+"""Benchmark of the paged-attention decode step at Llama-2-13B shape on one GPU.
+
+One step = reshape_and_cache of the 256 newest tokens, then paged decode of
+256 sequences (40 query heads = 40 kv heads, head_dim 128, bf16 cache, block
+size 16, lognormal context lengths with median 1024 clipped to [16, 4096],
+65536-block shuffled pool) with split-K partitions and their merge.  Inputs are
+seeded synthetic data already resident in GPU memory before timing starts.
+
+Prints one JSON line: KV GB/s over the whole step (the metric), % of the 8 TB/s
+HBM peak, tokens/s for one layer, the decode kernel's roofline position
+(algorithmic KV bytes / its own launch time, from HIP events on the launch
+stream), and the fp64 CPU oracle timed on a sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged-attn decode KV GB/s (% of HBM peak) + tokens/s at Llama-2-13B shape"
+COUNTERS = os.path.join(ROOT, "profiles", "decode_llama13b_counters.json")
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_453_amd", "csrc", "decode.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    with open(DECODE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(per_launch_algo_bytes: float):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, or None
+    when they are missing or were taken on a different decode kernel source."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("decode_source_sha256_16") != source_digest():
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float = 10.0):
+    """The fp64 oracle on the first sequences of the same workload, one thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from workloads import accounting
+
+    k, v = oracle.reshape_and_cache(w.k_host, w.v_host, w.new_k, w.new_v, w.host_slots())
+    g = w.decode
+    tables = w.host_tables(g.block_tables)
+    done, t_total = 0, 0.0
+    with threadpool_limits(1):
+        while done < g.num_seqs and t_total < budget_s:
+            hi = min(g.num_seqs, done + 8)
+            t0 = time.perf_counter()
+            oracle.decode(g.query[done:hi], k, v, tables[done:hi], g.context_lens[done:hi], w.scale,
+                          w.dtype)
+            t_total += time.perf_counter() - t0
+            done = hi
+    kv = accounting.decode_kv_bytes(g.context_lens[:done], w.num_kv_heads, w.head_dim,
+                                    w.elem_bytes)
+    return {"value": round(kv / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 numpy oracle decode (scatter excluded) of the first {done} of "
+                      f"{g.num_seqs} sequences, {int(g.context_lens[:done].sum())} tokens, "
+                      f"{t_total:.1f} s on 1 host thread"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--partition-size", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the paged-attention step runs on a single "
+              "device; run it with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from paged_kv_cache_453_amd import lib
+    from workloads import accounting, config2
+    from workloads.device import to_device
+
+    lib.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ps = args.partition_size
+
+    log("bench: generating the Llama-2-13B-shaped decode workload")
+    t0 = time.time()
+    w = config2(partition_size=ps)
+    g = w.decode
+    log(f"bench: generated in {time.time() - t0:.1f} s; uploading")
+    dw = to_device(w, device=dev)
+    dg = dw.decode
+    ws_bytes = lib.pa_decode_workspace_bytes(g.num_seqs, w.num_heads, w.head_dim,
+                                             g.max_context_len, ps)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        lib.pa_reshape_and_cache(dw.new_k, dw.new_v, dw.k_cache, dw.v_cache, dw.slot_mapping)
+        if ev is not None:
+            ev[1].record(stream)
+        lib.pa_decode(dg.out, dg.query, dw.k_cache, dw.v_cache, dg.block_tables, dg.context_lens,
+                      w.scale, g.max_context_len, ps, ws if ps else None)
+        if ev is not None:
+            ev[2].record(stream)
+        if ps:
+            lib.pa_decode_splitk_reduce(dg.out, ws, dg.context_lens, g.max_context_len, ps)
+        if ev is not None:
+            ev[3].record(stream)
+
+    log(f"bench: warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # whole-step timing
+    log(f"bench: timing {args.steps} steps")
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(stop) / args.steps
+
+    # per-kernel launch durations over a second timed pass, events on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    scatter_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    decode_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    reduce_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    log(f"bench: step {ms_per_step * 1e3:.1f} us (scatter {scatter_ms * 1e3:.1f}, decode "
+        f"{decode_ms * 1e3:.1f}, reduce {reduce_ms * 1e3:.1f})")
+
+    kv = accounting.decode_kv_bytes(g.context_lens, w.num_kv_heads, w.head_dim, w.elem_bytes)
+    gbs = kv / (ms_per_step * 1e-3) / 1e9
+    decode_gbs = kv / (decode_ms * 1e-3) / 1e9
+    traffic = measured_traffic(kv)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a sample")
+        cpu = cpu_baseline(w)
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(g.num_seqs / (ms_per_step * 1e-3), 1),
+        "tokens_per_s_note": "one decode token per sequence per step, one attention layer",
+        "kv_bytes_per_step": int(kv),
+        "kernel_us": {"reshape_and_cache": round(scatter_ms * 1e3, 2),
+                      "decode": round(decode_ms * 1e3, 2),
+                      "splitk_reduce": round(reduce_ms * 1e3, 2)},
+        "config": {"workload": "llama2-13b-shaped paged decode (scatter + decode + split-K merge)",
+                   "num_seqs": g.num_seqs, "num_heads": w.num_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": 16,
+                   "context_lens": "lognormal median 1024 sigma 0.5 clipped [16,4096]",
+                   "total_context_tokens": int(g.context_lens.sum()),
+                   "num_blocks": w.num_blocks, "partition_size": ps, "seed": 455},
+        "roofline": {"bound": "hbm", "achieved": round(decode_gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(decode_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "decode_valu_kernel<bf16,128,1>",
+                     "algorithmic_bytes_per_launch": int(kv)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

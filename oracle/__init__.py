@@ -4,7 +4,7 @@ TEST INFRASTRUCTURE ONLY: imported by tests/, by the package smoke check and by
 the benchmark's CPU-baseline leg, never by the product path.
 """
 from .paged_attention import (to_f64, reshape_and_cache, gather, attend, decode,
-                              decode_partials, merge_partials, prefill, within_tolerance, TOL)
+                              decode_partials, merge_partials, prefill)
 
 __all__ = ["to_f64", "reshape_and_cache", "gather", "attend", "decode", "decode_partials",
-           "merge_partials", "prefill", "within_tolerance", "TOL"]
+           "merge_partials", "prefill"]

@@ -212,18 +212,3 @@ def prefill(query, k_pool, v_pool, block_tables, query_start_loc, context_lens, 
             kh = h // g
             out[a:b, h] = attend(q64[a:b, h, :], ks[:, kh, :], vs[:, kh, :], scale, visible)
     return out
-
-
-# --------------------------------------------------------------------------
-# comparison helper with the tolerances attention is held to
-# --------------------------------------------------------------------------
-TOL = {"f32": (1e-5, 1e-5), "bf16": (4e-3, 1e-2)}
-
-
-def within_tolerance(got, ref, dtype):
-    """|got - ref| <= atol + rtol*|ref| elementwise; NaN never passes."""
-    atol, rtol = TOL[dtype]
-    got = np.asarray(got, dtype=np.float64)
-    err = np.abs(got - ref)
-    ok = err <= atol + rtol * np.abs(ref)
-    return bool(ok.all()), float(np.nanmax(err) if err.size else 0.0), int((~ok).sum())

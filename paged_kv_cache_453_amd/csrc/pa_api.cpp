@@ -1,0 +1,208 @@
+// C ABI of the paged-attention library: argument checks, kernel choice, launch.
+//
+// Every scalar and pointer argument is checked here, on the host, before any
+// HIP call; a bad argument returns a negative pa_status and launches nothing.
+// Launches go to the caller's stream; nothing here allocates or synchronises.
+#include <limits.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pa.h"
+#include "pa_launch.h"
+
+namespace {
+
+constexpr int kBlockSize = 16;
+constexpr int kMaxGroup = 16;
+constexpr int64_t kMaxGridY = 65535;
+
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+bool dtype_ok(pa_dtype t) { return t == PA_F32 || t == PA_BF16; }
+int elem_bytes(pa_dtype t) { return t == PA_F32 ? 4 : 2; }
+
+int max_partitions(int max_context_len, int partition_size) {
+  if (partition_size <= 0) return 1;
+  const int p = (int)(((int64_t)max_context_len + partition_size - 1) / partition_size);
+  return p > 0 ? p : 1;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "null pointer argument";
+    case PA_ERR_SHAPE: return "invalid or inconsistent size argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported block_size, head_dim, dtype or group size";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int pa_reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,
+                         const int64_t* slot_mapping, int64_t num_tokens, int64_t key_stride,
+                         int64_t value_stride, int num_kv_heads, int head_dim, int block_size,
+                         int64_t num_blocks, pa_dtype dtype, hipStream_t stream) {
+  if (!key_cache || !value_cache) return PA_ERR_NULL;
+  if (num_tokens > 0 && (!key || !value || !slot_mapping)) return PA_ERR_NULL;
+  if (!dtype_ok(dtype) || block_size != kBlockSize || !head_dim_ok(head_dim))
+    return PA_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_tokens > INT32_MAX || num_kv_heads < 1 || num_blocks < 1)
+    return PA_ERR_SHAPE;
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (key_stride < row || value_stride < row) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  pa::ScatterArgs a;
+  a.key = key;
+  a.value = value;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.key_stride = key_stride;
+  a.value_stride = value_stride;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = num_blocks;
+  a.elem_bytes = elem_bytes(dtype);
+  return status_of(pa::launch_reshape_and_cache(a, stream));
+}
+
+size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int max_context_len,
+                                 int partition_size) {
+  if (partition_size <= 0 || num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 ||
+      max_context_len < 0)
+    return 0;
+  const size_t rows = (size_t)num_seqs * (size_t)num_heads *
+                      (size_t)max_partitions(max_context_len, partition_size);
+  return rows * (size_t)head_dim * sizeof(float) + rows * sizeof(float);
+}
+
+int pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+              const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+              int num_heads, int num_kv_heads, int head_dim, int block_size,
+              int max_blocks_per_seq, int64_t num_blocks, int max_context_len, float scale,
+              int partition_size, void* workspace, size_t workspace_bytes, pa_dtype dtype,
+              hipStream_t stream) {
+  if (num_seqs < 0) return PA_ERR_SHAPE;
+  if (num_seqs > 0 && (!out || !query || !key_cache || !value_cache || !block_tables ||
+                       !context_lens))
+    return PA_ERR_NULL;
+  if (!dtype_ok(dtype) || block_size != kBlockSize || !head_dim_ok(head_dim))
+    return PA_ERR_UNSUPPORTED;
+  if (num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads != 0 ||
+      num_kv_heads > kMaxGridY || max_blocks_per_seq < 1 || num_blocks < 1 ||
+      max_context_len < 0 || partition_size < 0 || partition_size % kBlockSize != 0)
+    return PA_ERR_SHAPE;
+  if (num_heads / num_kv_heads > kMaxGroup) return PA_ERR_UNSUPPORTED;
+  const int nparts = max_partitions(max_context_len, partition_size);
+  if (nparts > kMaxGridY) return PA_ERR_SHAPE;
+  if (partition_size > 0) {
+    const size_t need = pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len,
+                                                  partition_size);
+    if (num_seqs > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+  }
+  if (num_seqs == 0) return PA_OK;
+  pa::DecodeArgs a = {};
+  a.out = out;
+  a.query = query;
+  a.k_cache = key_cache;
+  a.v_cache = value_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start_loc = nullptr;
+  const size_t rows = (size_t)num_seqs * num_heads * nparts;
+  a.part_o = partition_size > 0 ? static_cast<float*>(workspace) : nullptr;
+  a.part_lse = partition_size > 0 ? static_cast<float*>(workspace) + rows * head_dim : nullptr;
+  a.num_seqs = num_seqs;
+  a.num_items = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = num_heads / num_kv_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.max_context_len = max_context_len;
+  a.partition_blocks = partition_size / kBlockSize;
+  a.max_partitions = nparts;
+  a.max_query_len = 1;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return status_of(pa::launch_decode(a, head_dim, dtype == PA_BF16, stream));
+}
+
+int pa_decode_splitk_reduce(void* out, const void* workspace, size_t workspace_bytes,
+                            const int32_t* context_lens, int num_seqs, int num_heads,
+                            int head_dim, int max_context_len, int partition_size,
+                            pa_dtype out_dtype, hipStream_t stream) {
+  if (num_seqs < 0) return PA_ERR_SHAPE;
+  if (num_seqs > 0 && (!out || !context_lens)) return PA_ERR_NULL;
+  if (!dtype_ok(out_dtype) || !head_dim_ok(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (num_heads < 1 || num_heads > kMaxGridY || max_context_len < 0 || partition_size <= 0 ||
+      partition_size % kBlockSize != 0)
+    return PA_ERR_SHAPE;
+  const size_t need =
+      pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, partition_size);
+  if (num_seqs > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+  if (num_seqs == 0) return PA_OK;
+  const int nparts = max_partitions(max_context_len, partition_size);
+  const size_t rows = (size_t)num_seqs * num_heads * nparts;
+  pa::ReduceArgs a;
+  a.out = out;
+  a.part_o = static_cast<const float*>(workspace);
+  a.part_lse = static_cast<const float*>(workspace) + rows * head_dim;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.max_partitions = nparts;
+  a.partition_tokens = partition_size;
+  a.max_context_len = max_context_len;
+  return status_of(pa::launch_splitk_reduce(a, head_dim, out_dtype == PA_BF16, stream));
+}
+
+int pa_prefill_chunk(void* out, const void* query, const void* key_cache, const void* value_cache,
+                     const int32_t* block_tables, const int32_t* query_start_loc,
+                     const int32_t* context_lens, int num_seqs, int num_query_tokens,
+                     int num_heads, int num_kv_heads, int head_dim, int block_size,
+                     int max_blocks_per_seq, int64_t num_blocks, int max_query_len, float scale,
+                     pa_dtype dtype, hipStream_t stream) {
+  if (num_seqs < 0 || num_query_tokens < 0 || max_query_len < 0) return PA_ERR_SHAPE;
+  if (num_seqs > 0 && (!out || !query || !key_cache || !value_cache || !block_tables ||
+                       !query_start_loc || !context_lens))
+    return PA_ERR_NULL;
+  if (!dtype_ok(dtype) || block_size != kBlockSize || !head_dim_ok(head_dim))
+    return PA_ERR_UNSUPPORTED;
+  if (num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads != 0 ||
+      num_heads > kMaxGridY || num_kv_heads > kMaxGridY || max_blocks_per_seq < 1 ||
+      num_blocks < 1 || num_seqs > kMaxGridY)
+    return PA_ERR_SHAPE;
+  if (num_heads / num_kv_heads > kMaxGroup) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || num_query_tokens == 0) return PA_OK;
+  pa::DecodeArgs a = {};
+  a.out = out;
+  a.query = query;
+  a.k_cache = key_cache;
+  a.v_cache = value_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start_loc = query_start_loc;
+  a.num_seqs = num_seqs;
+  a.num_items = num_query_tokens;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = num_heads / num_kv_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.max_context_len = INT_MAX;
+  a.partition_blocks = 0;
+  a.max_partitions = 1;
+  a.max_query_len = max_query_len;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  if (dtype == PA_BF16) return status_of(pa::launch_prefill_mfma(a, head_dim, stream));
+  return status_of(pa::launch_decode(a, head_dim, false, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// Device helpers shared by the paged-attention kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 16;          // tokens per cache block
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef uint16_t bf16_t;            // bf16 kept as its bit pattern in memory
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---- bf16 <-> fp32 -------------------------------------------------------
+// A bf16 value is the top half of an fp32 word, so widening is a shift.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even (the hardware conversion on gfx950).
+__device__ __forceinline__ bf16_t f32_to_bf16(float x) {
+  __bf16 b = (__bf16)x;
+  return __builtin_bit_cast(bf16_t, b);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// ---- cross-lane sums inside groups of 2/4/8/16 lanes (DPP, no LDS) --------
+// quad_perm [1,0,3,2] swaps neighbours, [2,3,0,1] swaps pairs, half-row mirror
+// maps lane i of an 8-lane half onto 7-i, row mirror maps lane i of a 16-lane
+// row onto 15-i.  After the quad steps every lane of a quad holds the quad sum,
+// so each mirror step adds the partner quad / half and the sums stay exact
+// group totals in every lane.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group");
+  if constexpr (N >= 2) x += dpp_f32<0xB1>(x);     // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) x += dpp_f32<0x4E>(x);     // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) x += dpp_f32<0x141>(x);    // row_half_mirror
+  if constexpr (N >= 16) x += dpp_f32<0x140>(x);   // row_mirror
+  if constexpr (N >= 32) x += __shfl_xor(x, 16, 64);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
+// max over lanes that differ only in the lane-index bits [LO, 64): a
+// butterfly with shuffles (used once per workgroup, off the hot loop).
+template <int LO>
+__device__ __forceinline__ float xor_max_above(float x) {
+#pragma unroll
+  for (int o = LO; o < 64; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+template <int LO>
+__device__ __forceinline__ float xor_sum_above(float x) {
+#pragma unroll
+  for (int o = LO; o < 64; o <<= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+}  // namespace pa

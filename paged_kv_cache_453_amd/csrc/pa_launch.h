@@ -1,0 +1,65 @@
+// Host-side launchers of the paged-attention kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct ScatterArgs {
+  const void* key;
+  const void* value;
+  void* key_cache;
+  void* value_cache;
+  const int64_t* slot_mapping;
+  int64_t num_tokens;
+  int64_t key_stride;     // elements between tokens
+  int64_t value_stride;
+  int num_kv_heads;
+  int head_dim;
+  int64_t num_blocks;
+  int elem_bytes;
+};
+
+struct DecodeArgs {
+  void* out;
+  const void* query;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start_loc;  // non-null: one work item per prefill query token
+  float* part_o;
+  float* part_lse;
+  int num_seqs;
+  int num_items;          // grid z: sequences (decode) or query tokens (prefill)
+  int num_heads;
+  int num_kv_heads;
+  int group;
+  int max_blocks_per_seq;
+  int64_t num_blocks;
+  int max_context_len;
+  int partition_blocks;   // 0 = one workgroup walks the whole context
+  int max_partitions;
+  int max_query_len;
+  float scale_log2;       // softmax scale * log2(e)
+};
+
+struct ReduceArgs {
+  void* out;
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* context_lens;
+  int num_seqs;
+  int num_heads;
+  int max_partitions;
+  int partition_tokens;
+  int max_context_len;
+};
+
+hipError_t launch_reshape_and_cache(const ScatterArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t stream);
+hipError_t launch_splitk_reduce(const ReduceArgs& a, int head_dim, bool bf16, hipStream_t stream);
+hipError_t launch_prefill_mfma(const DecodeArgs& a, int head_dim, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,123 @@
+"""The C-ABI library on the CPU: it loads, exports every function include/pa.h
+declares, and rejects bad scalar arguments with the documented status before
+making any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE = 0, -1, -2, -3, -4
+F32, BF16 = 0, 1
+P = 0x1000  # a non-null stand-in pointer; never dereferenced because validation fails first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from paged_kv_cache_453_amd import lib as L
+    return L.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("pa_reshape_and_cache", "pa_decode", "pa_decode_splitk_reduce", "pa_prefill_chunk"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libpa.so does not export {name}"
+
+
+def test_binding_exposes_the_same_names():
+    import paged_kv_cache_453_amd as pkg
+    for name in declared_functions():
+        if name == "pa_status_string":
+            continue
+        assert callable(getattr(pkg, name))
+
+
+def test_status_strings(lib):
+    for code in (PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, -5, 7):
+        assert lib.pa_status_string(code)
+
+
+def decode(lib, **kw):
+    args = dict(out=P, query=P, k=P, v=P, bt=P, cl=P, S=4, hq=8, hkv=8, d=128, bs=16, mb=4,
+                nb=64, maxc=64, scale=0.1, ps=0, ws=None, wsb=0, dtype=BF16, stream=None)
+    args.update(kw)
+    a = args
+    return lib.pa_decode(a["out"], a["query"], a["k"], a["v"], a["bt"], a["cl"], a["S"], a["hq"],
+                         a["hkv"], a["d"], a["bs"], a["mb"], a["nb"], a["maxc"], a["scale"],
+                         a["ps"], a["ws"], a["wsb"], a["dtype"], a["stream"])
+
+
+def test_decode_validation(lib):
+    assert decode(lib, out=None) == PA_ERR_NULL
+    assert decode(lib, bt=None) == PA_ERR_NULL
+    assert decode(lib, d=96) == PA_ERR_UNSUPPORTED
+    assert decode(lib, bs=32) == PA_ERR_UNSUPPORTED
+    assert decode(lib, dtype=7) == PA_ERR_UNSUPPORTED
+    assert decode(lib, hq=12, hkv=8) == PA_ERR_SHAPE
+    assert decode(lib, hq=64, hkv=2) == PA_ERR_UNSUPPORTED      # group 32 > 16
+    assert decode(lib, S=-1) == PA_ERR_SHAPE
+    assert decode(lib, mb=0) == PA_ERR_SHAPE
+    assert decode(lib, ps=24) == PA_ERR_SHAPE
+    assert decode(lib, ps=16) == PA_ERR_WORKSPACE
+    need = lib.pa_decode_workspace_bytes(4, 8, 128, 64, 16)
+    assert decode(lib, ps=16, ws=P, wsb=need - 1) == PA_ERR_WORKSPACE
+    assert decode(lib, S=0, out=None, query=None) == PA_OK      # nothing to do, nothing launched
+
+
+def test_workspace_bytes(lib):
+    assert lib.pa_decode_workspace_bytes(32, 32, 128, 32768, 512) == 32 * 32 * 64 * 129 * 4
+    assert lib.pa_decode_workspace_bytes(2, 2, 64, 17, 16) == 2 * 2 * 2 * 65 * 4
+    assert lib.pa_decode_workspace_bytes(2, 2, 64, 17, 0) == 0
+
+
+def test_scatter_validation(lib):
+    f = lib.pa_reshape_and_cache
+    assert f(P, P, None, P, P, 4, 1024, 1024, 8, 128, 16, 64, BF16, None) == PA_ERR_NULL
+    assert f(None, P, P, P, P, 4, 1024, 1024, 8, 128, 16, 64, BF16, None) == PA_ERR_NULL
+    assert f(P, P, P, P, P, 4, 1023, 1024, 8, 128, 16, 64, BF16, None) == PA_ERR_SHAPE
+    assert f(P, P, P, P, P, -1, 1024, 1024, 8, 128, 16, 64, BF16, None) == PA_ERR_SHAPE
+    assert f(P, P, P, P, P, 4, 1024, 1024, 8, 80, 16, 64, BF16, None) == PA_ERR_UNSUPPORTED
+    assert f(P, P, P, P, P, 4, 1024, 1024, 8, 128, 8, 64, BF16, None) == PA_ERR_UNSUPPORTED
+    assert f(None, None, P, P, None, 0, 1024, 1024, 8, 128, 16, 64, BF16, None) == PA_OK
+
+
+def test_reduce_validation(lib):
+    f = lib.pa_decode_splitk_reduce
+    assert f(P, None, 0, P, 4, 8, 128, 64, 16, BF16, None) == PA_ERR_WORKSPACE
+    assert f(P, P, 10, P, 4, 8, 128, 64, 16, BF16, None) == PA_ERR_WORKSPACE
+    assert f(P, P, 1 << 30, P, 4, 8, 128, 64, 0, BF16, None) == PA_ERR_SHAPE
+    assert f(None, P, 1 << 30, P, 4, 8, 128, 64, 16, BF16, None) == PA_ERR_NULL
+
+
+def test_prefill_validation(lib):
+    f = lib.pa_prefill_chunk
+    base = [P, P, P, P, P, P, P, 2, 100, 8, 8, 128, 16, 8, 64, 64, 0.1, BF16, None]
+
+    def call(**kw):
+        a = list(base)
+        idx = dict(out=0, qsl=5, S=7, tq=8, hq=9, hkv=10, d=11, bs=12, mb=13, nb=14, mql=15,
+                   dtype=17)
+        for k, v in kw.items():
+            a[idx[k]] = v
+        return f(*a)
+
+    assert call(qsl=None) == PA_ERR_NULL
+    assert call(d=32) == PA_ERR_UNSUPPORTED
+    assert call(hq=9, hkv=2) == PA_ERR_SHAPE
+    assert call(mql=-1) == PA_ERR_SHAPE
+    assert call(nb=0) == PA_ERR_SHAPE
+    assert call(S=0, out=None) == PA_OK

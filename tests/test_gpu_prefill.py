@@ -1,0 +1,117 @@
+"""pa_prefill_chunk on the GPU against the fp64 oracle.
+
+bf16 runs on the MFMA kernel, fp32 on the per-token vector path.  Cases: the
+mixed workload's four 512-token chunks over paged prefixes, chunks with no
+prefix, ragged chunk and prefix lengths (not multiples of 16 or 64), GQA heads,
+head_dim 64, a one-token chunk equal to decode, and a prompt prefilled in two
+chunks equal to the same prompt in one chunk (xdnf.cn article, section 六.4).
+"""
+import numpy as np
+import pytest
+
+from workloads import config4, make_prefill
+
+from pa_harness import (as_f64, assert_close, gpu_decode, gpu_prefill, oracle_decode,
+                        oracle_prefill, say, to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+def run(w):
+    import torch
+    dw = to_device(w)
+    gpu_prefill(dw)
+    torch.cuda.synchronize()
+    return dw
+
+
+def test_mixed_workload_prefill_part(gpu):
+    say("prefill config4: 4 x 512-token chunks")
+    w = config4()
+    w.decode = None
+    dw = run(w)
+    assert_close(as_f64(dw.prefill.out), oracle_prefill(w), "bf16", "config4 prefill")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("hq,hkv,d", [(4, 4, 128), (8, 2, 128), (6, 3, 64)])
+def test_ragged_chunks(gpu, dtype, hq, hkv, d):
+    prefix = [0, 5, 16, 100, 777]
+    chunk = [1, 70, 64, 130, 33]
+    w = make_prefill(f"ragged-{hq}-{hkv}-{d}", 71 + hq, dtype, prefix, chunk, hq, hkv, d, 256)
+    dw = run(w)
+    assert_close(as_f64(dw.prefill.out), oracle_prefill(w), dtype, f"ragged {dtype} {hq}/{hkv}/{d}")
+
+
+def test_no_prefix_long_chunk(gpu):
+    w = make_prefill("noprefix", 72, "bf16", [0, 0], [1000, 257], 8, 8, 128, 256)
+    dw = run(w)
+    assert_close(as_f64(dw.prefill.out), oracle_prefill(w), "bf16", "no prefix")
+
+
+def test_fp32_prefill_tight(gpu):
+    w = make_prefill("f32", 73, "f32", [0, 300, 1000], [200, 64, 17], 8, 4, 128, 256)
+    dw = run(w)
+    assert_close(as_f64(dw.prefill.out), oracle_prefill(w), "f32", "f32 prefill")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_single_token_chunk_equals_decode(gpu, dtype):
+    import torch
+    w = make_prefill("one", 74, dtype, [0, 40, 500], [1, 1, 1], 8, 2, 128, 64)
+    dw = run(w)
+    g = dw.prefill
+    from workloads.device import DeviceGroup
+    dec = DeviceGroup(context_lens=g.context_lens, block_tables=g.block_tables, query=g.query,
+                      out=torch.empty_like(g.out), max_context_len=int(g.context_lens.max().item()))
+    gpu_decode(dw, 0, group=dec)
+    torch.cuda.synchronize()
+    assert_close(as_f64(g.out), as_f64(dec.out), dtype, "prefill(1) vs decode")
+    assert_close(as_f64(g.out), oracle_prefill(w), dtype, "prefill(1) vs oracle")
+
+
+def test_two_chunks_equal_one_shot(gpu):
+    import torch
+    w = make_prefill("oneshot", 75, "bf16", [0], [1024], 8, 8, 128, 128)
+    dw = run(w)
+    one = as_f64(dw.prefill.out)
+    g = dw.prefill
+    for lo in (0, 512):
+        out = torch.empty((512, 8, 128), dtype=g.out.dtype, device="cuda")
+        from paged_kv_cache_453_amd import lib
+        lib.pa_prefill_chunk(out, g.query[lo:lo + 512].contiguous(), dw.k_cache, dw.v_cache,
+                             g.block_tables, torch.tensor([0, 512], dtype=torch.int32, device="cuda"),
+                             torch.tensor([lo + 512], dtype=torch.int32, device="cuda"), w.scale, 512)
+        torch.cuda.synchronize()
+        assert_close(as_f64(out), one[lo:lo + 512], "bf16", f"chunk at {lo}")
+    assert_close(one, oracle_prefill(w), "bf16", "one shot")
+
+
+def test_prefill_contract_violation_gives_nan(gpu):
+    import torch
+    w = make_prefill("bad", 76, "bf16", [10, 10], [20, 20], 4, 4, 128, 64)
+    dw = to_device(w)
+    g = dw.prefill
+    lens = g.context_lens.clone()
+    lens[1] = 5                     # chunk longer than its context
+    g.context_lens = lens
+    gpu_prefill(dw)
+    torch.cuda.synchronize()
+    out = as_f64(g.out)
+    assert np.isnan(out[20:]).all()
+    assert_close(out[:20], oracle_prefill(w)[:20], "bf16", "healthy sequence")
+
+
+@pytest.mark.slow
+def test_mixed_step_prefill_then_decode(gpu):
+    """The whole mixed batch on one stream: 4 prefill chunks, then 192 decoders
+    that share 2048-token prefixes in groups of 3."""
+    import torch
+    say("mixed step config4")
+    w = config4()
+    dw = to_device(w)
+    gpu_prefill(dw)
+    gpu_decode(dw)
+    torch.cuda.synchronize()
+    assert_close(as_f64(dw.prefill.out), oracle_prefill(w), "bf16", "mixed: prefill part")
+    assert_close(as_f64(dw.decode.out), oracle_decode(w), "bf16", "mixed: decode part")

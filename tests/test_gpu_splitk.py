@@ -1,0 +1,63 @@
+"""Split-K partials on the GPU against the oracle's per-partition results.
+
+The workspace layout is part of the ABI: fp32 o_part [S, Hq, P, D] followed by
+fp32 lse_part [S, Hq, P] (natural log).  The merge is checked separately: any
+partition length gives the same final output within tolerance.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from workloads import make_decode
+
+from pa_harness import as_f64, assert_close, gpu_decode, lib, oracle_decode, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dtype,hq,hkv", [("bf16", 32, 8), ("f32", 8, 8), ("bf16", 40, 40)])
+def test_partials_match_oracle(gpu, dtype, hq, hkv):
+    import torch
+    rng = np.random.default_rng(61)
+    lens = np.concatenate([[1, 511, 512, 513], rng.integers(600, 3000, size=4)])
+    ps = 512
+    w = make_decode("parts", 61, dtype, lens, hq, hkv, 128, 2048, with_scatter=False)
+    dw = to_device(w)
+    g = dw.decode
+    ws = gpu_decode(dw, ps)
+    torch.cuda.synchronize()
+    S, P, D = len(lens), -(-int(lens.max()) // ps), 128
+    host = ws.cpu().numpy()
+    o_part = host[:S * hq * P * D * 4].view(np.float32).reshape(S, hq, P, D)
+    lse = host[S * hq * P * D * 4:S * hq * P * (D + 1) * 4].view(np.float32).reshape(S, hq, P)
+    ro, rl, n = oracle.decode_partials(w.decode.query, w.k_host, w.v_host,
+                                       w.host_tables(w.decode.block_tables), w.decode.context_lens,
+                                       w.scale, w.dtype, ps)
+    for s in range(S):
+        if n[s] <= 1:
+            continue   # written straight to the output, no partials
+        assert_close(o_part[s, :, :n[s]], ro[s, :, :n[s]], dtype, f"o_part seq {s}")
+        # lse: scores from fp32 dot products of 128 terms; 1e-4 absolute covers their rounding
+        err = np.abs(lse[s, :, :n[s]].astype(np.float64) - rl[s, :, :n[s]])
+        assert (err <= 1e-4 + 1e-5 * np.abs(rl[s, :, :n[s]])).all(), err.max()
+    assert_close(as_f64(g.out), oracle_decode(w), dtype, "merged")
+
+
+@pytest.mark.parametrize("ps", [16, 48, 512, 4096, 0])
+def test_any_partition_length_gives_the_same_answer(gpu, ps):
+    rng = np.random.default_rng(62)
+    lens = rng.integers(1, 3000, size=10)
+    w = make_decode("anyps", 62, "f32", lens, 8, 2, 64, 2048, with_scatter=True)
+    dw = to_device(w)
+    from pa_harness import gpu_scatter
+    import torch
+    gpu_scatter(dw)
+    gpu_decode(dw, ps)
+    torch.cuda.synchronize()
+    assert_close(as_f64(dw.decode.out), oracle_decode(w), "f32", f"ps={ps}")
+
+
+def test_workspace_size_formula(gpu):
+    L = lib()
+    assert L.pa_decode_workspace_bytes(32, 32, 128, 32768, 512) == 32 * 32 * 64 * (128 + 1) * 4
+    assert L.pa_decode_workspace_bytes(4, 8, 64, 100, 0) == 0
