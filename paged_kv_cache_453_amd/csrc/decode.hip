@@ -100,9 +100,11 @@ struct QFrag<bf16_t> {
   __device__ float dot(const u32x4& k) const {
     float s = 0.f;
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
-      s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q[x]),
-                                          __builtin_bit_cast(bf16x2, k[x]), s, false);
+    for (int x = 0; x < 4; ++x) {
+      const uint32_t qw = q[x];
+      const uint32_t kw = k[x];
+      s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qw), as_bf16x2(kw), s, false);
+    }
     return s;
   }
   __device__ static float post(float s, float scale_log2) { return s * scale_log2; }

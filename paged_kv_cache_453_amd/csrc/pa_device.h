@@ -24,6 +24,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Reinterpret one 32-bit word as two bf16 lanes.  Takes the word by value:
+// bit-casting a vector element expression in place (vec[i]) has been seen to
+// read element 0 whatever i is, so callers pass a plain scalar.
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
+
 // fp32 -> bf16, round to nearest even (the hardware conversion on gfx950).
 __device__ __forceinline__ bf16_t f32_to_bf16(float x) {
   __bf16 b = (__bf16)x;
