@@ -80,6 +80,24 @@ def cpu_baseline(w, budget_s: float = 10.0):
                       f"{t_total:.1f} s on 1 host thread"}
 
 
+def copy_calibration(torch, dev, nbytes: int = 1 << 30, reps: int = 3) -> int:
+    """A plain copy of known size: reads nbytes, writes nbytes per launch."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps,
+                      "ms_per_copy": round(ms, 4),
+                      "gbs_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -87,6 +105,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--partition-size", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time a plain 1 GiB device-to-device copy instead (for scaling the "
+                         "FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -100,9 +121,11 @@ def main(argv=None):
     from workloads import accounting, config2
     from workloads.device import to_device
 
-    lib.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        return copy_calibration(torch, dev)
+    lib.load()
     ps = args.partition_size
 
     log("bench: generating the Llama-2-13B-shaped decode workload")

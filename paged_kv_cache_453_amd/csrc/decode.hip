@@ -9,6 +9,7 @@
 // K/V blocks once at full width and hiding all arithmetic under those loads.
 //
 // Work decomposition.  One workgroup (4 waves) per (item, kv head, partition),
+// kv heads varying fastest in launch order,
 // where an item is a sequence (decode) or one prefill query token (the generic
 // per-token prefill path).  A partition is a run of consecutive blocks; the
 // waves of a workgroup take its blocks round-robin.  All query heads that share
@@ -157,9 +158,12 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   __shared__ float sh_l[NW][GP];
   __shared__ int sh_bad[NW];
 
-  const int item = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int part = blockIdx.z;
+  // blockIdx.x = item * num_kv_heads + kv head: workgroups launched together
+  // read the adjacent head slabs of the same physical blocks, which keeps the
+  // HBM accesses of concurrently running waves close together.
+  const int item = blockIdx.x / a.num_kv_heads;
+  const int kvh = blockIdx.x - item * a.num_kv_heads;
+  const int part = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = wave_uniform(threadIdx.x >> 6);
   const int r = lane / LPR;
@@ -386,7 +390,8 @@ __global__ __launch_bounds__(D) void splitk_reduce_kernel(ReduceArgs a) {
 
 template <typename T, int D>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-  dim3 grid(a.num_items, a.num_kv_heads, a.partition_blocks > 0 ? a.max_partitions : 1);
+  dim3 grid((unsigned)((int64_t)a.num_items * a.num_kv_heads),
+            a.partition_blocks > 0 ? a.max_partitions : 1);
   dim3 block(256);
   const int G = a.group;
   if (G <= 1)

@@ -101,7 +101,7 @@ int pa_decode(void* out, const void* query, const void* key_cache, const void* v
     return PA_ERR_SHAPE;
   if (num_heads / num_kv_heads > kMaxGroup) return PA_ERR_UNSUPPORTED;
   const int nparts = max_partitions(max_context_len, partition_size);
-  if (nparts > kMaxGridY) return PA_ERR_SHAPE;
+  if (nparts > kMaxGridY || (int64_t)num_seqs * num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;
   if (partition_size > 0) {
     const size_t need = pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len,
                                                   partition_size);
@@ -180,6 +180,7 @@ int pa_prefill_chunk(void* out, const void* query, const void* key_cache, const 
       num_blocks < 1 || num_seqs > kMaxGridY)
     return PA_ERR_SHAPE;
   if (num_heads / num_kv_heads > kMaxGroup) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)num_query_tokens * num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;
   if (num_seqs == 0 || num_query_tokens == 0) return PA_OK;
   pa::DecodeArgs a = {};
   a.out = out;
