@@ -80,6 +80,55 @@ def cpu_baseline(w, budget_s: float = 10.0):
                       f"{t_total:.1f} s on 1 host thread"}
 
 
+def _counter_rows(path: str, kernel_prefix: str):
+    import csv
+    with open(path) as f:
+        return [float(r["Counter_Value"]) for r in csv.DictReader(f)
+                if r["Kernel_Name"].startswith(kernel_prefix)]
+
+
+def digest_counters(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv: str,
+                    copy_bytes: int = 1 << 30) -> int:
+    """Turn four rocprofv3 --pmc runs into HBM bytes per decode launch.
+
+    FETCH_SIZE and WRITE_SIZE are read in KiB per dispatch.  Each is scaled by
+    what the same counter reads for a plain copy of copy_bytes (which reads and
+    writes exactly copy_bytes), so the result is in true bytes whatever share of
+    the memory channels the counter sees.  Writes the committed summary that
+    bench.py reports as roofline.traffic while decode.hip is unchanged.
+    """
+    import statistics
+    dec = "void pa::decode_valu_kernel<unsigned short, 128, 1>"
+    copy = "__amd_rocclr_copyBuffer"
+    f_dec = statistics.mean(_counter_rows(fetch_csv, dec))
+    w_dec = statistics.mean(_counter_rows(write_csv, dec))
+    f_copy = statistics.mean(_counter_rows(copy_fetch_csv, copy))
+    w_copy = statistics.mean(_counter_rows(copy_write_csv, copy))
+    f_scale = copy_bytes / (f_copy * 1024)
+    w_scale = copy_bytes / (w_copy * 1024)
+    hbm = f_dec * 1024 * f_scale + w_dec * 1024 * w_scale
+    out = {"kernel": dec, "decode_source_sha256_16": source_digest(),
+           "fetch_kib_per_launch": round(f_dec, 1), "write_kib_per_launch": round(w_dec, 1),
+           "copy_bytes": copy_bytes, "copy_fetch_kib": round(f_copy, 1),
+           "copy_write_kib": round(w_copy, 1), "fetch_scale": round(f_scale, 4),
+           "write_scale": round(w_scale, 4), "hbm_bytes_per_launch": int(round(hbm)),
+           "commands": [
+               "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o bench -- "
+               "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+               "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o bench -- "
+               "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+               "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_copy_fetch -o copy -- "
+               "python3 bench.py --copy-calibration",
+               "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_copy_write -o copy -- "
+               "python3 bench.py --copy-calibration"]}
+    os.makedirs(os.path.dirname(COUNTERS), exist_ok=True)
+    with open(COUNTERS, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def copy_calibration(torch, dev, nbytes: int = 1 << 30, reps: int = 3) -> int:
     """A plain copy of known size: reads nbytes, writes nbytes per launch."""
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
@@ -103,12 +152,18 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--partition-size", type=int, default=512)
+    ap.add_argument("--partition-size", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--digest-counters", nargs=4, metavar="CSV",
+                    help="write the committed HBM-traffic summary from four rocprofv3 "
+                         "counter_collection.csv files: decode FETCH_SIZE, decode WRITE_SIZE, "
+                         "copy FETCH_SIZE, copy WRITE_SIZE (no GPU needed)")
     args = ap.parse_args(argv)
+    if args.digest_counters:
+        return digest_counters(*args.digest_counters)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the paged-attention step runs on a single "

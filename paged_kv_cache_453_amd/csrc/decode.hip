@@ -25,6 +25,11 @@
 // partial dot products, done with DPP inside a 16-lane row.  Row groups, waves
 // and partitions are merged once at the end with the log-sum-exp rule.
 //
+// Streaming.  Each wave keeps two slabs in flight (the next block's K/V loads
+// are issued before the current block is consumed), the loads carry the
+// nontemporal hint, and full blocks take a path without row masks; only a
+// sequence's last, partly filled block pays for them.
+//
 // Scores are kept in base 2: q is pre-multiplied by scale*log2(e), so softmax
 // weights are exp2(s - m).
 #include <math.h>
@@ -110,6 +115,93 @@ struct QFrag<bf16_t> {
   }
   __device__ static float post(float s, float scale_log2) { return s * scale_log2; }
 };
+
+// One (block, kv head) slab of K and of V as this lane holds it: NLD
+// 16-byte pieces each, rows RPL apart.
+template <int NLD>
+struct Slab {
+  u32x4 k[NLD];
+  u32x4 v[NLD];
+};
+
+// K/V rows are read once per step and never reused by this launch: the loads
+// carry the nontemporal hint so they do not displace reusable lines (block
+// tables, queries, partials) in the caches.
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void load_slab(Slab<kBlock * D / (kWave * ElemTraits<T>::kPerLoad)>& s,
+                                          const T* kb, const T* vb) {
+  constexpr int RPL = kWave / (D / ElemTraits<T>::kPerLoad);
+  constexpr int NLD = kBlock / RPL;
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) s.k[i] = load16(kb + i * RPL * D);
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) s.v[i] = load16(vb + i * RPL * D);
+}
+
+// Fold one slab into this lane's online-softmax state (running max m, running
+// sum l, output slice acc per query head of the group).  MASKED: rows at or
+// past nvalid are skipped -- their scores never enter the max, their weights
+// are 0 and their V values are replaced by 0 before use, since they may hold
+// anything (NaN included) and 0 * NaN is NaN.
+template <typename T, int D, int GP, bool MASKED>
+__device__ __forceinline__ void consume_slab(
+    const Slab<kBlock * D / (kWave * ElemTraits<T>::kPerLoad)>& sl, const QFrag<T> (&q)[GP],
+    float scale_log2, int r, int nvalid, float (&m)[GP], float (&l)[GP],
+    float (&acc)[GP][ElemTraits<T>::kPerLoad]) {
+  constexpr int E = ElemTraits<T>::kPerLoad;
+  constexpr int LPR = D / E;
+  constexpr int RPL = kWave / LPR;
+  constexpr int NLD = kBlock / RPL;
+
+  // scores of this lane's rows, summed over the LPR lanes of each row
+  float s[GP][NLD];
+#pragma unroll
+  for (int g = 0; g < GP; ++g)
+#pragma unroll
+    for (int i = 0; i < NLD; ++i)
+      s[g][i] = QFrag<T>::post(group_sum<LPR>(q[g].dot(sl.k[i])), scale_log2);
+
+  bool valid[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) valid[i] = !MASKED || i * RPL + r < nvalid;
+
+  float p[GP][NLD];
+#pragma unroll
+  for (int g = 0; g < GP; ++g) {
+    float bm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i)
+      if (valid[i]) bm = fmaxf(bm, s[g][i]);
+    const float mn = fmaxf(m[g], bm);
+    // with masking, mn stays -inf while this row group has seen no token
+    const float alpha = (MASKED && mn == -INFINITY) ? 1.f : exp2f(m[g] - mn);
+    float lsum = l[g] * alpha;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[g][e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      p[g][i] = valid[i] ? exp2f(s[g][i] - mn) : 0.f;
+      lsum += p[g][i];
+    }
+    l[g] = lsum;
+    m[g] = mn;
+  }
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    u32x4 vr = sl.v[i];
+    if (MASKED) vr = valid[i] ? vr : u32x4{0u, 0u, 0u, 0u};
+    float v[E];
+    widen<T>(vr, v);
+#pragma unroll
+    for (int g = 0; g < GP; ++g)
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[g][e] = fmaf(p[g][i], v[e], acc[g][e]);
+  }
+}
 
 // Locate the sequence an item belongs to and how many of its tokens it sees.
 // Returns false if the item has no query row (past the last prefill token).
@@ -235,70 +327,36 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 
   // Blocks of this wave: jb + w, jb + w + NW, ...  Their ids are fetched 64 at
   // a time into one register (lane t holds the t-th) and broadcast per step.
+  // The K/V loads of the next block are issued before the current one is
+  // consumed, so every wave keeps two slabs in flight.  A block id outside the
+  // pool reads block 0 instead (in bounds) and poisons the result.
   const int nb_w = (je - jb - w + NW - 1) / NW;
   for (int base = 0; base < nb_w; base += kWave) {
     const int idx = base + lane;
     const int myb = idx < nb_w ? table[jb + w + NW * idx] : 0;
     const int cnt = min(kWave, nb_w - base);
-    for (int t = 0; t < cnt; ++t) {
+    const auto slab_ptr = [&](int t, const T* pool) {
       const int bid = __builtin_amdgcn_readlane(myb, t);
+      const bool ok = bid >= 0 && (int64_t)bid < a.num_blocks;
+      bad_block |= !ok;
+      return pool + ((int64_t)(ok ? bid : 0) * a.num_kv_heads + kvh) * head_slab + lane_off;
+    };
+    const auto consume = [&](const Slab<NLD>& sl, int t) {
       const int j = jb + w + NW * (base + t);
-      if (bid < 0 || (int64_t)bid >= a.num_blocks) {
-        bad_block = true;
-        continue;
-      }
-      const int64_t slab = ((int64_t)bid * a.num_kv_heads + kvh) * head_slab;
-      const T* kb = kpool + slab + lane_off;
-      const T* vb = vpool + slab + lane_off;
-      u32x4 kr[NLD], vr[NLD];
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) kr[i] = *reinterpret_cast<const u32x4*>(kb + i * RPL * D);
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) vr[i] = *reinterpret_cast<const u32x4*>(vb + i * RPL * D);
       const int nvalid = min(kBlock, tok_end - j * kBlock);
-
-      // scores of this lane's rows, summed over the LPR lanes of each row
-      float s[GP][NLD];
-#pragma unroll
-      for (int g = 0; g < GP; ++g)
-#pragma unroll
-        for (int i = 0; i < NLD; ++i)
-          s[g][i] = QFrag<T>::post(group_sum<LPR>(q[g].dot(kr[i])), a.scale_log2);
-
-      bool valid[NLD];
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) valid[i] = i * RPL + r < nvalid;
-
-      float p[GP][NLD];
-#pragma unroll
-      for (int g = 0; g < GP; ++g) {
-        float bm = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < NLD; ++i)
-          if (valid[i]) bm = fmaxf(bm, s[g][i]);
-        const float mn = fmaxf(m[g], bm);
-        // mn is -inf only if this row group has seen no token yet and none here
-        const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m[g] - mn);
-        float lsum = l[g] * alpha;
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[g][e] *= alpha;
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-          p[g][i] = valid[i] ? exp2f(s[g][i] - mn) : 0.f;
-          lsum += p[g][i];
-        }
-        l[g] = lsum;
-        m[g] = mn;
-      }
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        if (!valid[i]) continue;   // rows past the context may hold anything
-        float v[E];
-        widen<T>(vr[i], v);
-#pragma unroll
-        for (int g = 0; g < GP; ++g)
-#pragma unroll
-          for (int e = 0; e < E; ++e) acc[g][e] = fmaf(p[g][i], v[e], acc[g][e]);
+      if (nvalid == kBlock)
+        consume_slab<T, D, GP, false>(sl, q, a.scale_log2, r, nvalid, m, l, acc);
+      else
+        consume_slab<T, D, GP, true>(sl, q, a.scale_log2, r, nvalid, m, l, acc);
+    };
+    Slab<NLD> sa, sb;
+    load_slab<T, D>(sa, slab_ptr(0, kpool), slab_ptr(0, vpool));
+    for (int t = 0; t < cnt; t += 2) {
+      if (t + 1 < cnt) load_slab<T, D>(sb, slab_ptr(t + 1, kpool), slab_ptr(t + 1, vpool));
+      consume(sa, t);
+      if (t + 1 < cnt) {
+        if (t + 2 < cnt) load_slab<T, D>(sa, slab_ptr(t + 2, kpool), slab_ptr(t + 2, vpool));
+        consume(sb, t + 1);
       }
     }
   }
