@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpa.so")
 ARCH = "gfx950"
 
-SOURCES = ["pa_api.cpp", "reshape_and_cache.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["pa_api.cpp", "reshape_and_cache.hip", "decode.hip", "decode_mfma.hip", "prefill.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}",
@@ -27,6 +27,10 @@ FLAGS = [
     "-shared",
     # packed fp32 vector ops stay off (hand-written or generated)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the kernels rescale their accumulators on
+    # the vector ALUs, and AGPR results would be copied back and forth (decode:
+    # 178 -> 142 registers, 2 -> 3 waves per SIMD; prefill: 146 -> 108)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall",
     "-Wno-unused-function",
     "-Wno-unused-variable",

@@ -124,22 +124,34 @@ struct Slab {
   u32x4 v[NLD];
 };
 
-// K/V rows are read once per step and never reused by this launch: the loads
-// carry the nontemporal hint so they do not displace reusable lines (block
-// tables, queries, partials) in the caches.
-__device__ __forceinline__ u32x4 load16(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+// Slab loads go through a buffer resource per (block, kv head) slab: the base
+// is the slab's address (scalar registers), lanes add 32-bit byte offsets, and
+// the range check of the buffer unit turns a resource of size 0 into zero data
+// with no memory access -- used for a lookahead past the last block and for
+// block ids outside the pool.  K/V rows are read once per step and never
+// reused by this launch, so the loads carry the nontemporal hint.
+constexpr int kBufferWord3 = 0x00020000;   // raw 32-bit buffer, no format conversion
+constexpr int kNontemporal = 2;            // cache-policy bit of buffer loads
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferWord3);
+}
+
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t rsrc, int byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(rsrc, byte_off, 0, kNontemporal);
 }
 
 template <typename T, int D>
 __device__ __forceinline__ void load_slab(Slab<kBlock * D / (kWave * ElemTraits<T>::kPerLoad)>& s,
-                                          const T* kb, const T* vb) {
+                                          __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                          int lane_byte_off) {
   constexpr int RPL = kWave / (D / ElemTraits<T>::kPerLoad);
   constexpr int NLD = kBlock / RPL;
+  constexpr int STEP = RPL * D * (int)sizeof(T);
 #pragma unroll
-  for (int i = 0; i < NLD; ++i) s.k[i] = load16(kb + i * RPL * D);
+  for (int i = 0; i < NLD; ++i) s.k[i] = load16(kr, lane_byte_off + i * STEP);
 #pragma unroll
-  for (int i = 0; i < NLD; ++i) s.v[i] = load16(vb + i * RPL * D);
+  for (int i = 0; i < NLD; ++i) s.v[i] = load16(vr, lane_byte_off + i * STEP);
 }
 
 // Fold one slab into this lane's online-softmax state (running max m, running
@@ -322,24 +334,32 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   const T* vpool = static_cast<const T*>(a.v_cache);
   const int32_t* table = a.block_tables + (int64_t)it.seq * a.max_blocks_per_seq;
   const int64_t head_slab = (int64_t)kBlock * D;
-  const int lane_off = r * D + c * E;
+  const int lane_off = r * D + c * E;     // elements from the slab start
   bool bad_block = false;
 
   // Blocks of this wave: jb + w, jb + w + NW, ...  Their ids are fetched 64 at
   // a time into one register (lane t holds the t-th) and broadcast per step.
-  // The K/V loads of the next block are issued before the current one is
-  // consumed, so every wave keeps two slabs in flight.  A block id outside the
-  // pool reads block 0 instead (in bounds) and poisons the result.
+  // Two slabs are in flight: the next block's loads are issued before the
+  // current block is consumed, unconditionally (straight-line code, so each
+  // consume waits only for its own slab); past the last block the resource is
+  // empty and the load moves no data.  A block id outside the pool reads as
+  // zeros and poisons the result.
   const int nb_w = (je - jb - w + NW - 1) / NW;
+  const int slab_bytes = kBlock * D * (int)sizeof(T);
+  const int lane_byte_off = lane_off * (int)sizeof(T);
   for (int base = 0; base < nb_w; base += kWave) {
     const int idx = base + lane;
     const int myb = idx < nb_w ? table[jb + w + NW * idx] : 0;
     const int cnt = min(kWave, nb_w - base);
-    const auto slab_ptr = [&](int t, const T* pool) {
-      const int bid = __builtin_amdgcn_readlane(myb, t);
-      const bool ok = bid >= 0 && (int64_t)bid < a.num_blocks;
-      bad_block |= !ok;
-      return pool + ((int64_t)(ok ? bid : 0) * a.num_kv_heads + kvh) * head_slab + lane_off;
+    const auto load_step = [&](Slab<NLD>& sl, int t) {
+      const int bid = __builtin_amdgcn_readlane(myb, min(t, cnt - 1));
+      const bool in_pool = bid >= 0 && (int64_t)bid < a.num_blocks;
+      bad_block |= t < cnt && !in_pool;
+      const bool live = t < cnt && in_pool;
+      const int64_t off = live ? ((int64_t)bid * a.num_kv_heads + kvh) * head_slab : 0;
+      const int bytes = live ? slab_bytes : 0;
+      load_slab<T, D>(sl, slab_rsrc(kpool + off, bytes), slab_rsrc(vpool + off, bytes),
+                      lane_byte_off);
     };
     const auto consume = [&](const Slab<NLD>& sl, int t) {
       const int j = jb + w + NW * (base + t);
@@ -350,14 +370,13 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
         consume_slab<T, D, GP, true>(sl, q, a.scale_log2, r, nvalid, m, l, acc);
     };
     Slab<NLD> sa, sb;
-    load_slab<T, D>(sa, slab_ptr(0, kpool), slab_ptr(0, vpool));
+    load_step(sa, 0);
     for (int t = 0; t < cnt; t += 2) {
-      if (t + 1 < cnt) load_slab<T, D>(sb, slab_ptr(t + 1, kpool), slab_ptr(t + 1, vpool));
+      load_step(sb, t + 1);
       consume(sa, t);
-      if (t + 1 < cnt) {
-        if (t + 2 < cnt) load_slab<T, D>(sa, slab_ptr(t + 2, kpool), slab_ptr(t + 2, vpool));
-        consume(sb, t + 1);
-      }
+      if (t + 1 >= cnt) break;
+      load_step(sa, t + 2);
+      consume(sb, t + 1);
     }
   }
 
@@ -465,8 +484,14 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Grouped-query decode with at least this many query heads per kv head runs on
+// the matrix cores (bf16, head_dim 128); smaller groups stay on the vector ALUs.
+constexpr int kMfmaMinGroup = 4;
+
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t stream) {
   if (a.num_items == 0) return hipSuccess;
+  if (bf16 && head_dim == 128 && a.group >= kMfmaMinGroup && a.query_start_loc == nullptr)
+    return launch_decode_gqa_mfma(a, stream);
   if (bf16) return head_dim == 64 ? launch_decode_t<bf16_t, 64>(a, stream)
                                   : launch_decode_t<bf16_t, 128>(a, stream);
   return head_dim == 64 ? launch_decode_t<float, 64>(a, stream)

@@ -1,0 +1,349 @@
+// Paged-attention decode for grouped-query heads on bf16 matrix cores (MFMA).
+//
+// Same computation as the vector-ALU decode: for each query head h of a
+// sequence, softmax(scale * q_h K^T) V over the sequence's cached tokens, K and
+// V read through the block table from the pool [num_blocks, num_kv_heads,
+// block_size, head_dim] ("vLLM 基本原理", section PagedAttention;
+// intelliparadigm.com article, section 3.1).  When G = num_heads / num_kv_heads
+// query heads share one kv head, every K/V row meets G queries, so q.K^T and
+// p.V become small dense products: S^T = K Q^T (16 tokens x G heads, reduced
+// over head_dim) and O^T = V^T P^T (head_dim x G heads, reduced over tokens).
+// Decode stays bound by HBM (xdnf.cn article, section 六.5): the matrix cores
+// only take the arithmetic off the vector ALUs so that the loads are never
+// starved.
+//
+// Work decomposition.  One wave per (sequence, kv head, partition); a
+// workgroup holds the 4 waves of 4 consecutive kv heads of the same sequence
+// and partition, so they walk the same block ids and read neighbouring 4 KiB
+// head slabs.  Waves never exchange data: each owns its heads' whole softmax
+// state, and partitions meet in the split-K merge.
+//
+// Operand layouts (v_mfma_f32_16x16x32_bf16 for scores, v_mfma_f32_16x16x16_bf16
+// for p.V).  In both, lane l = 16 g + r supplies row/column r and reduction
+// slots [8g, 8g+8) resp. [4g, 4g+4); a 16x16 result leaves rows 4g .. 4g+3 of
+// column r in lane l.
+//  - K is the A operand of the score product with token r in row r.  The
+//    reduction order over head_dim is free as long as Q uses the same one, so
+//    lane (r, g) takes 16-byte chunk 4ks + g of token r at k-step ks.  Loading
+//    that pattern straight from memory (16 rows touched per instruction) runs
+//    well below the HBM rate, so K is loaded exactly like V (16 lanes per
+//    contiguous 256-byte row) and turned around through a small per-wave LDS
+//    tile: 4 16-byte writes and 4 16-byte reads per lane and block, rows
+//    padded to 272 bytes so neither side has bank conflicts.
+//  - Q^T is the B operand: lane (r, g) holds chunk 4ks + g of query head r
+//    (zero for r >= G).
+//  - The score result leaves tokens 4g .. 4g+3 of head r in lane (r, g): the
+//    softmax state of head r lives in the 4 lanes r, r+16, r+32, r+48, and its
+//    probabilities are already laid out as the B operand of p.V (P^T).
+//  - V is the A operand of O^T = V^T P^T, where row r of d-tile t stands for
+//    column 8r + t.  Lane (r, g) loads columns 8r .. 8r+7 of tokens 4g .. 4g+3
+//    (one fully contiguous 256-byte row per 16 lanes and instruction) and
+//    takes element t of each of the four loads as its operand for tile t, a
+//    register-local repack.  Output tile t then holds columns 8(4g+i) + t in
+//    lane (r, g), so every lane ends with 4 runs of 8 consecutive columns.
+//
+// Scores are kept in base 2 (scale * log2(e)); probabilities are rounded to
+// bf16 for the p.V product and the running sum adds the rounded values, so
+// numerator and denominator use the same weights.
+#include <math.h>
+
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kD = 128;          // head_dim handled here
+constexpr int kHeadsPerWG = 4;   // kv heads (= waves) per workgroup
+constexpr float kRescaleSlack = 8.f;   // base-2 headroom of the lazy softmax rescale
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma_qk(const u32x4& k, const u32x4& q, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k),
+                                                 __builtin_bit_cast(bf16x8, q), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_pv(const u32x2& v, const u32x2& p, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, v),
+                                                   __builtin_bit_cast(i16x4, p), c, 0, 0, 0);
+}
+
+// Loads go through a buffer resource per slab (base = the slab's address,
+// lanes add byte offsets); a resource of size 0 yields zeros with no memory
+// access, used for a lookahead past the last block and for block ids outside
+// the pool.  The data is read once per step: nontemporal hint.
+constexpr int kBufferWord3 = 0x00020000;   // raw 32-bit buffer, no format conversion
+constexpr int kNontemporal = 2;            // cache-policy bit of buffer loads
+constexpr int kSlabBytes = kBlock * kD * 2;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const bf16_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(base), 0, bytes, kBufferWord3);
+}
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t rsrc, int byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(rsrc, byte_off, 0, kNontemporal);
+}
+
+// K and V of one (block, kv head) slab as this lane loads them: token 4g+i,
+// columns 8r .. 8r+7 (16 lanes per contiguous 256-byte row).
+struct MfmaSlab {
+  u32x4 k[4];
+  u32x4 v[4];
+};
+
+__device__ __forceinline__ void load_mfma_slab(MfmaSlab& s, __amdgpu_buffer_rsrc_t kr,
+                                               __amdgpu_buffer_rsrc_t vr, int r, int g) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s.k[i] = load16(kr, 2 * ((4 * g + i) * kD + 8 * r));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s.v[i] = load16(vr, 2 * ((4 * g + i) * kD + 8 * r));
+}
+
+// Per-wave LDS tile that turns K around: 16 token rows of 256 bytes, padded.
+constexpr int kKRowBytes = kD * 2 + 16;
+constexpr int kKTileBytes = kBlock * kKRowBytes;
+
+// Orders this wave's LDS accesses around a turn-around (LDS operations of one
+// wave complete in order; this keeps the compiler from moving them).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The low (t even) or high (t odd) bf16 of word w of two registers, packed as
+// (hi_src << 16) | lo_src.
+template <int T>
+__device__ __forceinline__ uint32_t pick_pair(const u32x4& lo_src, const u32x4& hi_src) {
+  const uint32_t sel = (T & 1) ? 0x07060302u : 0x05040100u;
+  const uint32_t lo = lo_src[T / 2];
+  const uint32_t hi = hi_src[T / 2];
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+struct HeadState {
+  float m;        // reference max (base-2 scores) of head r, same in its 4 lanes
+  float lsum;     // this lane's share of the running sum
+  f32x4 o[8];     // O^T tiles: o[t][i] is column 8(4g+i) + t of head r
+};
+
+// Fold one slab into the state.  Tokens at or past nvalid (only in a
+// sequence's last block) are skipped: score -inf, weight 0, and their V rows
+// replaced by zero in place, since they may hold anything and 0 * NaN is NaN.
+// The masking only edits the inputs inside a uniform branch, so the
+// accumulators keep one register assignment.  Token 0 of a block is always
+// valid, so the block max is finite and the first block sets the reference.
+__device__ __forceinline__ void consume_mfma_slab(MfmaSlab& sl, const u32x4 (&qb)[4],
+                                                  float scale_log2, int r, int g, int nvalid,
+                                                  uint8_t* ktile, HeadState& st) {
+  // K into A-operand layout: write row 4g+i / chunk r, read row r / chunk 4ks+g.
+  wave_lds_sync();
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<u32x4*>(ktile + (4 * g + i) * kKRowBytes + 16 * r) = sl.k[i];
+  wave_lds_sync();
+  u32x4 ka[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    ka[ks] = *reinterpret_cast<const u32x4*>(ktile + r * kKRowBytes + 16 * (4 * ks + g));
+
+  f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) sc = mfma_qk(ka[ks], qb[ks], sc);
+
+  float s[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s[i] = sc[i] * scale_log2;
+  if (nvalid < kBlock) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = 4 * g + i < nvalid;
+      s[i] = ok ? s[i] : -INFINITY;
+      sl.v[i] = ok ? sl.v[i] : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+  bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+  // Lazy rescaling: the reference max st.m only moves when a block's max
+  // exceeds it by more than kRescaleSlack, so weights stay <= 2^kRescaleSlack
+  // and the accumulators are rescaled (off the matrix cores) only then --
+  // in practice on the first block and rarely after.  The result does not
+  // depend on the reference: out = o / lsum and lse = st.m + log2(lsum).
+  const bool grow = bm > st.m + kRescaleSlack;
+  if (__ballot(grow) != 0) {
+    const float mn = grow ? bm : st.m;
+    const float alpha = exp2f(st.m - mn);
+    st.lsum *= alpha;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) st.o[t] *= alpha;
+    st.m = mn;
+  }
+  const float mr = st.m;
+  const uint32_t p01 = pack_bf16x2(exp2f(s[0] - mr), exp2f(s[1] - mr));
+  const uint32_t p23 = pack_bf16x2(exp2f(s[2] - mr), exp2f(s[3] - mr));
+  st.lsum += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
+
+  const u32x2 pb = u32x2{p01, p23};
+#define PA_PV_TILE(T)                                                               \
+  st.o[T] = mfma_pv(u32x2{pick_pair<T>(sl.v[0], sl.v[1]), pick_pair<T>(sl.v[2], sl.v[3])}, \
+                    pb, st.o[T]);
+  PA_PV_TILE(0) PA_PV_TILE(1) PA_PV_TILE(2) PA_PV_TILE(3)
+  PA_PV_TILE(4) PA_PV_TILE(5) PA_PV_TILE(6) PA_PV_TILE(7)
+#undef PA_PV_TILE
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t sh_k[kHeadsPerWG][kKTileBytes];
+  const int hgroups = (a.num_kv_heads + kHeadsPerWG - 1) / kHeadsPerWG;
+  const int seq = blockIdx.x / hgroups;
+  const int kvh = (blockIdx.x - seq * hgroups) * kHeadsPerWG + wave_uniform(threadIdx.x >> 6);
+  const int part = blockIdx.y;
+  if (kvh >= a.num_kv_heads) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int G = a.group;
+  const int hq = a.num_heads;
+  bf16_t* out = static_cast<bf16_t*>(a.out);
+
+  const int ctx = a.context_lens[seq];
+  const bool bad = ctx < 0 || ctx > a.max_blocks_per_seq * kBlock ||
+                   (a.partition_blocks > 0 && ctx > a.max_context_len);
+  const int nblk = bad ? 0 : (ctx + kBlock - 1) / kBlock;
+  const bool split = a.partition_blocks > 0;
+  const int nparts = split ? (nblk + a.partition_blocks - 1) / a.partition_blocks : 1;
+  if (part >= (nparts > 0 ? nparts : 1)) return;
+
+  // Degenerate sequences (only partition 0 gets here): no context gives zeros,
+  // a violated contract gives NaN, in the partials too if the merge will read
+  // them.
+  if (bad || ctx == 0) {
+    const float fill = bad ? __builtin_nanf("") : 0.f;
+    if (split && bad && ctx > 0 && ctx <= a.max_context_len) {
+      const int ptok = a.partition_blocks * kBlock;
+      const int np_bad = (ctx + ptok - 1) / ptok;
+      if (np_bad > 1) {
+        for (int i = lane; i < np_bad * G * kD; i += kWave) {
+          const int p = i / (G * kD);
+          const int h = (i / kD) % G;
+          const int64_t row = ((int64_t)seq * hq + kvh * G + h) * a.max_partitions + p;
+          a.part_o[row * kD + i % kD] = fill;
+          if (i % kD == 0) a.part_lse[row] = fill;
+        }
+        return;
+      }
+    }
+    for (int i = lane; i < G * kD; i += kWave)
+      out[((int64_t)seq * hq + kvh * G) * kD + i] = f32_to_bf16(fill);
+    return;
+  }
+
+  const int jb = split ? part * a.partition_blocks : 0;
+  const int je = split ? min(nblk, jb + a.partition_blocks) : nblk;
+  const int tok_end = min(ctx, je * kBlock);
+
+  u32x4 qb[4];
+  const bf16_t* qrow = static_cast<const bf16_t*>(a.query) + ((int64_t)seq * hq + kvh * G + r) * kD;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    qb[ks] = r < G ? *reinterpret_cast<const u32x4*>(qrow + (4 * ks + g) * 8)
+                   : u32x4{0u, 0u, 0u, 0u};
+
+  HeadState st;
+  st.m = -INFINITY;
+  st.lsum = 0.f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) st.o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const bf16_t* kpool = static_cast<const bf16_t*>(a.k_cache);
+  const bf16_t* vpool = static_cast<const bf16_t*>(a.v_cache);
+  const int32_t* table = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
+  const int64_t head_slab = (int64_t)kBlock * kD;
+  uint8_t* ktile = sh_k[kvh % kHeadsPerWG];
+  bool bad_block = false;
+
+  // Blocks jb .. je-1, their ids fetched 64 at a time (lane t holds the t-th)
+  // and broadcast per step.  Two slabs are in flight: the next block's loads
+  // are issued before the current one is consumed, unconditionally
+  // (straight-line code, so each consume waits only for its own slab); past
+  // the last block the resource is empty and the load moves no data.  An id
+  // outside the pool reads as zeros and poisons the result.
+  for (int base = jb; base < je; base += kWave) {
+    const int myb = base + lane < je ? table[base + lane] : 0;
+    const int cnt = min(kWave, je - base);
+    const auto load_step = [&](MfmaSlab& sl, int t) {
+      const int bid = __builtin_amdgcn_readlane(myb, min(t, cnt - 1));
+      const bool in_pool = bid >= 0 && (int64_t)bid < a.num_blocks;
+      bad_block |= t < cnt && !in_pool;
+      const bool live = t < cnt && in_pool;
+      const int64_t off = live ? ((int64_t)bid * a.num_kv_heads + kvh) * head_slab : 0;
+      const int bytes = live ? kSlabBytes : 0;
+      load_mfma_slab(sl, slab_rsrc(kpool + off, bytes), slab_rsrc(vpool + off, bytes), r, g);
+    };
+    const auto consume = [&](MfmaSlab& sl, int t) {
+      const int nvalid = min(kBlock, tok_end - (base + t) * kBlock);
+      consume_mfma_slab(sl, qb, a.scale_log2, r, g, nvalid, ktile, st);
+    };
+    MfmaSlab sa, sb;
+    load_step(sa, 0);
+    for (int t = 0; t < cnt; t += 2) {
+      load_step(sb, t + 1);
+      consume(sa, t);
+      if (t + 1 >= cnt) break;
+      load_step(sa, t + 2);
+      consume(sb, t + 1);
+    }
+  }
+
+  // Head r's full sum is spread over its 4 lanes.  bad_block is the same in
+  // every lane (block ids are broadcast).
+  float lsum = st.lsum;
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  const bool poisoned = __builtin_amdgcn_readfirstlane((int)bad_block) != 0;
+  if (r >= G) return;
+  const float inv = 1.f / lsum;
+  const int h = kvh * G + r;
+  if (nparts <= 1) {
+    bf16_t* dst = out + ((int64_t)seq * hq + h) * kD;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u32x4 w;
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        w[x] = poisoned ? 0x7FC07FC0u
+                        : pack_bf16x2(st.o[2 * x][i] * inv, st.o[2 * x + 1][i] * inv);
+      *reinterpret_cast<u32x4*>(dst + 8 * (4 * g + i)) = w;
+    }
+  } else {
+    const int64_t row = ((int64_t)seq * hq + h) * a.max_partitions + part;
+    float* dst = a.part_o + row * kD;
+    const float nan = __builtin_nanf("");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4 lo, hi;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        lo[x] = poisoned ? nan : st.o[x][i] * inv;
+        hi[x] = poisoned ? nan : st.o[4 + x][i] * inv;
+      }
+      *reinterpret_cast<f32x4*>(dst + 8 * (4 * g + i)) = lo;
+      *reinterpret_cast<f32x4*>(dst + 8 * (4 * g + i) + 4) = hi;
+    }
+    if (g == 0) a.part_lse[row] = poisoned ? nan : (st.m + log2f(lsum)) * kLn2;
+  }
+}
+
+hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, hipStream_t stream) {
+  if (a.num_items == 0) return hipSuccess;
+  const int hgroups = (a.num_kv_heads + kHeadsPerWG - 1) / kHeadsPerWG;
+  dim3 grid((unsigned)((int64_t)a.num_items * hgroups),
+            a.partition_blocks > 0 ? a.max_partitions : 1);
+  hipLaunchKernelGGL(decode_gqa_mfma_kernel, grid, dim3(64 * kHeadsPerWG), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -59,6 +59,7 @@ struct ReduceArgs {
 
 hipError_t launch_reshape_and_cache(const ScatterArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t stream);
+hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_splitk_reduce(const ReduceArgs& a, int head_dim, bool bf16, hipStream_t stream);
 hipError_t launch_prefill_mfma(const DecodeArgs& a, int head_dim, hipStream_t stream);
 

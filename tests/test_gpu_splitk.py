@@ -37,9 +37,13 @@ def test_partials_match_oracle(gpu, dtype, hq, hkv):
         if n[s] <= 1:
             continue   # written straight to the output, no partials
         assert_close(o_part[s, :, :n[s]], ro[s, :, :n[s]], dtype, f"o_part seq {s}")
-        # lse: scores from fp32 dot products of 128 terms; 1e-4 absolute covers their rounding
+        # lse: scores come from fp32 dot products of 128 terms; 1e-4 absolute covers
+        # their rounding.  The bf16 matrix-core path also rounds each probability
+        # to bf16 (relative error <= 2^-8) and sums the rounded weights, which
+        # moves the log of the sum by at most ln(1 + 2^-8) < 3.9e-3.
+        lse_atol = 1e-4 if dtype == "f32" else 1e-4 + 3.9e-3
         err = np.abs(lse[s, :, :n[s]].astype(np.float64) - rl[s, :, :n[s]])
-        assert (err <= 1e-4 + 1e-5 * np.abs(rl[s, :, :n[s]])).all(), err.max()
+        assert (err <= lse_atol + 1e-5 * np.abs(rl[s, :, :n[s]])).all(), err.max()
     assert_close(as_f64(g.out), oracle_decode(w), dtype, "merged")
 
 
