@@ -78,4 +78,14 @@ __device__ __forceinline__ float xor_sum_above(float x) {
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also releases global
+// memory, which makes every wave wait for all of its outstanding global loads
+// (vmcnt 0) at the barrier; a kernel that prefetches the next tile from global
+// memory while computing on LDS must not pay that.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 }  // namespace pa
