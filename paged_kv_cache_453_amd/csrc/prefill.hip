@@ -33,8 +33,10 @@
 // Softmax in base 2 with lazy rescaling: a row's reference max moves only when
 // a tile's max exceeds it by more than 8, so the accumulators are rarely
 // touched by the vector ALUs.  Probabilities are rounded to bf16 for the p.V
-// product and the running sum adds the rounded values, so numerator and
-// denominator use the same weights.
+// product, and the running sum is taken over the same rounded values -- on
+// the matrix cores, as the product of an all-ones operand with P^T -- so
+// numerator and denominator use the same weights.  exp2 is the raw hardware
+// instruction: weights below 2^-126 flush to zero, which a softmax ignores.
 #include <math.h>
 
 #include "pa_device.h"
@@ -47,6 +49,8 @@ namespace {
 constexpr int kKeys = 64;             // keys per tile (4 blocks)
 constexpr int kBufferWord3 = 0x00020000;   // raw 32-bit buffer resource, no format conversion
 constexpr float kSlack = 8.f;         // base-2 headroom of the lazy rescale
+// bf16 1.0 in every slot: A operand whose product with P^T is the row sums
+constexpr u32x4 kOnes = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 
 __device__ __forceinline__ f32x4 mfma_16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -214,11 +218,12 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
   };
 
   f32x4 o[QB][DT];
-  float mref[QB], lsum[QB];
+  f32x4 lacc[QB];      // every element: the row's running sum of weights
+  float mref[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     mref[qb] = -INFINITY;
-    lsum[qb] = 0.f;
+    lacc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < DT; ++t) o[qb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -257,33 +262,38 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
       }
 
       // ---- online softmax; lane holds S[row 16qb + r][key tile_first + 16nt + 4g + i] ----
+      // The common path needs no cross-lane step: each lane checks its own
+      // max against the row's reference, and only if some lane of the wave
+      // exceeds it by more than kSlack is the row max gathered and the
+      // reference moved (rare after the first tile).
       u32x4 pk[2][QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const int qpos = wave_first_pos + 16 * qb + r;
-        float tmax = -INFINITY;
+        if (need_mask) {
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              sc[qb][nt][i] = (tile_first + 16 * nt + 4 * g + i <= qpos) ? sc[qb][nt][i] : -INFINITY;
+        }
+        float lmax = -INFINITY;
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float v = sc[qb][nt][i] * sl2;
-            if (need_mask) v = (tile_first + 16 * nt + 4 * g + i <= qpos) ? v : -INFINITY;
-            sc[qb][nt][i] = v;
-            tmax = fmaxf(tmax, v);
-          }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const bool grow = tmax > mref[qb] + kSlack;
-        if (__ballot(grow) != 0) {
-          const float mn = grow ? tmax : mref[qb];
-          const float alpha = exp2f(mref[qb] - mn);
-          lsum[qb] *= alpha;
+          lmax = fmaxf(lmax, fmaxf(fmaxf(sc[qb][nt][0], sc[qb][nt][1]),
+                                   fmaxf(sc[qb][nt][2], sc[qb][nt][3])));
+        lmax *= sl2;
+        if (__ballot(lmax > mref[qb] + kSlack) != 0) {
+          float rmax = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
+          rmax = fmaxf(rmax, __shfl_xor(rmax, 32, 64));
+          const float mn = rmax > mref[qb] + kSlack ? rmax : mref[qb];
+          const float alpha = __builtin_amdgcn_exp2f(mref[qb] - mn);
+          lacc[qb] *= alpha;
 #pragma unroll
           for (int t = 0; t < DT; ++t) o[qb][t] *= alpha;
           mref[qb] = mn;
         }
-        const float mr = mref[qb];
-        float ls = 0.f;
+        const float nmr = -mref[qb];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           uint32_t wv[4];
@@ -291,12 +301,13 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
           for (int x = 0; x < 4; ++x) {
             const f32x4& sv = sc[qb][2 * kk + x / 2];
             const int i0 = 2 * (x % 2);
-            wv[x] = pack_bf16x2(exp2f(sv[i0] - mr), exp2f(sv[i0 + 1] - mr));
-            ls += bf16_lo(wv[x]) + bf16_hi(wv[x]);
+            wv[x] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sv[i0], sl2, nmr)),
+                                __builtin_amdgcn_exp2f(fmaf(sv[i0 + 1], sl2, nmr)));
           }
           pk[kk][qb] = u32x4{wv[0], wv[1], wv[2], wv[3]};
+          // row sum of the rounded weights on the matrix cores: all-ones A operand
+          lacc[qb] = mfma_16x16x32(kOnes, pk[kk][qb], lacc[qb]);
         }
-        lsum[qb] += ls;
       }
 
       // ---- O^T += V^T P^T, 32 keys per step ----
@@ -328,9 +339,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
   const bool poisoned = sh_bad != 0;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    float l = lsum[qb];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    const float l = lacc[qb][0];
     const int qi = qw0 + 16 * qb + r;
     if (qi >= chunk) continue;
     const float inv = 1.f / l;
