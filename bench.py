@@ -1,15 +1,25 @@
-"""Benchmark of the paged-attention decode step at Llama-2-13B shape on one GPU.
+"""Benchmark of the paged-attention hot path on one GPU.
 
-One step = reshape_and_cache of the 256 newest tokens, then paged decode of
-256 sequences (40 query heads = 40 kv heads, head_dim 128, bf16 cache, block
-size 16, lognormal context lengths with median 1024 clipped to [16, 4096],
-65536-block shuffled pool) with split-K partitions and their merge.  Inputs are
-seeded synthetic data already resident in GPU memory before timing starts.
+Default workload (the metric's configuration), one step = reshape_and_cache of
+the 256 newest tokens, then paged decode of 256 sequences at Llama-2-13B shape
+(40 query heads = 40 kv heads, head_dim 128, bf16 cache, block size 16,
+lognormal context lengths with median 1024 clipped to [16, 4096], 65536-block
+shuffled pool) with split-K partitions and their merge.
 
-Prints one JSON line: KV GB/s over the whole step (the metric), % of the 8 TB/s
-HBM peak, tokens/s for one layer, the decode kernel's roofline position
-(algorithmic KV bytes / its own launch time, from HIP events on the launch
-stream), and the fp64 CPU oracle timed on a sample of the same workload.
+--workload selects the other shapes the hot path is measured on:
+  llama7b   decode of 64 sequences, 32 = 32 heads, lengths U[128, 2048]
+  gqa       decode of 32 sequences, 32 query heads over 8 kv heads, lengths
+            U[8192, 32768], 512-token split-K partitions + merge
+  mixed     chunked prefill of 4 x 512-token chunks over paged prefixes, then
+            decode of 192 sequences sharing 2048-token prefixes in groups of 3
+            (also timed with prefill and decode on two streams)
+
+Inputs are seeded synthetic data already resident in GPU memory before timing
+starts.  Prints one JSON line: KV GB/s over the whole step (the metric), % of
+the 8 TB/s HBM peak, tokens/s for one layer, the dominant kernel's roofline
+position (algorithmic bytes or flops / its own launch time, from HIP events on
+the launch stream), and the fp64 CPU oracle timed on a sample of the same
+workload.
 """
 from __future__ import annotations
 
@@ -25,6 +35,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "paged-attn decode KV GB/s (% of HBM peak) + tokens/s at Llama-2-13B shape"
 COUNTERS = os.path.join(ROOT, "profiles", "decode_llama13b_counters.json")
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_453_amd", "csrc", "decode.hip")
@@ -53,31 +64,54 @@ def measured_traffic(per_launch_algo_bytes: float):
 
 
 def cpu_baseline(w, budget_s: float = 10.0):
-    """The fp64 oracle on the first sequences of the same workload, one thread."""
-    import numpy as np
+    """The fp64 oracle on a bounded sample of the same workload, one host thread.
+
+    Decode: the first sequences in order (scatter included where the workload
+    has one) until budget_s of CPU time.  Prefill (mixed workload): the first
+    chunk first, then decode sequences.  Reported in the metric's unit, KV GB/s
+    of decode over the sample.
+    """
     from threadpoolctl import threadpool_limits
 
     import oracle
     from workloads import accounting
 
-    k, v = oracle.reshape_and_cache(w.k_host, w.v_host, w.new_k, w.new_v, w.host_slots())
-    g = w.decode
-    tables = w.host_tables(g.block_tables)
-    done, t_total = 0, 0.0
+    k, v = w.k_host, w.v_host
+    t_total = 0.0
+    notes = []
     with threadpool_limits(1):
-        while done < g.num_seqs and t_total < budget_s:
+        if w.slot_mapping is not None:
+            t0 = time.perf_counter()
+            k, v = oracle.reshape_and_cache(k, v, w.new_k, w.new_v, w.host_slots())
+            t_total += time.perf_counter() - t0
+            notes.append(f"scatter of {len(w.slot_mapping)} tokens")
+        if w.prefill is not None:
+            p = w.prefill
+            qsl = p.query_start_loc
+            t0 = time.perf_counter()
+            oracle.prefill(p.query[qsl[0]:qsl[1]], k, v, w.host_tables(p.block_tables[:1]),
+                           qsl[:2] - qsl[0], p.context_lens[:1], w.scale, w.dtype)
+            dt = time.perf_counter() - t0
+            t_total += dt
+            notes.append(f"prefill of the first {int(qsl[1] - qsl[0])}-token chunk "
+                         f"({dt:.1f} s)")
+        g = w.decode
+        tables = w.host_tables(g.block_tables)
+        done, t_dec = 0, 0.0
+        while done < g.num_seqs and t_total + t_dec < budget_s:
             hi = min(g.num_seqs, done + 8)
             t0 = time.perf_counter()
-            oracle.decode(g.query[done:hi], k, v, tables[done:hi], g.context_lens[done:hi], w.scale,
-                          w.dtype)
-            t_total += time.perf_counter() - t0
+            oracle.decode(g.query[done:hi], k, v, tables[done:hi], g.context_lens[done:hi],
+                          w.scale, w.dtype)
+            t_dec += time.perf_counter() - t0
             done = hi
     kv = accounting.decode_kv_bytes(g.context_lens[:done], w.num_kv_heads, w.head_dim,
                                     w.elem_bytes)
-    return {"value": round(kv / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"fp64 numpy oracle decode (scatter excluded) of the first {done} of "
-                      f"{g.num_seqs} sequences, {int(g.context_lens[:done].sum())} tokens, "
-                      f"{t_total:.1f} s on 1 host thread"}
+    notes.append(f"decode of the first {done} of {g.num_seqs} sequences "
+                 f"({int(g.context_lens[:done].sum())} tokens, {t_dec:.1f} s)")
+    return {"value": round(kv / t_dec / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "fp64 numpy oracle on 1 host thread: " + "; ".join(notes) +
+                      "; value = decode KV bytes / decode time"}
 
 
 def _counter_rows(path: str, kernel_prefix: str):
@@ -147,12 +181,79 @@ def copy_calibration(torch, dev, nbytes: int = 1 << 30, reps: int = 3) -> int:
     return 0
 
 
+class StepTimer:
+    """Times launches with HIP events recorded on the stream each launch uses."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def per_step(self, step, steps: int, streams) -> float:
+        """Milliseconds per step of `step()` over `steps` calls, all streams joined."""
+        torch = self.torch
+        main = streams[0]
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(main)
+        for _ in range(steps):
+            step()
+        for s in streams[1:]:
+            e = torch.cuda.Event()
+            e.record(s)
+            main.wait_event(e)
+        b.record(main)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    def per_launch(self, launches, steps: int, stream):
+        """Average milliseconds of each launch in `launches` (name, fn) run in order
+        on one stream, from events recorded on that stream around each launch."""
+        torch = self.torch
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)]
+               for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            evs[i][0].record(stream)
+            for k, (_, fn) in enumerate(launches):
+                fn()
+                evs[i][k + 1].record(stream)
+        torch.cuda.synchronize()
+        return {name: sum(e[k].elapsed_time(e[k + 1]) for e in evs) / steps
+                for k, (name, _) in enumerate(launches)}
+
+
+WORKLOADS = ("llama13b", "llama7b", "gqa", "mixed")
+
+
+def build_workload(name: str, ps: int):
+    from workloads import config1, config2, config3, config4
+    if name == "llama13b":
+        return config2(partition_size=ps), {
+            "workload": "llama2-13b-shaped paged decode (scatter + decode + split-K merge)",
+            "context_lens": "lognormal median 1024 sigma 0.5 clipped [16,4096]", "seed": 455}
+    if name == "llama7b":
+        return config1(partition_size=ps), {
+            "workload": "llama2-7b-shaped paged decode (decode + split-K merge)",
+            "context_lens": "uniform [128,2048]", "seed": 454}
+    if name == "gqa":
+        return config3(partition_size=ps), {
+            "workload": "llama3-8b-shaped GQA long-context paged decode (decode + split-K merge)",
+            "context_lens": "uniform [8192,32768]", "seed": 456}
+    return config4(partition_size=ps), {
+        "workload": "mixed chunked prefill + shared-prefix paged decode",
+        "prefill": "4 x 512-token causal chunks over paged prefixes U{0..3584}",
+        "decode": "64 prompts x 3 samples sharing 2048-token prefixes + U{0..512} private",
+        "seed": 457}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--partition-size", type=int, default=2048)
+    ap.add_argument("--workload", choices=WORKLOADS, default="llama13b")
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="split-K partition length in tokens (default: 2048 for the Llama "
+                         "shapes, 512 for gqa as its configuration states, 2048 for mixed)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead (for scaling the "
@@ -173,7 +274,7 @@ def main(argv=None):
     import torch
 
     from paged_kv_cache_453_amd import lib
-    from workloads import accounting, config2
+    from workloads import accounting
     from workloads.device import to_device
 
     dev = torch.device("cuda:0")
@@ -182,10 +283,12 @@ def main(argv=None):
         return copy_calibration(torch, dev)
     lib.load()
     ps = args.partition_size
+    if ps is None:
+        ps = 512 if args.workload == "gqa" else 2048
 
-    log("bench: generating the Llama-2-13B-shaped decode workload")
+    log(f"bench: generating the {args.workload} workload")
     t0 = time.time()
-    w = config2(partition_size=ps)
+    w, cfg = build_workload(args.workload, ps)
     g = w.decode
     log(f"bench: generated in {time.time() - t0:.1f} s; uploading")
     dw = to_device(w, device=dev)
@@ -194,62 +297,124 @@ def main(argv=None):
                                              g.max_context_len, ps)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
-
     stream = torch.cuda.current_stream()
+    timer = StepTimer(torch)
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        lib.pa_reshape_and_cache(dw.new_k, dw.new_v, dw.k_cache, dw.v_cache, dw.slot_mapping)
-        if ev is not None:
-            ev[1].record(stream)
-        lib.pa_decode(dg.out, dg.query, dw.k_cache, dw.v_cache, dg.block_tables, dg.context_lens,
-                      w.scale, g.max_context_len, ps, ws if ps else None)
-        if ev is not None:
-            ev[2].record(stream)
+    def scatter():
+        lib.pa_reshape_and_cache(dw.new_k, dw.new_v, dw.k_cache, dw.v_cache, dw.slot_mapping,
+                                 stream=stream)
+
+    def decode(s=stream):
+        lib.pa_decode(dg.out, dg.query, dw.k_cache, dw.v_cache, dg.block_tables,
+                      dg.context_lens, w.scale, g.max_context_len, ps, ws if ps else None,
+                      stream=s)
+
+    def reduce(s=stream):
         if ps:
-            lib.pa_decode_splitk_reduce(dg.out, ws, dg.context_lens, g.max_context_len, ps)
-        if ev is not None:
-            ev[3].record(stream)
+            lib.pa_decode_splitk_reduce(dg.out, ws, dg.context_lens, g.max_context_len, ps,
+                                        stream=s)
+
+    def prefill(s=stream):
+        p = dw.prefill
+        lib.pa_prefill_chunk(p.out, p.query, dw.k_cache, dw.v_cache, p.block_tables,
+                             p.query_start_loc, p.context_lens, w.scale, p.max_query_len,
+                             stream=s)
+
+    launches = []
+    if w.slot_mapping is not None:
+        launches.append(("reshape_and_cache", scatter))
+    if w.prefill is not None:
+        launches.append(("prefill", prefill))
+    launches.append(("decode", decode))
+    if ps:
+        launches.append(("splitk_reduce", reduce))
+
+    def step():
+        for _, fn in launches:
+            fn()
 
     log(f"bench: warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-
-    # whole-step timing
     log(f"bench: timing {args.steps} steps")
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(stop) / args.steps
-
-    # per-kernel launch durations over a second timed pass, events on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    scatter_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    decode_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    reduce_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
-    log(f"bench: step {ms_per_step * 1e3:.1f} us (scatter {scatter_ms * 1e3:.1f}, decode "
-        f"{decode_ms * 1e3:.1f}, reduce {reduce_ms * 1e3:.1f})")
+    ms_per_step = timer.per_step(step, args.steps, [stream])
+    kernel_ms = timer.per_launch(launches, args.steps, stream)
+    log("bench: step %.1f us (%s)" % (ms_per_step * 1e3, ", ".join(
+        f"{k} {v * 1e3:.1f}" for k, v in kernel_ms.items())))
 
     kv = accounting.decode_kv_bytes(g.context_lens, w.num_kv_heads, w.head_dim, w.elem_bytes)
     gbs = kv / (ms_per_step * 1e-3) / 1e9
-    decode_gbs = kv / (decode_ms * 1e-3) / 1e9
-    traffic = measured_traffic(kv)
+    decode_gbs = kv / (kernel_ms["decode"] * 1e-3) / 1e9
+    tokens = g.num_seqs
+    extra = {}
+    group = w.num_heads // w.num_kv_heads
+    dec_kernel = ("decode_gqa_mfma_kernel" if group >= 4 else
+                  f"decode_valu_kernel<bf16,{w.head_dim},{group}>")
+    roofline = {"bound": "hbm", "achieved": round(decode_gbs, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(decode_gbs / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(kv) if args.workload == "llama13b" else None,
+                "kernel": dec_kernel, "algorithmic_bytes_per_launch": int(kv)}
+
+    if w.prefill is not None:
+        p = w.prefill
+        flops = accounting.prefill_flops(p.query_start_loc, p.context_lens, w.num_heads,
+                                         w.head_dim)
+        unique = accounting.unique_kv_bytes(g.block_tables, g.context_lens, w.num_kv_heads,
+                                            w.head_dim, w.elem_bytes)
+        tokens += int(p.query_start_loc[-1])
+        pf_tflops = flops / (kernel_ms["prefill"] * 1e-3) / 1e12
+        unique_gbs = unique / (kernel_ms["decode"] * 1e-3) / 1e9
+        # the decode of shared prefixes must read each physical row once at least
+        roofline.update({"achieved": round(unique_gbs, 2),
+                         "frac": round(unique_gbs / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes_per_launch": int(unique),
+                         "logical_bytes_per_launch": int(kv),
+                         "logical_gbs": round(decode_gbs, 2),
+                         "note": "achieved = unique (physical) KV bytes / decode time; "
+                                 "logical bytes count shared prefix rows once per sequence"})
+        extra["roofline_prefill"] = {
+            "bound": "mfma", "achieved": round(pf_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(pf_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None, "kernel": "prefill_mfma_kernel<128,32>",
+            "algorithmic_flops_per_launch": int(flops)}
+        extra["prefill_tokens_per_step"] = int(p.query_start_loc[-1])
+        extra["prefixes"] = w.meta.get("prefixes")
+
+        # the same step with prefill (matrix cores) and decode (HBM) on two streams
+        side = torch.cuda.Stream(device=dev)
+
+        def step_overlap():
+            fork = torch.cuda.Event()
+            fork.record(stream)
+            side.wait_event(fork)
+            prefill(side)
+            decode(stream)
+            join = torch.cuda.Event()
+            join.record(side)
+            stream.wait_event(join)
+            reduce(stream)
+
+        for _ in range(args.warmup):
+            step_overlap()
+        ms_overlap = timer.per_step(step_overlap, args.steps, [stream, side])
+        extra["overlapped_two_streams"] = {
+            "ms_per_step": round(ms_overlap, 5),
+            "kv_gbs_logical": round(kv / (ms_overlap * 1e-3) / 1e9, 2),
+            "tokens_per_s": round(tokens / (ms_overlap * 1e-3), 1)}
+        log(f"bench: overlapped step {ms_overlap * 1e3:.1f} us")
 
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a sample")
         cpu = cpu_baseline(w)
 
+    config = {"workload": cfg.pop("workload"), "num_seqs": g.num_seqs,
+              "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
+              "head_dim": w.head_dim, "block_size": 16,
+              "total_context_tokens": int(g.context_lens.sum()),
+              "num_blocks": w.num_blocks, "partition_size": ps}
+    config.update(cfg)
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -264,24 +429,16 @@ def main(argv=None):
         "dtype": "bf16",
         "data": "synthetic",
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
-        "tokens_per_s": round(g.num_seqs / (ms_per_step * 1e-3), 1),
-        "tokens_per_s_note": "one decode token per sequence per step, one attention layer",
+        "tokens_per_s": round(tokens / (ms_per_step * 1e-3), 1),
+        "tokens_per_s_note": "one decode token per sequence (plus the prefill chunk tokens "
+                             "where present) per step, one attention layer",
         "kv_bytes_per_step": int(kv),
-        "kernel_us": {"reshape_and_cache": round(scatter_ms * 1e3, 2),
-                      "decode": round(decode_ms * 1e3, 2),
-                      "splitk_reduce": round(reduce_ms * 1e3, 2)},
-        "config": {"workload": "llama2-13b-shaped paged decode (scatter + decode + split-K merge)",
-                   "num_seqs": g.num_seqs, "num_heads": w.num_heads,
-                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": 16,
-                   "context_lens": "lognormal median 1024 sigma 0.5 clipped [16,4096]",
-                   "total_context_tokens": int(g.context_lens.sum()),
-                   "num_blocks": w.num_blocks, "partition_size": ps, "seed": 455},
-        "roofline": {"bound": "hbm", "achieved": round(decode_gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(decode_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "decode_valu_kernel<bf16,128,1>",
-                     "algorithmic_bytes_per_launch": int(kv)},
+        "kernel_us": {k: round(v * 1e3, 2) for k, v in kernel_ms.items()},
+        "config": config,
+        "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    result.update(extra)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -31,7 +31,8 @@
 // sequence's last, partly filled block pays for them.
 //
 // Scores are kept in base 2: q is pre-multiplied by scale*log2(e), so softmax
-// weights are exp2(s - m).
+// weights are exp2(s - m), taken with the raw v_exp_f32 inside the block loop
+// (weights below 2^-126 flush to zero, which a softmax ignores).
 #include <math.h>
 
 #include "pa_device.h"
@@ -190,13 +191,13 @@ __device__ __forceinline__ void consume_slab(
       if (valid[i]) bm = fmaxf(bm, s[g][i]);
     const float mn = fmaxf(m[g], bm);
     // with masking, mn stays -inf while this row group has seen no token
-    const float alpha = (MASKED && mn == -INFINITY) ? 1.f : exp2f(m[g] - mn);
+    const float alpha = (MASKED && mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m[g] - mn);
     float lsum = l[g] * alpha;
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[g][e] *= alpha;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      p[g][i] = valid[i] ? exp2f(s[g][i] - mn) : 0.f;
+      p[g][i] = valid[i] ? __builtin_amdgcn_exp2f(s[g][i] - mn) : 0.f;
       lsum += p[g][i];
     }
     l[g] = lsum;

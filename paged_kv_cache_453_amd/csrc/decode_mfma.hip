@@ -162,26 +162,30 @@ __device__ __forceinline__ void consume_mfma_slab(MfmaSlab& sl, const u32x4 (&qb
       sl.v[i] = ok ? sl.v[i] : u32x4{0u, 0u, 0u, 0u};
     }
   }
-  float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-  bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-  bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-  // Lazy rescaling: the reference max st.m only moves when a block's max
-  // exceeds it by more than kRescaleSlack, so weights stay <= 2^kRescaleSlack
-  // and the accumulators are rescaled (off the matrix cores) only then --
-  // in practice on the first block and rarely after.  The result does not
-  // depend on the reference: out = o / lsum and lse = st.m + log2(lsum).
-  const bool grow = bm > st.m + kRescaleSlack;
-  if (__ballot(grow) != 0) {
-    const float mn = grow ? bm : st.m;
-    const float alpha = exp2f(st.m - mn);
+  // Lazy rescaling: the reference max st.m only moves when a score exceeds it
+  // by more than kRescaleSlack, so weights stay <= 2^kRescaleSlack and the
+  // accumulators are rescaled only then -- in practice on the first block and
+  // rarely after.  Each lane checks its own 4 scores and the wave votes; the
+  // head's max over its 4 lanes is gathered only inside that rare branch.
+  // The result does not depend on the reference: out = o / lsum and
+  // lse = st.m + log2(lsum).
+  const float lmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  if (__ballot(lmax > st.m + kRescaleSlack) != 0) {
+    float bm = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
+    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+    const float mn = bm > st.m + kRescaleSlack ? bm : st.m;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - mn);
     st.lsum *= alpha;
 #pragma unroll
     for (int t = 0; t < 8; ++t) st.o[t] *= alpha;
     st.m = mn;
   }
+  // raw v_exp_f32: weights below 2^-126 flush to zero, which a softmax ignores
   const float mr = st.m;
-  const uint32_t p01 = pack_bf16x2(exp2f(s[0] - mr), exp2f(s[1] - mr));
-  const uint32_t p23 = pack_bf16x2(exp2f(s[2] - mr), exp2f(s[3] - mr));
+  const uint32_t p01 = pack_bf16x2(__builtin_amdgcn_exp2f(s[0] - mr),
+                                   __builtin_amdgcn_exp2f(s[1] - mr));
+  const uint32_t p23 = pack_bf16x2(__builtin_amdgcn_exp2f(s[2] - mr),
+                                   __builtin_amdgcn_exp2f(s[3] - mr));
   st.lsum += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
 
   const u32x2 pb = u32x2{p01, p23};
