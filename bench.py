@@ -38,7 +38,9 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "paged-attn decode KV GB/s (% of HBM peak) + tokens/s at Llama-2-13B shape"
 COUNTERS = os.path.join(ROOT, "profiles", "decode_llama13b_counters.json")
-DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_453_amd", "csrc", "decode.hip")
+# sources the measured decode kernel is compiled from
+DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_453_amd", "csrc", f)
+               for f in ("decode_valu.h", "decode_valu_bf16.hip", "pa_device.h")]
 
 
 def log(*a):
@@ -46,8 +48,11 @@ def log(*a):
 
 
 def source_digest() -> str:
-    with open(DECODE_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in DECODE_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(per_launch_algo_bytes: float):
@@ -129,10 +134,11 @@ def digest_counters(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_wr
     what the same counter reads for a plain copy of copy_bytes (which reads and
     writes exactly copy_bytes), so the result is in true bytes whatever share of
     the memory channels the counter sees.  Writes the committed summary that
-    bench.py reports as roofline.traffic while decode.hip is unchanged.
+    bench.py reports as roofline.traffic while the decode kernel sources are
+    unchanged.
     """
     import statistics
-    dec = "void pa::decode_valu_kernel<unsigned short, 128, 1>"
+    dec = "void pa::decode_valu_kernel<unsigned short, 128, 1, false>"
     copy = "__amd_rocclr_copyBuffer"
     f_dec = statistics.mean(_counter_rows(fetch_csv, dec))
     w_dec = statistics.mean(_counter_rows(write_csv, dec))
@@ -307,7 +313,7 @@ def main(argv=None):
     def decode(s=stream):
         lib.pa_decode(dg.out, dg.query, dw.k_cache, dw.v_cache, dg.block_tables,
                       dg.context_lens, w.scale, g.max_context_len, ps, ws if ps else None,
-                      stream=s)
+                      stream=s, shared_prefix_blocks=dg.shared_prefix_blocks)
 
     def reduce(s=stream):
         if ps:
@@ -379,6 +385,10 @@ def main(argv=None):
             "traffic": None, "kernel": "prefill_mfma_kernel<128,32>",
             "algorithmic_flops_per_launch": int(flops)}
         extra["prefill_tokens_per_step"] = int(p.query_start_loc[-1])
+        # a rate against the HBM peak must count each physical row once
+        extra["kv_gbs_logical"] = round(gbs, 2)
+        extra["kv_bytes_unique_per_step"] = int(unique)
+        gbs = unique / (ms_per_step * 1e-3) / 1e9
         extra["prefixes"] = w.meta.get("prefixes")
 
         # the same step with prefill (matrix cores) and decode (HBM) on two streams
@@ -433,6 +443,9 @@ def main(argv=None):
         "tokens_per_s_note": "one decode token per sequence (plus the prefill chunk tokens "
                              "where present) per step, one attention layer",
         "kv_bytes_per_step": int(kv),
+        "value_note": "KV bytes of the step / step time" + (
+            "; unique (physical) bytes: shared prefix rows count once"
+            if w.prefill is not None else ""),
         "kernel_us": {k: round(v * 1e3, 2) for k, v in kernel_ms.items()},
         "config": config,
         "roofline": roofline,

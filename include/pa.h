@@ -102,6 +102,15 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int 
  *                 ceil(context_lens[s] / block_size) are never read.
  *  context_lens   int32 [num_seqs]: cached tokens of each sequence, the newest
  *                 included (scatter it first).  0 gives a zero output.
+ *  shared_prefix_blocks  optional (NULL = none), int32 [num_seqs]: how many
+ *                 leading entries of each sequence's block table name physical
+ *                 blocks that other sequences of this call also read -- the
+ *                 prompt blocks that forked samples keep in common ("vLLM 基本原理",
+ *                 section 内存共享) or a cached prefix (xdnf.cn article, section
+ *                 六.3).  A performance hint only: those blocks are read with
+ *                 the default cache policy so that sequences reading them at the
+ *                 same time hit in L2, the others are streamed past the caches.
+ *                 Any value (negative, or past the table) gives the same result.
  *  scale          softmax scale (usually 1/sqrt(head_dim)).
  *  partition_size 0: one pass per sequence writes out directly.  Otherwise a
  *                 multiple of block_size: the context is cut into partitions of
@@ -116,7 +125,8 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int 
  *                 NULL when partition_size == 0.
  */
 int pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
-              const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+              const int32_t* block_tables, const int32_t* context_lens,
+              const int32_t* shared_prefix_blocks, int num_seqs,
               int num_heads, int num_kv_heads, int head_dim, int block_size,
               int max_blocks_per_seq, int64_t num_blocks, int max_context_len, float scale,
               int partition_size, void* workspace, size_t workspace_bytes, pa_dtype dtype,

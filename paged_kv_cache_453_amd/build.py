@@ -1,7 +1,8 @@
 """Build the paged-attention shared library (libpa.so) for gfx950 with hipcc.
 
-Compiles the HIP kernels and the C-ABI host code in csrc/ into one shared
-library next to this file.  Every call rebuilds.
+Compiles the HIP kernels and the C-ABI host code in csrc/ (one object per
+source, in parallel, under _build/) and links them into one shared library
+next to this file.  Every call rebuilds.
 """
 from __future__ import annotations
 
@@ -17,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpa.so")
 ARCH = "gfx950"
 
-SOURCES = ["pa_api.cpp", "reshape_and_cache.hip", "decode.hip", "decode_mfma.hip", "prefill.hip"]
+SOURCES = ["pa_api.cpp", "reshape_and_cache.hip", "decode.hip", "decode_valu_bf16.hip",
+           "decode_valu_f32.hip", "decode_mfma.hip", "prefill.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}",
@@ -44,10 +46,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the ROCm toolchain is required to build libpa.so")
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", *srcs, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -57,6 +56,28 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object in parallel, then link libpa.so."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    cc = hipcc()
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    jobs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        cmd = [cc, *compile_flags, f"-I{INCLUDE}", f"-I{CSRC}", "-c",
+               os.path.join(CSRC, src), "-o", obj]
+        jobs.append((cmd, obj))
+    workers = max(1, min(len(jobs), os.cpu_count() or 1))
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(lambda j: _run(j[0], verbose), jobs))
+    tmp = LIB + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *[o for _, o in jobs], "-o", tmp],
+         verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -47,6 +47,8 @@
 // numerator and denominator use the same weights.
 #include <math.h>
 
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -72,16 +74,20 @@ __device__ __forceinline__ f32x4 mfma_pv(const u32x2& v, const u32x2& p, const f
 // Loads go through a buffer resource per slab (base = the slab's address,
 // lanes add byte offsets); a resource of size 0 yields zeros with no memory
 // access, used for a lookahead past the last block and for block ids outside
-// the pool.  The data is read once per step: nontemporal hint.
+// the pool.  Blocks only this sequence reads are streamed (nontemporal hint);
+// blocks the caller marks as shared with other sequences use the default
+// policy so that concurrent sharers hit in L2.
 constexpr int kBufferWord3 = 0x00020000;   // raw 32-bit buffer, no format conversion
-constexpr int kNontemporal = 2;            // cache-policy bit of buffer loads
+constexpr int kStreamPolicy = 2;           // cache-policy bits: nontemporal
+constexpr int kSharedPolicy = 0;           // cache-policy bits: default
 constexpr int kSlabBytes = kBlock * kD * 2;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const bf16_t* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(base), 0, bytes, kBufferWord3);
 }
+template <int POLICY>
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t rsrc, int byte_off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(rsrc, byte_off, 0, kNontemporal);
+  return __builtin_amdgcn_raw_buffer_load_b128(rsrc, byte_off, 0, POLICY);
 }
 
 // K and V of one (block, kv head) slab as this lane loads them: token 4g+i,
@@ -91,12 +97,13 @@ struct MfmaSlab {
   u32x4 v[4];
 };
 
+template <int POLICY>
 __device__ __forceinline__ void load_mfma_slab(MfmaSlab& s, __amdgpu_buffer_rsrc_t kr,
                                                __amdgpu_buffer_rsrc_t vr, int r, int g) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) s.k[i] = load16(kr, 2 * ((4 * g + i) * kD + 8 * r));
+  for (int i = 0; i < 4; ++i) s.k[i] = load16<POLICY>(kr, 2 * ((4 * g + i) * kD + 8 * r));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) s.v[i] = load16(vr, 2 * ((4 * g + i) * kD + 8 * r));
+  for (int i = 0; i < 4; ++i) s.v[i] = load16<POLICY>(vr, 2 * ((4 * g + i) * kD + 8 * r));
 }
 
 // Per-wave LDS tile that turns K around: 16 token rows of 256 bytes, padded.
@@ -199,6 +206,9 @@ __device__ __forceinline__ void consume_mfma_slab(MfmaSlab& sl, const u32x4 (&qb
 
 }  // namespace
 
+// HINT: the caller passed shared_prefix_blocks, so batches of shared blocks
+// take the caching load path; without it only the streaming path is compiled.
+template <bool HINT>
 __global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t sh_k[kHeadsPerWG][kKTileBytes];
   const int hgroups = (a.num_kv_heads + kHeadsPerWG - 1) / kHeadsPerWG;
@@ -275,31 +285,48 @@ __global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(DecodeArgs a) {
   // (straight-line code, so each consume waits only for its own slab); past
   // the last block the resource is empty and the load moves no data.  An id
   // outside the pool reads as zeros and poisons the result.
-  for (int base = jb; base < je; base += kWave) {
-    const int myb = base + lane < je ? table[base + lane] : 0;
-    const int cnt = min(kWave, je - base);
-    const auto load_step = [&](MfmaSlab& sl, int t) {
-      const int bid = __builtin_amdgcn_readlane(myb, min(t, cnt - 1));
-      const bool in_pool = bid >= 0 && (int64_t)bid < a.num_blocks;
-      bad_block |= t < cnt && !in_pool;
-      const bool live = t < cnt && in_pool;
-      const int64_t off = live ? ((int64_t)bid * a.num_kv_heads + kvh) * head_slab : 0;
-      const int bytes = live ? kSlabBytes : 0;
-      load_mfma_slab(sl, slab_rsrc(kpool + off, bytes), slab_rsrc(vpool + off, bytes), r, g);
+  // Batches never mix blocks the caller marks as shared with private ones, so
+  // each batch runs with one cache policy.
+  const int nshared = HINT ? a.shared_prefix_blocks[seq] : 0;
+  const int shared_end = max(jb, min(je, nshared));
+  for (int base = jb; base < je;) {
+    const bool shared_batch = base < shared_end;
+    const int cnt = min(kWave, (shared_batch ? shared_end : je) - base);
+    const int myb = lane < cnt ? table[base + lane] : 0;
+    const auto run_batch = [&](auto policy) {
+      constexpr int P = decltype(policy)::value;
+      const auto load_step = [&](MfmaSlab& sl, int t) {
+        const int bid = __builtin_amdgcn_readlane(myb, min(t, cnt - 1));
+        const bool in_pool = bid >= 0 && (int64_t)bid < a.num_blocks;
+        bad_block |= t < cnt && !in_pool;
+        const bool live = t < cnt && in_pool;
+        const int64_t off = live ? ((int64_t)bid * a.num_kv_heads + kvh) * head_slab : 0;
+        const int bytes = live ? kSlabBytes : 0;
+        load_mfma_slab<P>(sl, slab_rsrc(kpool + off, bytes), slab_rsrc(vpool + off, bytes), r, g);
+      };
+      const auto consume = [&](MfmaSlab& sl, int t) {
+        const int nvalid = min(kBlock, tok_end - (base + t) * kBlock);
+        consume_mfma_slab(sl, qb, a.scale_log2, r, g, nvalid, ktile, st);
+      };
+      MfmaSlab sa, sb;
+      load_step(sa, 0);
+      for (int t = 0; t < cnt; t += 2) {
+        load_step(sb, t + 1);
+        consume(sa, t);
+        if (t + 1 >= cnt) break;
+        load_step(sa, t + 2);
+        consume(sb, t + 1);
+      }
     };
-    const auto consume = [&](MfmaSlab& sl, int t) {
-      const int nvalid = min(kBlock, tok_end - (base + t) * kBlock);
-      consume_mfma_slab(sl, qb, a.scale_log2, r, g, nvalid, ktile, st);
-    };
-    MfmaSlab sa, sb;
-    load_step(sa, 0);
-    for (int t = 0; t < cnt; t += 2) {
-      load_step(sb, t + 1);
-      consume(sa, t);
-      if (t + 1 >= cnt) break;
-      load_step(sa, t + 2);
-      consume(sb, t + 1);
+    if constexpr (HINT) {
+      if (shared_batch)
+        run_batch(std::integral_constant<int, kSharedPolicy>());
+      else
+        run_batch(std::integral_constant<int, kStreamPolicy>());
+    } else {
+      run_batch(std::integral_constant<int, kStreamPolicy>());
     }
+    base += cnt;
   }
 
   // Head r's full sum is spread over its 4 lanes.  bad_block is the same in
@@ -346,7 +373,10 @@ hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, hipStream_t stream) {
   const int hgroups = (a.num_kv_heads + kHeadsPerWG - 1) / kHeadsPerWG;
   dim3 grid((unsigned)((int64_t)a.num_items * hgroups),
             a.partition_blocks > 0 ? a.max_partitions : 1);
-  hipLaunchKernelGGL(decode_gqa_mfma_kernel, grid, dim3(64 * kHeadsPerWG), 0, stream, a);
+  if (a.shared_prefix_blocks != nullptr)
+    hipLaunchKernelGGL(decode_gqa_mfma_kernel<true>, grid, dim3(64 * kHeadsPerWG), 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_gqa_mfma_kernel<false>, grid, dim3(64 * kHeadsPerWG), 0, stream, a);
   return hipGetLastError();
 }
 

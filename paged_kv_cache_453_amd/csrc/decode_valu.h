@@ -1,0 +1,498 @@
+// Paged-attention decode on the vector ALUs: kernel templates.
+//
+// Included by decode_valu_bf16.hip and decode_valu_f32.hip, which instantiate
+// the kernels for one element type each (they compile in parallel), and by
+// decode.hip for the element traits of the split-K merge.
+//
+// What is computed: for every query row, softmax(scale * q K^T) V over the
+// tokens of its sequence, K and V being read through the sequence's block table
+// from the pool [num_blocks, num_kv_heads, block_size, head_dim] ("vLLM 基本原理",
+// section PagedAttention; intelliparadigm.com article, section 3.1).  Decode
+// re-reads the whole cache for one new token and is bound by memory bandwidth
+// (xdnf.cn article, section 六.5), so the kernel is built around streaming the
+// K/V blocks once at full width and hiding all arithmetic under those loads.
+//
+// Work decomposition.  One workgroup (4 waves) per (item, kv head, partition),
+// kv heads varying fastest in launch order,
+// where an item is a sequence (decode) or one prefill query token (the generic
+// per-token prefill path).  A partition is a run of consecutive blocks; the
+// waves of a workgroup take its blocks round-robin.  All query heads that share
+// the kv head (a GQA group) are handled by the same workgroup, so each K/V
+// block is read from HBM exactly once per step.
+//
+// Lane layout inside a wave for one 16-token block slab (16 x head_dim values,
+// contiguous in memory): every lane issues 16-byte loads; LPR = head_dim*elem/16
+// lanes cover one token row, so a wave-wide load covers 64/LPR rows and a slab
+// takes 16*LPR/64 loads per lane.  A lane's row group keeps its own online
+// softmax state (running max m, running sum l, output slice acc) for the tokens
+// it sees; the only per-token cross-lane step is the LPR-lane sum of the q.k
+// partial dot products, done with DPP inside a 16-lane row.  Row groups, waves
+// and partitions are merged once at the end with the log-sum-exp rule.
+//
+// Streaming.  Each wave keeps two slabs in flight (the next block's K/V loads
+// are issued before the current block is consumed), the loads carry the
+// nontemporal hint, and full blocks take a path without row masks; only a
+// sequence's last, partly filled block pays for them.
+//
+// Scores are kept in base 2: q is pre-multiplied by scale*log2(e), so softmax
+// weights are exp2(s - m), taken with the raw v_exp_f32 inside the block loop
+// (weights below 2^-126 flush to zero, which a softmax ignores).
+#pragma once
+
+#include <math.h>
+
+#include <type_traits>
+
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+constexpr int kWavesPerGroup = 4;
+
+template <typename T>
+struct ElemTraits;
+template <>
+struct ElemTraits<float> {
+  static constexpr int kPerLoad = 4;
+  __device__ static float to_f32(float x) { return x; }
+  __device__ static float from_f32(float x) { return x; }
+};
+template <>
+struct ElemTraits<bf16_t> {
+  static constexpr int kPerLoad = 8;
+  __device__ static float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
+  __device__ static bf16_t from_f32(float x) { return f32_to_bf16(x); }
+};
+
+// Widen the E elements held in one 16-byte register quad to fp32.
+template <typename T>
+__device__ __forceinline__ void widen(const u32x4& r, float* out);
+template <>
+__device__ __forceinline__ void widen<float>(const u32x4& r, float* out) {
+#pragma unroll
+  for (int x = 0; x < 4; ++x) out[x] = __uint_as_float(r[x]);
+}
+template <>
+__device__ __forceinline__ void widen<bf16_t>(const u32x4& r, float* out) {
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    out[2 * x] = bf16_lo(r[x]);
+    out[2 * x + 1] = bf16_hi(r[x]);
+  }
+}
+
+// Partial q.k over this lane's E elements.  bf16 uses the packed bf16 dot
+// instruction on the raw bits (q kept unscaled in bf16, products exact in fp32),
+// fp32 uses fused multiply-adds on pre-scaled q.
+template <typename T>
+struct QFrag;
+template <>
+struct QFrag<float> {
+  float q[4];
+  __device__ void load(const float* p, float scale_log2) {
+    const u32x4 r = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) q[x] = __uint_as_float(r[x]) * scale_log2;
+  }
+  __device__ void zero() {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) q[x] = 0.f;
+  }
+  __device__ float dot(const u32x4& k) const {
+    float s = 0.f;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) s = fmaf(q[x], __uint_as_float(k[x]), s);
+    return s;
+  }
+  __device__ static float post(float s, float) { return s; }
+};
+template <>
+struct QFrag<bf16_t> {
+  u32x4 q;
+  __device__ void load(const bf16_t* p, float) { q = *reinterpret_cast<const u32x4*>(p); }
+  __device__ void zero() { q = u32x4{0u, 0u, 0u, 0u}; }
+  __device__ float dot(const u32x4& k) const {
+    float s = 0.f;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const uint32_t qw = q[x];
+      const uint32_t kw = k[x];
+      s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qw), as_bf16x2(kw), s, false);
+    }
+    return s;
+  }
+  __device__ static float post(float s, float scale_log2) { return s * scale_log2; }
+};
+
+// One (block, kv head) slab of K and of V as this lane holds it: NLD
+// 16-byte pieces each, rows RPL apart.
+template <int NLD>
+struct Slab {
+  u32x4 k[NLD];
+  u32x4 v[NLD];
+};
+
+// Slab loads go through a buffer resource per (block, kv head) slab: the base
+// is the slab's address (scalar registers), lanes add 32-bit byte offsets, and
+// the range check of the buffer unit turns a resource of size 0 into zero data
+// with no memory access -- used for a lookahead past the last block and for
+// block ids outside the pool.  A block that only this sequence reads is
+// streamed with the nontemporal hint (measured ~10% faster than default
+// caching on private KV); a block the caller marks as shared with other
+// sequences of the call is read with the default policy, so sharers running
+// at the same time hit in L2 (the shared-prefix decode runs ~1.5x faster).
+constexpr int kBufferWord3 = 0x00020000;   // raw 32-bit buffer, no format conversion
+constexpr int kStreamPolicy = 2;           // cache-policy bits: nontemporal
+constexpr int kSharedPolicy = 0;           // cache-policy bits: default
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferWord3);
+}
+
+template <int POLICY>
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t rsrc, int byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(rsrc, byte_off, 0, POLICY);
+}
+
+template <typename T, int D, int POLICY>
+__device__ __forceinline__ void load_slab(Slab<kBlock * D / (kWave * ElemTraits<T>::kPerLoad)>& s,
+                                          __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                          int lane_byte_off) {
+  constexpr int RPL = kWave / (D / ElemTraits<T>::kPerLoad);
+  constexpr int NLD = kBlock / RPL;
+  constexpr int STEP = RPL * D * (int)sizeof(T);
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) s.k[i] = load16<POLICY>(kr, lane_byte_off + i * STEP);
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) s.v[i] = load16<POLICY>(vr, lane_byte_off + i * STEP);
+}
+
+// Fold one slab into this lane's online-softmax state (running max m, running
+// sum l, output slice acc per query head of the group).  MASKED: rows at or
+// past nvalid are skipped -- their scores never enter the max, their weights
+// are 0 and their V values are replaced by 0 before use, since they may hold
+// anything (NaN included) and 0 * NaN is NaN.
+template <typename T, int D, int GP, bool MASKED>
+__device__ __forceinline__ void consume_slab(
+    const Slab<kBlock * D / (kWave * ElemTraits<T>::kPerLoad)>& sl, const QFrag<T> (&q)[GP],
+    float scale_log2, int r, int nvalid, float (&m)[GP], float (&l)[GP],
+    float (&acc)[GP][ElemTraits<T>::kPerLoad]) {
+  constexpr int E = ElemTraits<T>::kPerLoad;
+  constexpr int LPR = D / E;
+  constexpr int RPL = kWave / LPR;
+  constexpr int NLD = kBlock / RPL;
+
+  // scores of this lane's rows, summed over the LPR lanes of each row
+  float s[GP][NLD];
+#pragma unroll
+  for (int g = 0; g < GP; ++g)
+#pragma unroll
+    for (int i = 0; i < NLD; ++i)
+      s[g][i] = QFrag<T>::post(group_sum<LPR>(q[g].dot(sl.k[i])), scale_log2);
+
+  bool valid[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) valid[i] = !MASKED || i * RPL + r < nvalid;
+
+  float p[GP][NLD];
+#pragma unroll
+  for (int g = 0; g < GP; ++g) {
+    float bm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i)
+      if (valid[i]) bm = fmaxf(bm, s[g][i]);
+    const float mn = fmaxf(m[g], bm);
+    // with masking, mn stays -inf while this row group has seen no token
+    const float alpha = (MASKED && mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m[g] - mn);
+    float lsum = l[g] * alpha;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[g][e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      p[g][i] = valid[i] ? __builtin_amdgcn_exp2f(s[g][i] - mn) : 0.f;
+      lsum += p[g][i];
+    }
+    l[g] = lsum;
+    m[g] = mn;
+  }
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    u32x4 vr = sl.v[i];
+    if (MASKED) vr = valid[i] ? vr : u32x4{0u, 0u, 0u, 0u};
+    float v[E];
+    widen<T>(vr, v);
+#pragma unroll
+    for (int g = 0; g < GP; ++g)
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[g][e] = fmaf(p[g][i], v[e], acc[g][e]);
+  }
+}
+
+// Locate the sequence an item belongs to and how many of its tokens it sees.
+// Returns false if the item has no query row (past the last prefill token).
+struct ItemInfo {
+  int seq;
+  int ctx;      // tokens visible to this item
+  bool bad;     // contract violated: the item's outputs become NaN
+};
+
+__device__ __forceinline__ bool locate_item(const DecodeArgs& a, int item, ItemInfo& it) {
+  if (a.query_start_loc == nullptr) {
+    it.seq = item;
+    it.ctx = a.context_lens[item];
+    it.bad = it.ctx < 0 || it.ctx > a.max_blocks_per_seq * kBlock ||
+             (a.partition_blocks > 0 && it.ctx > a.max_context_len);
+    return true;
+  }
+  const int32_t* qsl = a.query_start_loc;
+  if (item >= qsl[a.num_seqs] || item < qsl[0]) return false;
+  int lo = 0, hi = a.num_seqs;  // invariant: qsl[lo] <= item < qsl[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (qsl[mid] <= item) lo = mid; else hi = mid;
+  }
+  const int chunk = qsl[lo + 1] - qsl[lo];
+  const int len = a.context_lens[lo];
+  it.seq = lo;
+  it.ctx = len - chunk + (item - qsl[lo]) + 1;
+  // a non-monotone query_start_loc can leave item outside its chunk
+  it.bad = item >= qsl[lo + 1] || chunk > len || chunk > a.max_query_len ||
+           len > a.max_blocks_per_seq * kBlock || it.ctx < 1 || it.ctx > len;
+  return true;
+}
+
+// HINT: the caller passed shared_prefix_blocks, so batches of shared blocks
+// take the caching load path; without it only the streaming path is compiled.
+template <typename T, int D, int GP, bool HINT>
+__global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
+  constexpr int E = ElemTraits<T>::kPerLoad;   // elements per 16-byte load
+  constexpr int LPR = D / E;                   // lanes per token row
+  constexpr int RPL = kWave / LPR;             // token rows per wave-wide load
+  constexpr int NLD = kBlock / RPL;            // loads per block slab per lane
+  constexpr int NW = kWavesPerGroup;
+  static_assert(LPR >= 2 && LPR <= 32 && NLD >= 1, "layout");
+
+  __shared__ float sh_acc[NW][GP][D];
+  __shared__ float sh_m[NW][GP];
+  __shared__ float sh_l[NW][GP];
+  __shared__ int sh_bad[NW];
+
+  // blockIdx.x = item * num_kv_heads + kv head: workgroups launched together
+  // read the adjacent head slabs of the same physical blocks, which keeps the
+  // HBM accesses of concurrently running waves close together.
+  const int item = blockIdx.x / a.num_kv_heads;
+  const int kvh = blockIdx.x - item * a.num_kv_heads;
+  const int part = blockIdx.y;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = wave_uniform(threadIdx.x >> 6);
+  const int r = lane / LPR;
+  const int c = lane % LPR;
+  const int G = a.group;
+
+  ItemInfo it;
+  if (!locate_item(a, item, it)) return;
+  const int nblk = it.bad ? 0 : (it.ctx + kBlock - 1) / kBlock;
+  const bool split = a.partition_blocks > 0;
+  const int nparts = split ? (nblk + a.partition_blocks - 1) / a.partition_blocks : 1;
+  if (part >= (nparts > 0 ? nparts : 1)) return;
+  const int jb = split ? part * a.partition_blocks : 0;
+  const int je = split ? min(nblk, jb + a.partition_blocks) : nblk;
+  const int tok_end = min(it.ctx, je * kBlock);
+  const int hq = a.num_heads;
+  T* out = static_cast<T*>(a.out);
+
+  // Degenerate items (only partition 0 gets here): no context gives zeros, a
+  // violated contract gives NaN.
+  if (it.bad || it.ctx == 0) {
+    const float fill = it.bad ? __builtin_nanf("") : 0.f;
+    if (split && it.bad && it.ctx > 0 && it.ctx <= a.max_context_len) {
+      // the merge step will read this item's partitions: poison all of them
+      const int ptok = a.partition_blocks * kBlock;
+      const int np_bad = (it.ctx + ptok - 1) / ptok;
+      if (np_bad > 1) {
+        for (int i = threadIdx.x; i < np_bad * G * D; i += blockDim.x) {
+          const int p = i / (G * D);
+          const int g = (i / D) % G;
+          const int64_t row = ((int64_t)it.seq * hq + kvh * G + g) * a.max_partitions + p;
+          a.part_o[row * D + i % D] = fill;
+          if (i % D == 0) a.part_lse[row] = fill;
+        }
+        return;
+      }
+    }
+    for (int i = threadIdx.x; i < G * D; i += blockDim.x)
+      out[((int64_t)item * hq + kvh * G) * D + i] = ElemTraits<T>::from_f32(fill);
+    return;
+  }
+
+  // Query fragments of the group's heads: this lane's E elements of each.
+  QFrag<T> q[GP];
+#pragma unroll
+  for (int g = 0; g < GP; ++g) {
+    if (g < G)
+      q[g].load(static_cast<const T*>(a.query) + ((int64_t)item * hq + kvh * G + g) * D + c * E,
+                a.scale_log2);
+    else
+      q[g].zero();
+  }
+
+  float m[GP], l[GP], acc[GP][E];
+#pragma unroll
+  for (int g = 0; g < GP; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[g][e] = 0.f;
+  }
+
+  const T* kpool = static_cast<const T*>(a.k_cache);
+  const T* vpool = static_cast<const T*>(a.v_cache);
+  const int32_t* table = a.block_tables + (int64_t)it.seq * a.max_blocks_per_seq;
+  const int64_t head_slab = (int64_t)kBlock * D;
+  const int lane_off = r * D + c * E;     // elements from the slab start
+  bool bad_block = false;
+
+  // Blocks of this wave: jb + w, jb + w + NW, ...  Their ids are fetched up to
+  // 64 at a time into one register (lane t holds the t-th) and broadcast per
+  // step.  Two slabs are in flight: the next block's loads are issued before
+  // the current block is consumed, unconditionally (straight-line code, so
+  // each consume waits only for its own slab); past the last block of a batch
+  // the resource is empty and the load moves no data.  A block id outside the
+  // pool reads as zeros and poisons the result.  Batches never mix shared and
+  // private blocks, so each batch runs with one cache policy.
+  const int nb_w = (je - jb - w + NW - 1) / NW;
+  const int slab_bytes = kBlock * D * (int)sizeof(T);
+  const int lane_byte_off = lane_off * (int)sizeof(T);
+  const int nshared = HINT ? a.shared_prefix_blocks[it.seq] : 0;
+  const int shared_ahead = nshared - jb - w;   // this wave's block idx is shared iff idx < idx_shared
+  const int idx_shared = shared_ahead > 0 ? min(nb_w, (shared_ahead + NW - 1) / NW) : 0;
+  for (int base = 0; base < nb_w;) {
+    const bool shared_batch = base < idx_shared;
+    const int cnt = min(kWave, (shared_batch ? idx_shared : nb_w) - base);
+    const int myb = lane < cnt ? table[jb + w + NW * (base + lane)] : 0;
+    const auto run_batch = [&](auto policy) {
+      constexpr int P = decltype(policy)::value;
+      const auto load_step = [&](Slab<NLD>& sl, int t) {
+        const int bid = __builtin_amdgcn_readlane(myb, min(t, cnt - 1));
+        const bool in_pool = bid >= 0 && (int64_t)bid < a.num_blocks;
+        bad_block |= t < cnt && !in_pool;
+        const bool live = t < cnt && in_pool;
+        const int64_t off = live ? ((int64_t)bid * a.num_kv_heads + kvh) * head_slab : 0;
+        const int bytes = live ? slab_bytes : 0;
+        load_slab<T, D, P>(sl, slab_rsrc(kpool + off, bytes), slab_rsrc(vpool + off, bytes),
+                           lane_byte_off);
+      };
+      const auto consume = [&](const Slab<NLD>& sl, int t) {
+        const int j = jb + w + NW * (base + t);
+        const int nvalid = min(kBlock, tok_end - j * kBlock);
+        if (nvalid == kBlock)
+          consume_slab<T, D, GP, false>(sl, q, a.scale_log2, r, nvalid, m, l, acc);
+        else
+          consume_slab<T, D, GP, true>(sl, q, a.scale_log2, r, nvalid, m, l, acc);
+      };
+      Slab<NLD> sa, sb;
+      load_step(sa, 0);
+      for (int t = 0; t < cnt; t += 2) {
+        load_step(sb, t + 1);
+        consume(sa, t);
+        if (t + 1 >= cnt) break;
+        load_step(sa, t + 2);
+        consume(sb, t + 1);
+      }
+    };
+    if constexpr (HINT) {
+      if (shared_batch)
+        run_batch(std::integral_constant<int, kSharedPolicy>());
+      else
+        run_batch(std::integral_constant<int, kStreamPolicy>());
+    } else {
+      run_batch(std::integral_constant<int, kStreamPolicy>());
+    }
+    base += cnt;
+  }
+
+  // Merge the row groups of this wave (lanes that differ in index bits >= LPR).
+#pragma unroll
+  for (int g = 0; g < GP; ++g) {
+    const float mw = xor_max_above<LPR>(m[g]);
+    const float f = (m[g] == -INFINITY) ? 0.f : exp2f(m[g] - mw);
+    l[g] = xor_sum_above<LPR>(l[g] * f);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[g][e] = xor_sum_above<LPR>(acc[g][e] * f);
+    m[g] = mw;
+  }
+  __syncthreads();
+  if (lane == 0) sh_bad[w] = __builtin_amdgcn_readfirstlane((int)bad_block);
+  if (r == 0) {
+#pragma unroll
+    for (int g = 0; g < GP; ++g)
+#pragma unroll
+      for (int e = 0; e < E; ++e) sh_acc[w][g][c * E + e] = acc[g][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < GP; ++g) {
+      sh_m[w][g] = m[g];
+      sh_l[w][g] = l[g];
+    }
+  }
+  __syncthreads();
+
+  // Merge the waves and write this workgroup's result.
+  bool poisoned = false;
+#pragma unroll
+  for (int x = 0; x < NW; ++x) poisoned |= sh_bad[x] != 0;
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
+    const int g = i / D;
+    const int d = i - g * D;
+    float mm = -INFINITY;
+#pragma unroll
+    for (int x = 0; x < NW; ++x) mm = fmaxf(mm, sh_m[x][g]);
+    float lsum = 0.f, o = 0.f;
+#pragma unroll
+    for (int x = 0; x < NW; ++x) {
+      const float f = (sh_m[x][g] == -INFINITY) ? 0.f : exp2f(sh_m[x][g] - mm);
+      lsum = fmaf(sh_l[x][g], f, lsum);
+      o = fmaf(sh_acc[x][g][d], f, o);
+    }
+    o = poisoned ? __builtin_nanf("") : o / lsum;
+    const int h = kvh * G + g;
+    if (nparts <= 1) {
+      out[((int64_t)item * hq + h) * D + d] = ElemTraits<T>::from_f32(o);
+    } else {
+      const int64_t row = ((int64_t)it.seq * hq + h) * a.max_partitions + part;
+      a.part_o[row * D + d] = o;
+      if (d == 0) a.part_lse[row] = poisoned ? __builtin_nanf("") : (mm + log2f(lsum)) * kLn2;
+    }
+  }
+}
+
+template <typename T, int D, bool HINT>
+inline void launch_decode_group(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
+  const dim3 block(256);
+  const int G = a.group;
+  if (G <= 1)
+    hipLaunchKernelGGL((decode_valu_kernel<T, D, 1, HINT>), grid, block, 0, stream, a);
+  else if (G <= 2)
+    hipLaunchKernelGGL((decode_valu_kernel<T, D, 2, HINT>), grid, block, 0, stream, a);
+  else if (G <= 4)
+    hipLaunchKernelGGL((decode_valu_kernel<T, D, 4, HINT>), grid, block, 0, stream, a);
+  else if (G <= 8)
+    hipLaunchKernelGGL((decode_valu_kernel<T, D, 8, HINT>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_valu_kernel<T, D, 16, HINT>), grid, block, 0, stream, a);
+}
+
+template <typename T, int D>
+inline hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+  dim3 grid((unsigned)((int64_t)a.num_items * a.num_kv_heads),
+            a.partition_blocks > 0 ? a.max_partitions : 1);
+  if (a.shared_prefix_blocks != nullptr)
+    launch_decode_group<T, D, true>(a, grid, stream);
+  else
+    launch_decode_group<T, D, false>(a, grid, stream);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -84,7 +84,8 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int 
 }
 
 int pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
-              const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+              const int32_t* block_tables, const int32_t* context_lens,
+              const int32_t* shared_prefix_blocks, int num_seqs,
               int num_heads, int num_kv_heads, int head_dim, int block_size,
               int max_blocks_per_seq, int64_t num_blocks, int max_context_len, float scale,
               int partition_size, void* workspace, size_t workspace_bytes, pa_dtype dtype,
@@ -116,6 +117,7 @@ int pa_decode(void* out, const void* query, const void* key_cache, const void* v
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.query_start_loc = nullptr;
+  a.shared_prefix_blocks = shared_prefix_blocks;
   const size_t rows = (size_t)num_seqs * num_heads * nparts;
   a.part_o = partition_size > 0 ? static_cast<float*>(workspace) : nullptr;
   a.part_lse = partition_size > 0 ? static_cast<float*>(workspace) + rows * head_dim : nullptr;
@@ -190,6 +192,7 @@ int pa_prefill_chunk(void* out, const void* query, const void* key_cache, const 
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.query_start_loc = query_start_loc;
+  a.shared_prefix_blocks = nullptr;
   a.num_seqs = num_seqs;
   a.num_items = num_query_tokens;
   a.num_heads = num_heads;

@@ -29,6 +29,7 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   const int32_t* query_start_loc;  // non-null: one work item per prefill query token
+  const int32_t* shared_prefix_blocks;  // optional per-sequence cache hint (decode only)
   float* part_o;
   float* part_lse;
   int num_seqs;
@@ -60,6 +61,8 @@ struct ReduceArgs {
 hipError_t launch_reshape_and_cache(const ScatterArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t stream);
 hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_valu_bf16(const DecodeArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_decode_valu_f32(const DecodeArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_splitk_reduce(const ReduceArgs& a, int head_dim, bool bf16, hipStream_t stream);
 hipError_t launch_prefill_mfma(const DecodeArgs& a, int head_dim, hipStream_t stream);
 

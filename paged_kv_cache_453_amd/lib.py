@@ -44,8 +44,8 @@ def load() -> ctypes.CDLL:
     lib.pa_reshape_and_cache.restype = i32
     lib.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.pa_decode_workspace_bytes.restype = sz
-    lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, i32, f32,
-                              i32, vp, sz, i32, vp]
+    lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, i32,
+                              f32, i32, vp, sz, i32, vp]
     lib.pa_decode.restype = i32
     lib.pa_decode_splitk_reduce.argtypes = [vp, vp, sz, vp, i32, i32, i32, i32, i32, i32, vp]
     lib.pa_decode_splitk_reduce.restype = i32
@@ -133,8 +133,10 @@ def pa_decode_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_
 
 
 def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, scale: float,
-              max_context_len: int, partition_size: int = 0, workspace=None, stream=None) -> None:
-    """out/query [S, Hq, D]; caches [NB, Hkv, 16, D]; block_tables int32 [S, MB]; context_lens int32 [S]."""
+              max_context_len: int, partition_size: int = 0, workspace=None, stream=None,
+              shared_prefix_blocks=None) -> None:
+    """out/query [S, Hq, D]; caches [NB, Hkv, 16, D]; block_tables int32 [S, MB]; context_lens
+    int32 [S]; shared_prefix_blocks optional int32 [S] (cache hint, see include/pa.h)."""
     torch = _torch()
     lib = load()
     _on_gpu(out, query, key_cache, value_cache, block_tables, context_lens)
@@ -146,13 +148,18 @@ def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, sc
     _need(block_tables.dim() == 2 and block_tables.shape[0] == s and context_lens.numel() == s,
           "block_tables must be [S, MB] and context_lens [S]")
     _need(out.dtype == query.dtype == key_cache.dtype == value_cache.dtype, "dtype mismatch")
+    if shared_prefix_blocks is not None:
+        _on_gpu(shared_prefix_blocks)
+        _need(shared_prefix_blocks.dtype == torch.int32 and shared_prefix_blocks.numel() == s,
+              "shared_prefix_blocks must be int32 [S]")
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         _on_gpu(workspace)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     _check("pa_decode", lib.pa_decode(
         _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
-        _ptr(context_lens), s, hq, hkv, d, bs, block_tables.shape[1], nb, int(max_context_len),
+        _ptr(context_lens), _ptr(shared_prefix_blocks), s, hq, hkv, d, bs, block_tables.shape[1],
+        nb, int(max_context_len),
         float(scale), int(partition_size), ws_ptr, ws_bytes, _dtype_code(query), _stream(stream)))
 
 

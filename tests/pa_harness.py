@@ -55,7 +55,8 @@ def gpu_scatter(dw: DeviceWorkload):
     lib().pa_reshape_and_cache(dw.new_k, dw.new_v, dw.k_cache, dw.v_cache, dw.slot_mapping)
 
 
-def gpu_decode(dw: DeviceWorkload, partition_size: Optional[int] = None, group=None):
+def gpu_decode(dw: DeviceWorkload, partition_size: Optional[int] = None, group=None,
+               use_shared_hint: bool = True):
     import torch
     L = lib()
     g = dw.decode if group is None else group
@@ -66,8 +67,9 @@ def gpu_decode(dw: DeviceWorkload, partition_size: Optional[int] = None, group=N
         nbytes = L.pa_decode_workspace_bytes(g.query.shape[0], w.num_heads, w.head_dim,
                                              g.max_context_len, ps)
         ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=g.query.device)
+    hint = getattr(g, "shared_prefix_blocks", None) if use_shared_hint else None
     L.pa_decode(g.out, g.query, dw.k_cache, dw.v_cache, g.block_tables, g.context_lens, w.scale,
-                g.max_context_len, ps, ws)
+                g.max_context_len, ps, ws, shared_prefix_blocks=hint)
     if ps > 0:
         L.pa_decode_splitk_reduce(g.out, ws, g.context_lens, g.max_context_len, ps)
     return ws

@@ -52,11 +52,12 @@ def test_status_strings(lib):
 
 
 def decode(lib, **kw):
-    args = dict(out=P, query=P, k=P, v=P, bt=P, cl=P, S=4, hq=8, hkv=8, d=128, bs=16, mb=4,
-                nb=64, maxc=64, scale=0.1, ps=0, ws=None, wsb=0, dtype=BF16, stream=None)
+    args = dict(out=P, query=P, k=P, v=P, bt=P, cl=P, shared=None, S=4, hq=8, hkv=8, d=128, bs=16,
+                mb=4, nb=64, maxc=64, scale=0.1, ps=0, ws=None, wsb=0, dtype=BF16, stream=None)
     args.update(kw)
     a = args
-    return lib.pa_decode(a["out"], a["query"], a["k"], a["v"], a["bt"], a["cl"], a["S"], a["hq"],
+    return lib.pa_decode(a["out"], a["query"], a["k"], a["v"], a["bt"], a["cl"], a["shared"],
+                         a["S"], a["hq"],
                          a["hkv"], a["d"], a["bs"], a["mb"], a["nb"], a["maxc"], a["scale"],
                          a["ps"], a["ws"], a["wsb"], a["dtype"], a["stream"])
 

@@ -186,3 +186,35 @@ def test_abi_rejects_bad_arguments_on_device(gpu):
         ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
         lib().pa_decode(g.out, g.query, dw.k_cache, dw.v_cache, g.block_tables, g.context_lens,
                         w.scale, g.max_context_len, 24, ws)
+
+
+@pytest.mark.parametrize("hq,hkv", [(40, 40), (32, 8)])
+@pytest.mark.parametrize("ps", [0, 256])
+def test_shared_prefix_hint_changes_nothing(gpu, hq, hkv, ps):
+    """shared_prefix_blocks only selects the cache policy of the loads: outputs
+    are bitwise identical with no hint, the true hint, and nonsense hints."""
+    import torch
+    w = config4(num_prompts=6, samples=3, num_prefill=1, num_blocks=4096, heads=hq)
+    w.prefill = None
+    if hkv != hq:
+        # same tables and lengths, grouped-query heads
+        w = make_decode("hint-gqa", 77, "bf16", w.decode.context_lens, hq, hkv, 128, 4096,
+                        with_scatter=False)
+        w.decode.shared_prefix_blocks = np.full(w.decode.num_seqs, 40, dtype=np.int32)
+    dw = to_device(w)
+    g = dw.decode
+    S = g.context_lens.numel()
+    hints = [None, g.shared_prefix_blocks,
+             torch.full((S,), 1 << 20, dtype=torch.int32, device="cuda"),
+             torch.full((S,), -7, dtype=torch.int32, device="cuda"),
+             torch.randint(0, 200, (S,), dtype=torch.int32, device="cuda")]
+    outs = []
+    for hint in hints:
+        g.shared_prefix_blocks = hint
+        g.out.fill_(float("nan"))
+        gpu_decode(dw, ps)
+        torch.cuda.synchronize()
+        outs.append(g.out.clone())
+    for o in outs[1:]:
+        assert torch.equal(outs[0].view(torch.int16), o.view(torch.int16))
+    assert_close(as_f64(outs[0]), oracle_decode(w), "bf16", f"hint test {hq}/{hkv} ps={ps}")

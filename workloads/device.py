@@ -54,6 +54,7 @@ class DeviceGroup:
     query_start_loc: Optional[object] = None
     max_context_len: int = 0
     max_query_len: int = 0
+    shared_prefix_blocks: Optional[object] = None
 
 
 @dataclass
@@ -95,7 +96,11 @@ def _group(g, dtype, hq, d, device):
     qsl = None
     if g.query_start_loc is not None:
         qsl = torch.from_numpy(g.query_start_loc.astype(np.int32)).to(device)
+    shared = None
+    if g.shared_prefix_blocks is not None:
+        shared = torch.from_numpy(g.shared_prefix_blocks.astype(np.int32)).to(device)
     return DeviceGroup(
+        shared_prefix_blocks=shared,
         context_lens=torch.from_numpy(g.context_lens.astype(np.int32)).to(device),
         block_tables=torch.from_numpy(g.block_tables.astype(np.int32)).to(device),
         query=q, out=out, query_start_loc=qsl, max_context_len=g.max_context_len,
