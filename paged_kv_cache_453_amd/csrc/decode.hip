@@ -11,32 +11,66 @@
 namespace pa {
 
 // Split-K merge: out = sum_p exp(lse_p - M) o_p / sum_p exp(lse_p - M).
+//
+// One wave per (sequence, head), four per workgroup.  A first pass takes the
+// max of the log-sum-exps with one partition per lane; then each lane owns
+// D/64 adjacent columns and walks the partitions, the weight of partition p
+// broadcast from the lane that computed it.  The partials of successive
+// partitions are independent loads, unrolled so that many are in flight --
+// the merge is a short stream over the workspace, not a chain of waits.
+constexpr int kReduceWaves = 4;
+
 template <typename T, int D>
-__global__ __launch_bounds__(D) void splitk_reduce_kernel(ReduceArgs a) {
-  const int s = blockIdx.x;
-  const int h = blockIdx.y;
-  const int d = threadIdx.x;
+__global__ __launch_bounds__(64 * kReduceWaves) void splitk_reduce_kernel(ReduceArgs a) {
+  constexpr int E = D / kWave;          // columns per lane
+  const int row_sh = blockIdx.x * kReduceWaves + wave_uniform(threadIdx.x >> 6);
+  if (row_sh >= a.num_seqs * a.num_heads) return;
+  const int s = row_sh / a.num_heads;
+  const int h = row_sh - s * a.num_heads;
+  const int lane = threadIdx.x & (kWave - 1);
   const int len = a.context_lens[s];
   if (len <= 0 || len > a.max_context_len) return;   // the decode kernel wrote these
   const int n = (len + a.partition_tokens - 1) / a.partition_tokens;
   if (n <= 1) return;
-  const int64_t row = ((int64_t)s * a.num_heads + h) * a.max_partitions;
+  const int64_t row = (int64_t)row_sh * a.max_partitions;
   const float* lse = a.part_lse + row;
+
   float mm = -INFINITY;
   bool nan = false;
-  for (int p = 0; p < n; ++p) {
-    const float x = lse[p];
+  for (int p0 = 0; p0 < n; p0 += kWave) {
+    const float x = p0 + lane < n ? lse[p0 + lane] : -INFINITY;
     nan |= isnan(x);
     mm = fmaxf(mm, x);
   }
-  float wsum = 0.f, o = 0.f;
-  for (int p = 0; p < n; ++p) {
-    const float wgt = expf(lse[p] - mm);
-    wsum += wgt;
-    o = fmaf(wgt, a.part_o[(row + p) * D + d], o);
+  mm = xor_max_above<1>(mm);
+  nan = __ballot(nan) != 0;
+
+  float acc[E], wsum = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  const float* po = a.part_o + row * D + lane * E;
+  for (int p0 = 0; p0 < n; p0 += kWave) {
+    const float wl = p0 + lane < n ? expf(lse[p0 + lane] - mm) : 0.f;
+    wsum += wl;
+    const int cnt = min(kWave, n - p0);
+#pragma unroll 8
+    for (int t = 0; t < cnt; ++t) {
+      const float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), t));
+      const float* src = po + (int64_t)(p0 + t) * D;
+      if constexpr (E == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(src);
+        acc[0] = fmaf(wt, v.x, acc[0]);
+        acc[1] = fmaf(wt, v.y, acc[1]);
+      } else {
+        acc[0] = fmaf(wt, src[0], acc[0]);
+      }
+    }
   }
-  o = nan ? __builtin_nanf("") : o / wsum;
-  static_cast<T*>(a.out)[((int64_t)s * a.num_heads + h) * D + d] = ElemTraits<T>::from_f32(o);
+  wsum = xor_sum_above<1>(wsum);
+  T* dst = static_cast<T*>(a.out) + (int64_t)row_sh * D + lane * E;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    dst[e] = ElemTraits<T>::from_f32(nan ? __builtin_nanf("") : acc[e] / wsum);
 }
 
 // Grouped-query decode with at least this many query heads per kv head runs on
@@ -53,17 +87,19 @@ hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool bf16, hipStream
 
 hipError_t launch_splitk_reduce(const ReduceArgs& a, int head_dim, bool bf16, hipStream_t stream) {
   if (a.num_seqs == 0) return hipSuccess;
-  dim3 grid(a.num_seqs, a.num_heads);
+  const int64_t rows = (int64_t)a.num_seqs * a.num_heads;
+  const dim3 grid((unsigned)((rows + kReduceWaves - 1) / kReduceWaves));
+  const dim3 block(64 * kReduceWaves);
   if (bf16) {
     if (head_dim == 64)
-      hipLaunchKernelGGL((splitk_reduce_kernel<bf16_t, 64>), grid, dim3(64), 0, stream, a);
+      hipLaunchKernelGGL((splitk_reduce_kernel<bf16_t, 64>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((splitk_reduce_kernel<bf16_t, 128>), grid, dim3(128), 0, stream, a);
+      hipLaunchKernelGGL((splitk_reduce_kernel<bf16_t, 128>), grid, block, 0, stream, a);
   } else {
     if (head_dim == 64)
-      hipLaunchKernelGGL((splitk_reduce_kernel<float, 64>), grid, dim3(64), 0, stream, a);
+      hipLaunchKernelGGL((splitk_reduce_kernel<float, 64>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((splitk_reduce_kernel<float, 128>), grid, dim3(128), 0, stream, a);
+      hipLaunchKernelGGL((splitk_reduce_kernel<float, 128>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }

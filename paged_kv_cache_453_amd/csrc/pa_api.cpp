@@ -144,7 +144,7 @@ int pa_decode_splitk_reduce(void* out, const void* workspace, size_t workspace_b
   if (num_seqs > 0 && (!out || !context_lens)) return PA_ERR_NULL;
   if (!dtype_ok(out_dtype) || !head_dim_ok(head_dim)) return PA_ERR_UNSUPPORTED;
   if (num_heads < 1 || num_heads > kMaxGridY || max_context_len < 0 || partition_size <= 0 ||
-      partition_size % kBlockSize != 0)
+      partition_size % kBlockSize != 0 || (int64_t)num_seqs * num_heads > INT32_MAX)
     return PA_ERR_SHAPE;
   const size_t need =
       pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, partition_size);
