@@ -38,7 +38,7 @@ def test_tiny_fp32_decode(gpu, ps):
     assert_close(as_f64(dw.decode.out), oracle_decode(w), "f32", f"config0 ps={ps}")
 
 
-@pytest.mark.parametrize("ps", [0, 256, 512])
+@pytest.mark.parametrize("ps", [0, 256, 512, 2048])   # 2048: the launch bench.py times
 def test_llama7b_bf16_decode(gpu, ps):
     say(f"decode config1 bf16 ps={ps}")
     w = config1(partition_size=ps)
@@ -55,12 +55,13 @@ def test_llama7b_fp32_twin_tight(gpu, ps):
 
 
 @pytest.mark.slow
-def test_llama13b_bf16_decode_full(gpu):
-    say("decode config2 full size (scatter, split-K 512)")
-    w = config2()
+@pytest.mark.parametrize("ps", [512, 2048])   # 2048: the launch bench.py times
+def test_llama13b_bf16_decode_full(gpu, ps):
+    say(f"decode config2 full size (scatter, split-K {ps})")
+    w = config2(partition_size=ps)
     dw = run(w)
     say("decode config2: oracle")
-    assert_close(as_f64(dw.decode.out), oracle_decode(w), "bf16", "config2")
+    assert_close(as_f64(dw.decode.out), oracle_decode(w), "bf16", f"config2 ps={ps}")
 
 
 @pytest.mark.slow
