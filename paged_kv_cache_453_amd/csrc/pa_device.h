@@ -34,8 +34,10 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float x) {
   __bf16 b = (__bf16)x;
   return __builtin_bit_cast(bf16_t, b);
 }
+// Two fp32 -> bf16 (nearest even) in one v_cvt_pk_bf16_f32; lo in bits 0..15.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
 // ---- cross-lane sums inside groups of 2/4/8/16 lanes (DPP, no LDS) --------

@@ -84,14 +84,6 @@ __device__ __forceinline__ u32x4 v_operand(const typename VRow<D>::type (&vr)[8]
                pick_pair<T>(vr[4], vr[5]), pick_pair<T>(vr[6], vr[7])};
 }
 
-template <int D, int QB, int T>
-__device__ __forceinline__ void pv_tile(const typename VRow<D>::type (&vr)[8],
-                                        const u32x4 (&pk)[QB], f32x4 (&o)[QB][D / 16]) {
-  const u32x4 va = v_operand<D, T>(vr);
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) o[qb][T] = mfma_16x16x32(va, pk[qb], o[qb][T]);
-}
-
 }  // namespace
 
 template <int D, int RW>
@@ -319,16 +311,23 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
           const int key = 32 * kk + (j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4));
           vr[j] = *reinterpret_cast<const vrow_t*>(vb + key * ROW + 2 * DT * r);
         }
-        pv_tile<D, QB, 0>(vr, pk[kk], o);
-        pv_tile<D, QB, 1>(vr, pk[kk], o);
-        pv_tile<D, QB, 2>(vr, pk[kk], o);
-        pv_tile<D, QB, 3>(vr, pk[kk], o);
+        // all d-tile operands first, then the MFMAs back to back: building each
+        // operand right before its MFMA serialises on the operand registers
+        u32x4 va[DT];
+        va[0] = v_operand<D, 0>(vr);
+        va[1] = v_operand<D, 1>(vr);
+        va[2] = v_operand<D, 2>(vr);
+        va[3] = v_operand<D, 3>(vr);
         if constexpr (DT > 4) {
-          pv_tile<D, QB, 4>(vr, pk[kk], o);
-          pv_tile<D, QB, 5>(vr, pk[kk], o);
-          pv_tile<D, QB, 6>(vr, pk[kk], o);
-          pv_tile<D, QB, 7>(vr, pk[kk], o);
+          va[4] = v_operand<D, 4>(vr);
+          va[5] = v_operand<D, 5>(vr);
+          va[6] = v_operand<D, 6>(vr);
+          va[7] = v_operand<D, 7>(vr);
         }
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) o[qb][t] = mfma_16x16x32(va[t], pk[kk][qb], o[qb][t]);
       }
     }
     stage_store((kt + 1) & 1);
