@@ -18,26 +18,52 @@ What it models, and the passages it follows (page titles as printed):
   copies it first (intelliparadigm.com article, section 2.2: RefCounter for
   copy-on-write; section 3.3: with reference counts only a writer that still
   shares the block copies it -- the last owner writes in place).
+* Three sharing modes (intelliparadigm.com article, section 2.3): a whole
+  sequence (fork), its first n blocks (a prefix), or chosen logical blocks.
 * A finished sequence returns its blocks at once (xdnf.cn article, section
   六.1).
+* Swap space: a second pool in host memory (intelliparadigm.com article,
+  section 5.1, the swap-space setting); a swapped-out sequence's blocks are
+  copied there and its device blocks released, and swapping in reverses it.
 
-Readings where the pages leave the policy open (the same in the native
-manager, so tables can be compared exactly; the invariants below hold for any
+Readings where the pages leave the policy open (the native manager follows the
+same ones, so tables can be compared exactly; the invariants hold for any
 policy):
-* Free blocks form a stack: allocation takes the most recently freed block;
-  initially blocks come out in increasing id order.
-* Freeing a sequence releases its table from the last entry to the first, so
-  its first block is the next to be reused.
-* Appending n tokens is all-or-nothing: if the pool cannot supply every block
-  needed (copy-on-write included), nothing changes and OutOfBlocks is raised.
-* Only a partly filled shared last block is copied on write; full shared
-  blocks stay shared (nothing is ever written into them again).
+* R1  Free blocks form a stack: allocation takes the most recently released
+      block; initially blocks come out in increasing id order.
+* R2  Releasing a table goes from its last entry to its first, so the first
+      block is the next to be reused.
+* R3  Every operation is all-or-nothing: if a pool cannot supply every block
+      it needs, nothing changes and OutOfBlocks is raised.
+* R4  Only a partly filled shared last block is copied on write; full shared
+      blocks stay shared (nothing is written into them again).
+* R5  Prefix and selected-block sharing take whole (full) blocks only -- a
+      cached prefix is reused in whole blocks (xdnf.cn article, section 六.3)
+      and only a last block may be partly filled.  The new sequence's table is
+      the chosen blocks in the order given.
+* R6  Data movement is recorded as (src, dst) pairs -- copies within the
+      device pool, swap-outs device -> host, swap-ins host -> device -- and
+      handed out by take_moves().  Until then, a block named by a pending pair
+      that drops to reference count 0 is held back from its free stack and
+      pushed (in release order) by take_moves().  So no destination of a batch
+      is reused, and no source overwritten, before the batch has run.
+* R7  An operation whose source block is the destination of a pending pair
+      (its contents not there yet) is refused with Busy, changing nothing.
+  With R6 and R7 the pairs of one batch have distinct destinations, none of
+  them a source of the batch: they can run in any order, or all at once.
+* R8  Swapping a list of sequences maps each distinct block once: sequences
+      of the list that shared a block share its copy.  Only resident
+      sequences fork, share, append or swap out; only swapped-out ones swap in.
+* R9  The tokens reserved by append_slots are written by the caller after the
+      batch's moves have run.  Until the next take_moves(), a sequence that
+      reserved slots cannot be forked, shared from or swapped out (Busy): a
+      copy of its blocks would miss those tokens.
 
 Data movement: copy_blocks copies whole physical blocks within a pool (the
-copy-on-write step); swap_blocks copies whole blocks between two pools (a
-device pool and a host pool).  A physical block of a [num_blocks, num_heads,
-block_size, head_dim] pool is one contiguous run of
-num_heads * block_size * head_dim elements.
+copy-on-write step); swap_blocks copies whole blocks between two pools (device
+and host).  A physical block of a [num_blocks, num_heads, block_size,
+head_dim] pool is one contiguous run of num_heads * block_size * head_dim
+elements.
 """
 from __future__ import annotations
 
@@ -50,80 +76,222 @@ class OutOfBlocks(RuntimeError):
     pass
 
 
-class BlockManager:
-    """Reference block manager: free stack, ref counts, block tables."""
+class Busy(RuntimeError):
+    pass
 
-    def __init__(self, num_blocks: int, block_size: int = 16):
-        self.block_size = block_size
-        self.num_blocks = num_blocks
-        self.free: List[int] = list(range(num_blocks - 1, -1, -1))   # top = end of list
-        self.ref = [0] * num_blocks
-        self.tables: Dict[int, List[int]] = {}
-        self.ntok: Dict[int, int] = {}
-        self.copies: List[Tuple[int, int]] = []
 
-    # ---- sequences ----
-    def add_sequence(self, seq: int) -> None:
-        if seq in self.tables:
-            raise KeyError(f"sequence {seq} exists")
-        self.tables[seq] = []
-        self.ntok[seq] = 0
+class _Pool:
+    """Free stack and reference counts of one pool."""
 
-    def fork(self, parent: int, child: int) -> None:
-        """child starts with every token of parent, on the same physical blocks."""
-        if child in self.tables:
-            raise KeyError(f"sequence {child} exists")
-        self.tables[child] = list(self.tables[parent])
-        self.ntok[child] = self.ntok[parent]
-        for b in self.tables[child]:
-            self.ref[b] += 1
+    def __init__(self, n: int):
+        self.free: List[int] = list(range(n - 1, -1, -1))    # top = end of list
+        self.ref = [0] * n
+        self.held: List[int] = []                            # released while pending (R6)
+        self.pending: set = set()                            # named by a pending pair
+        self.pending_dst: set = set()
 
-    def free_sequence(self, seq: int) -> None:
-        for b in reversed(self.tables.pop(seq)):
-            self.ref[b] -= 1
-            if self.ref[b] == 0:
-                self.free.append(b)
-        del self.ntok[seq]
-
-    # ---- allocation ----
-    def _take(self) -> int:
+    def take(self) -> int:
         b = self.free.pop()
         self.ref[b] = 1
         return b
+
+    def release(self, b: int) -> None:
+        self.ref[b] -= 1
+        if self.ref[b] == 0:
+            (self.held if b in self.pending else self.free).append(b)
+
+    def settle(self) -> None:
+        self.free.extend(self.held)
+        self.held = []
+        self.pending = set()
+        self.pending_dst = set()
+
+
+class BlockManager:
+    """Reference block manager: free stacks, ref counts, block tables."""
+
+    def __init__(self, num_blocks: int, block_size: int = 16, num_host_blocks: int = 0):
+        self.block_size = block_size
+        self.num_blocks = num_blocks
+        self.num_host_blocks = num_host_blocks
+        self.dev = _Pool(num_blocks)
+        self.host = _Pool(num_host_blocks)
+        self.tables: Dict[int, List[int]] = {}
+        self.ntok: Dict[int, int] = {}
+        self.on_host: Dict[int, bool] = {}
+        self.dirty: set = set()                              # reserved slots this batch (R9)
+        self.copies: List[Tuple[int, int]] = []
+        self.swapped_out: List[Tuple[int, int]] = []
+        self.swapped_in: List[Tuple[int, int]] = []
+
+    # convenience views of the device pool (tests read them)
+    @property
+    def free(self) -> List[int]:
+        return self.dev.free
+
+    @property
+    def ref(self) -> List[int]:
+        return self.dev.ref
+
+    def _resident(self, seq: int) -> None:
+        if seq not in self.tables:
+            raise KeyError(f"no sequence {seq}")
+        if self.on_host[seq]:
+            raise KeyError(f"sequence {seq} is swapped out")
+
+    def _clean(self, seq: int) -> None:
+        if seq in self.dirty:
+            raise Busy(f"sequence {seq} reserved slots since the last take_moves()")
+
+    def _new(self, seq: int) -> None:
+        if seq in self.tables:
+            raise KeyError(f"sequence {seq} exists")
+
+    # ---- sequences ----
+    def add_sequence(self, seq: int) -> None:
+        self._new(seq)
+        self.tables[seq] = []
+        self.ntok[seq] = 0
+        self.on_host[seq] = False
+
+    def fork(self, parent: int, child: int) -> None:
+        """Whole-sequence sharing: child starts with every token of parent, on
+        the same physical blocks."""
+        self._resident(parent)
+        self._clean(parent)
+        self._new(child)
+        self.tables[child] = list(self.tables[parent])
+        self.ntok[child] = self.ntok[parent]
+        self.on_host[child] = False
+        for b in self.tables[child]:
+            self.dev.ref[b] += 1
+
+    def share(self, src: int, dst: int, logical_blocks) -> None:
+        """New sequence dst made of the listed full logical blocks of src (R5):
+        list(range(n)) shares a prefix of n blocks."""
+        self._resident(src)
+        self._clean(src)
+        self._new(dst)
+        full = self.ntok[src] // self.block_size
+        idx = [int(i) for i in logical_blocks]
+        if any(i < 0 or i >= full for i in idx):
+            raise ValueError("only full logical blocks of the source can be shared")
+        self.tables[dst] = [self.tables[src][i] for i in idx]
+        self.ntok[dst] = len(idx) * self.block_size
+        self.on_host[dst] = False
+        for b in self.tables[dst]:
+            self.dev.ref[b] += 1
+
+    def free_sequence(self, seq: int) -> None:
+        if seq not in self.tables:
+            raise KeyError(f"no sequence {seq}")
+        pool = self.host if self.on_host[seq] else self.dev
+        for b in reversed(self.tables.pop(seq)):
+            pool.release(b)
+        del self.ntok[seq]
+        del self.on_host[seq]
+        self.dirty.discard(seq)
+
+    # ---- allocation ----
+    def _cow_needed(self, seq: int, n: int) -> bool:
+        have = self.ntok[seq]
+        return n > 0 and have % self.block_size != 0 and self.dev.ref[self.tables[seq][-1]] > 1
 
     def blocks_needed(self, seq: int, n: int) -> int:
         bs = self.block_size
         have = self.ntok[seq]
         new = -(-(have + n) // bs) - (-(-have // bs))
-        cow = n > 0 and have % bs != 0 and self.ref[self.tables[seq][-1]] > 1
-        return new + (1 if cow else 0)
+        return new + (1 if self._cow_needed(seq, n) else 0)
 
     def append_slots(self, seq: int, n: int) -> List[int]:
         """Reserve slots for n new tokens of seq; returns their physical slots
         (block * block_size + row), in token order."""
-        if self.blocks_needed(seq, n) > len(self.free):
+        self._resident(seq)
+        if n < 0:
+            raise ValueError("negative token count")
+        if self._cow_needed(seq, n) and self.tables[seq][-1] in self.dev.pending_dst:
+            raise Busy("the block to copy is the destination of a pending move")
+        if self.blocks_needed(seq, n) > len(self.dev.free):
             raise OutOfBlocks(f"sequence {seq} needs {self.blocks_needed(seq, n)} blocks, "
-                              f"{len(self.free)} free")
+                              f"{len(self.dev.free)} free")
         bs = self.block_size
         table = self.tables[seq]
         slots = []
         for _ in range(n):
             pos = self.ntok[seq]
             if pos % bs == 0:
-                table.append(self._take())
-            elif self.ref[table[-1]] > 1:
+                table.append(self.dev.take())
+            elif self.dev.ref[table[-1]] > 1:
                 old = table[-1]
-                new = self._take()
-                self.ref[old] -= 1
+                new = self.dev.take()
                 self.copies.append((old, new))
+                self.dev.pending |= {old, new}
+                self.dev.pending_dst.add(new)
+                self.dev.release(old)
                 table[-1] = new
             slots.append(table[-1] * bs + pos % bs)
             self.ntok[seq] = pos + 1
+        if n > 0:
+            self.dirty.add(seq)
         return slots
 
-    def take_copies(self) -> List[Tuple[int, int]]:
-        out, self.copies = self.copies, []
+    # ---- swapping ----
+    def _swap(self, seqs, to_host: bool) -> None:
+        src, dst = (self.dev, self.host) if to_host else (self.host, self.dev)
+        seqs = [int(s) for s in seqs]
+        if len(set(seqs)) != len(seqs):
+            raise KeyError("a sequence is listed twice")
+        for s in seqs:
+            if s not in self.tables or self.on_host[s] == to_host:
+                raise KeyError(f"sequence {s} cannot be swapped {'out' if to_host else 'in'}")
+        for s in seqs:
+            self._clean(s)
+        distinct = []
+        for s in seqs:
+            for b in self.tables[s]:
+                if b not in distinct:
+                    distinct.append(b)
+        if any(b in src.pending_dst for b in distinct):
+            raise Busy("a block to move is the destination of a pending move")
+        if len(distinct) > len(dst.free):
+            raise OutOfBlocks(f"{len(distinct)} blocks needed, {len(dst.free)} free")
+        moved = {}
+        record = self.swapped_out if to_host else self.swapped_in
+        for s in seqs:
+            table = self.tables[s]
+            for j, b in enumerate(table):
+                if b in moved:
+                    dst.ref[moved[b]] += 1
+                else:
+                    moved[b] = dst.take()
+                    record.append((b, moved[b]))
+                    src.pending.add(b)
+                    dst.pending.add(moved[b])
+                    dst.pending_dst.add(moved[b])
+                src.release(b)
+                table[j] = moved[b]
+            self.on_host[s] = to_host
+
+    def swap_out(self, seqs) -> None:
+        self._swap(seqs, True)
+
+    def swap_in(self, seqs) -> None:
+        self._swap(seqs, False)
+
+    # ---- pending data movement ----
+    def take_moves(self):
+        """(copies, swap_out, swap_in) recorded since the last call; releases
+        the blocks held back for them (R6)."""
+        out = (self.copies, self.swapped_out, self.swapped_in)
+        self.copies, self.swapped_out, self.swapped_in = [], [], []
+        self.dirty = set()
+        self.dev.settle()
+        self.host.settle()
         return out
+
+    def take_copies(self) -> List[Tuple[int, int]]:
+        """Device copies only (for callers that never swap)."""
+        return self.take_moves()[0]
 
     # ---- queries ----
     def block_table(self, seq: int) -> List[int]:
@@ -132,20 +300,38 @@ class BlockManager:
     def num_tokens(self, seq: int) -> int:
         return self.ntok[seq]
 
-    def num_free(self) -> int:
-        return len(self.free)
+    def is_swapped(self, seq: int) -> bool:
+        return self.on_host[seq]
+
+    def num_free(self, host: bool = False) -> int:
+        return len((self.host if host else self.dev).free)
+
+    def shared_prefix_blocks(self, seq: int) -> int:
+        """Leading table entries whose block another sequence also holds."""
+        n = 0
+        for b in self.tables[seq]:
+            if self.dev.ref[b] < 2:
+                break
+            n += 1
+        return n
 
     def check_invariants(self) -> None:
-        """Reference counts equal table occurrences; free blocks are exactly the
-        unreferenced ones; only last blocks may be partly filled."""
-        count = [0] * self.num_blocks
+        """Reference counts equal table occurrences; free plus held-back blocks
+        are exactly the unreferenced ones; only last blocks may be partly
+        filled."""
+        for host, pool, n in ((False, self.dev, self.num_blocks),
+                              (True, self.host, self.num_host_blocks)):
+            count = [0] * n
+            for seq, t in self.tables.items():
+                if self.on_host[seq] == host:
+                    for b in t:
+                        count[b] += 1
+            assert count == pool.ref
+            idle = pool.free + pool.held
+            assert sorted(idle) == [b for b in range(n) if count[b] == 0]
+            assert len(set(idle)) == len(idle)
         for seq, t in self.tables.items():
-            for b in t:
-                count[b] += 1
             assert len(t) == -(-self.ntok[seq] // self.block_size), seq
-        assert count == self.ref
-        assert sorted(self.free) == [b for b in range(self.num_blocks) if count[b] == 0]
-        assert len(set(self.free)) == len(self.free)
 
 
 # --------------------------------------------------------------------------
