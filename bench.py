@@ -13,6 +13,11 @@ shuffled pool) with split-K partitions and their merge.
   mixed     chunked prefill of 4 x 512-token chunks over paged prefixes, then
             decode of 192 sequences sharing 2048-token prefixes in groups of 3
             (also timed with prefill and decode on two streams)
+  block_moves  the data movement around the step at the Llama-2-13B pool shape:
+            copy-on-write block copies (pa_copy_blocks, 1024 pairs in one call;
+            the metric of that line is its read + write GB/s), swaps to and
+            from pinned host memory (pa_swap_blocks), and the native block
+            manager's host time for one decode step of 256 sequences
 
 Inputs are seeded synthetic data already resident in GPU memory before timing
 starts.  Prints one JSON line: KV GB/s over the whole step (the metric), % of
@@ -227,7 +232,8 @@ class StepTimer:
                 for k, (name, _) in enumerate(launches)}
 
 
-WORKLOADS = ("llama13b", "llama7b", "gqa", "mixed")
+WORKLOADS = ("llama13b", "llama7b", "gqa", "mixed", "block_moves")
+COPY_METRIC = "paged KV block copy GB/s (copy-on-write, read + write bytes) at Llama-2-13B pool shape"
 
 
 def build_workload(name: str, ps: int):
@@ -249,6 +255,119 @@ def build_workload(name: str, ps: int):
         "prefill": "4 x 512-token causal chunks over paged prefixes U{0..3584}",
         "decode": "64 prompts x 3 samples sharing 2048-token prefixes + U{0..512} private",
         "seed": 457}
+
+
+def bench_block_moves(args, torch, dev, lib, timer) -> int:
+    """pa_copy_blocks / pa_swap_blocks throughput and block-manager host time."""
+    import numpy as np
+
+    nb, hkv, d, bs, pairs_n = 65536, 40, 128, 16, 1024
+    block_bytes = hkv * bs * d * 2
+    log("bench: allocating two 10 GiB bf16 pools")
+    g = torch.Generator(device=dev).manual_seed(453)
+    kc = torch.randint(-2**15, 2**15, (nb, hkv, bs, d), dtype=torch.int16, device=dev,
+                       generator=g).view(torch.bfloat16)
+    vc = torch.randint(-2**15, 2**15, (nb, hkv, bs, d), dtype=torch.int16, device=dev,
+                       generator=g).view(torch.bfloat16)
+    rng = np.random.default_rng(453)
+    ids = rng.permutation(nb)
+    pairs = np.stack([rng.choice(ids[pairs_n:], pairs_n), ids[:pairs_n]], 1).astype(np.int32)
+    mapping = torch.from_numpy(pairs).to(dev)
+    stream = torch.cuda.current_stream()
+
+    def copy():
+        lib.pa_copy_blocks(kc, vc, mapping, stream=stream)
+
+    for _ in range(args.warmup):
+        copy()
+    torch.cuda.synchronize()
+    log(f"bench: timing {args.steps} copy launches")
+    ms = timer.per_launch([("copy_blocks", copy)], args.steps, stream)["copy_blocks"]
+    algo = 2 * 2 * pairs_n * block_bytes              # K and V, read + write
+    gbs = algo / (ms * 1e-3) / 1e9
+
+    # swaps: 256 scattered blocks, and one run of 256 consecutive blocks
+    nh, sw = 1024, 256
+    hk = torch.empty((nh, hkv, bs, d), dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty((nh, hkv, bs, d), dtype=torch.bfloat16, pin_memory=True)
+    scattered = np.stack([rng.choice(nb, sw, replace=False),
+                          rng.choice(nh, sw, replace=False)], 1).astype(np.int32)
+    run = np.stack([np.arange(4096, 4096 + sw), np.arange(sw)], 1).astype(np.int32)
+    swaps = {}
+    for name, m in (("scattered", scattered), ("one_run", run)):
+        for direction, (a, b) in (("out", ((kc, vc), (hk, hv))), ("in", ((hk, hv), (kc, vc)))):
+            src_m = m if direction == "out" else m[:, ::-1].copy()
+
+            def sw_call(a=a, b=b, src_m=src_m):
+                lib.pa_swap_blocks(a[0], a[1], b[0], b[1], src_m, stream=stream)
+
+            sw_call()
+            torch.cuda.synchronize()
+            t = timer.per_step(sw_call, max(3, args.steps // 5), [stream])
+            swaps[f"{direction}_{name}"] = {
+                "ms": round(t, 4), "gbs": round(2 * sw * block_bytes / (t * 1e-3) / 1e9, 2)}
+    log("bench: swaps " + ", ".join(f"{k} {v['gbs']} GB/s" for k, v in swaps.items()))
+
+    # block manager host time for one decode step of 256 sequences
+    bm = lib.BlockManager(nb, bs, 0)
+    seqs = np.arange(256, dtype=np.int64)
+    lens = np.clip(np.round(rng.lognormal(np.log(1024), 0.5, 256)), 16, 4096).astype(np.int32)
+    for s_, n_ in zip(seqs, lens):
+        bm.add_sequence(int(s_))
+        bm.append_slots(int(s_), int(n_) - 1)
+    bm.take_moves()
+    ones = np.ones(256, dtype=np.int32)
+    reps = 200
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        slots, done, st = bm.append_batch(seqs, ones)
+        bm.take_moves()
+        tables, cl, sh = bm.build_batch(seqs, 320)
+    host_us = (time.perf_counter() - t0) / reps * 1e6
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        log("bench: timing the CPU oracle block copy on a sample")
+        nbs = 2048
+        kp = np.zeros((nbs, hkv, bs, d), dtype=np.uint16)
+        sp = pairs[:64] % nbs
+        sp = sp[np.unique(sp[:, 1], return_index=True)[1]]
+        t0 = time.perf_counter()
+        n_calls = 0
+        while time.perf_counter() - t0 < 10.0:
+            oracle.copy_blocks(kp, sp)
+            n_calls += 1
+        el = time.perf_counter() - t0
+        cpu = {"value": round(2 * len(sp) * block_bytes * n_calls / el / 1e9, 3),
+               "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"oracle.copy_blocks on one {nbs}-block 13B-shaped pool, {len(sp)} "
+                         f"pairs, {n_calls} calls in {el:.1f} s (the oracle returns a copied "
+                         "pool, so each call also copies the whole pool)"}
+
+    result = {
+        "metric": COPY_METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "copy-on-write block copies, 1024 pairs, Llama-2-13B pools "
+                               "(65536 blocks x 40 kv heads x 16 x 128 bf16, 10 GiB each)",
+                   "pairs": pairs_n, "block_bytes_per_pool": block_bytes, "seed": 453},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "copy_blocks_kernel<u32x4>",
+                     "algorithmic_bytes_per_launch": int(algo)},
+        "swap_blocks_256": swaps,
+        "swap_note": "pa_swap_blocks between the device pools and pinned host pools, K and V, "
+                     "GB/s over PCIe; scattered = 256 random block ids (one copy per block "
+                     "and pool), one_run = 256 consecutive ids merged into one copy per pool",
+        "block_manager_host_us_per_step": round(host_us, 1),
+        "block_manager_note": "append_batch (1 token x 256 sequences) + take_moves + "
+                              "build_batch (256 x 320 table) through the C ABI from Python",
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
 
 
 def main(argv=None):
@@ -291,6 +410,9 @@ def main(argv=None):
     ps = args.partition_size
     if ps is None:
         ps = 512 if args.workload == "gqa" else 2048
+
+    if args.workload == "block_moves":
+        return bench_block_moves(args, torch, dev, lib, StepTimer(torch))
 
     log(f"bench: generating the {args.workload} workload")
     t0 = time.time()

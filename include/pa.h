@@ -17,11 +17,13 @@
  *
  * Conventions shared by every entry point
  *  - Ownership: the caller allocates and owns every buffer (device memory),
- *    workspace included.  The library allocates no device memory, keeps no
- *    state between calls and never synchronises.  Outputs must not alias
- *    inputs.
- *  - Asynchrony: every call only enqueues kernels on `stream` (NULL = the
- *    default stream) and returns; results are ready when the stream is.
+ *    workspace included.  The library allocates no device memory and never
+ *    synchronises; the kernels' entry points keep no state between calls.
+ *    The one stateful object is the block manager (pa_bm_*), host memory the
+ *    caller creates and destroys.  Outputs must not alias inputs.
+ *  - Asynchrony: every call that takes a `stream` only enqueues kernels or
+ *    copies on it (NULL = the default stream) and returns; results are ready
+ *    when the stream is.  The block manager's calls are plain host calls.
  *  - Errors: invalid scalar arguments or null pointers return a negative
  *    pa_status before any HIP call is made, and nothing is launched.  A failed
  *    launch returns PA_ERR_LAUNCH.  The contents of device arrays (block ids,
@@ -53,7 +55,14 @@ typedef enum {
   PA_ERR_SHAPE = -2,       /* a size is negative, zero where it must not be, or inconsistent */
   PA_ERR_UNSUPPORTED = -3, /* block_size, head_dim, dtype or group size outside the supported set */
   PA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than pa_decode_workspace_bytes() */
-  PA_ERR_LAUNCH = -5       /* the HIP runtime refused a kernel launch */
+  PA_ERR_LAUNCH = -5,      /* the HIP runtime refused a kernel launch or a copy */
+  PA_ERR_NO_BLOCKS = -6,   /* block manager: a pool has too few free blocks; nothing changed */
+  PA_ERR_SEQ = -7,         /* block manager: unknown or duplicate sequence id, or the sequence
+                              is on the wrong side (swapped out / resident) for the call */
+  PA_ERR_BUSY = -8,        /* block manager: the call needs data a pending move has not
+                              delivered yet; take and run the moves first.  Nothing changed */
+  PA_ERR_NO_MEMORY = -9,   /* block manager: host allocation failed */
+  PA_ERR_STATE = -10       /* block manager: an internal invariant does not hold */
 } pa_status;
 
 /*
@@ -167,6 +176,148 @@ int pa_prefill_chunk(void* out, const void* query, const void* key_cache, const 
                      int num_heads, int num_kv_heads, int head_dim, int block_size,
                      int max_blocks_per_seq, int64_t num_blocks, int max_query_len, float scale,
                      pa_dtype dtype, hipStream_t stream);
+
+/*
+ * pa_copy_blocks -- copy whole physical blocks inside the K and V pools.
+ *
+ * For each pair (src, dst) = (block_mapping[2i], block_mapping[2i+1]) copies
+ * block src of key_cache onto block dst, and the same in value_cache, bit for
+ * bit.  This is the copy of copy-on-write: a sequence about to write into a
+ * partly filled block it still shares gets its own copy first
+ * (intelliparadigm.com article, sections 2.2 and 3.3).  The pairs
+ * pa_bm_take_moves() hands out as copies are made for this call.
+ *
+ *  key_cache,
+ *  value_cache    [num_blocks, num_kv_heads, block_size, head_dim], dtype; updated in place.
+ *  block_mapping  device int32 [num_pairs][2].
+ * The pairs must be independent: destinations distinct and none of them a
+ * source of the call (they run all at once).  A pair naming a block outside
+ * [0, num_blocks), or with src == dst, is skipped.
+ */
+int pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* block_mapping,
+                   int64_t num_pairs, int num_kv_heads, int head_dim, int block_size,
+                   int64_t num_blocks, pa_dtype dtype, hipStream_t stream);
+
+/*
+ * pa_swap_blocks -- copy whole blocks between two pools, one of them usually
+ * in host memory: the swap space a sequence's blocks move to when it is
+ * preempted and from which they return (intelliparadigm.com article, section
+ * 5.1, swap space).
+ *
+ * For each pair (src, dst) copies block src of src_key / src_value onto block
+ * dst of dst_key / dst_value, bit for bit, with the HIP runtime's copy engines
+ * (hipMemcpyAsync, direction from the pointers).  Runs of pairs whose sources
+ * and destinations both advance by one are merged into one copy.
+ *
+ *  src_key, src_value  [src_num_blocks, num_kv_heads, block_size, head_dim]
+ *  dst_key, dst_value  [dst_num_blocks, num_kv_heads, block_size, head_dim]
+ *  block_mapping       HOST int32 [num_pairs][2]; every id must be in range
+ *                      (else PA_ERR_SHAPE and nothing is copied).
+ * Host pools should be pinned (hipHostMalloc): copies from or to pageable
+ * memory are not asynchronous.  The pairs must be independent, as for
+ * pa_copy_blocks.  A failed copy returns PA_ERR_LAUNCH; copies enqueued
+ * before it stay enqueued.
+ */
+int pa_swap_blocks(const void* src_key, const void* src_value, void* dst_key, void* dst_value,
+                   const int32_t* block_mapping, int64_t num_pairs, int64_t src_num_blocks,
+                   int64_t dst_num_blocks, int num_kv_heads, int head_dim, int block_size,
+                   pa_dtype dtype, hipStream_t stream);
+
+/*
+ * Block manager -- host bookkeeping of which physical blocks hold which
+ * sequence's tokens; it produces the block tables, context lengths and slot
+ * mappings the kernels above take, and the block moves that keep them right.
+ *
+ * Model ("vLLM 基本原理", section PagedAttention, items 1-3, 按需分配 and 内存共享;
+ * intelliparadigm.com article, sections 2.2, 2.3, 3.3 and 5.1; xdnf.cn article,
+ * section 六.1):
+ *  - a device pool of num_blocks blocks and a host pool (swap space) of
+ *    num_host_blocks, each with a free stack and per-block reference counts;
+ *  - a sequence (caller-chosen int64 id) owns a block table; it takes a new
+ *    block only when its last block is full, so only the last block may be
+ *    partly filled;
+ *  - sharing: pa_bm_fork gives a new sequence every block of another (whole
+ *    sequence), pa_bm_share chosen full blocks of another (a prefix, or any
+ *    list of logical blocks); shared blocks count their holders;
+ *  - copy on write: a sequence appending into a partly filled last block that
+ *    others still hold gets a fresh block and a pending copy (old, new); the
+ *    last holder writes in place;
+ *  - a freed sequence returns its blocks at once; swap out / swap in move a
+ *    sequence's blocks between the pools, each distinct block once per call.
+ *
+ * Policy: free blocks are a stack (the most recently released is reused
+ * first; at the start ids come out in increasing order); a freed table is
+ * released last entry first; every call is all-or-nothing -- on any error
+ * nothing changes.
+ *
+ * Moves: copies (device -> device), swap-outs (device -> host) and swap-ins
+ * (host -> device) accumulate as (src, dst) pairs until pa_bm_take_moves().
+ * Until then a block named by a pending pair is not reused even if released,
+ * and a call that would read a pending destination fails with PA_ERR_BUSY, so
+ * the pairs of one take never overlap and may run in any order.
+ *
+ * The caller's step: free finished sequences, swap out / swap in, fork and
+ * share, append slots (pa_bm_append_slots / pa_bm_append_batch), take the
+ * moves and run them (pa_copy_blocks, pa_swap_blocks), then write the new
+ * tokens' K/V into the slots (pa_reshape_and_cache) and run attention with
+ * pa_bm_build_batch's tables.  A sequence that reserved slots since the last
+ * take cannot be forked, shared from or swapped out (PA_ERR_BUSY): its new
+ * tokens are not in its blocks yet.
+ *
+ * Not thread-safe: one caller thread per manager.  Block ids are int32, token
+ * counts int64, slots int64 (block * block_size + row).
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+/* Creates a manager; *out is NULL on error.  block_size must be 16. */
+int pa_bm_create(int64_t num_blocks, int64_t num_host_blocks, int block_size,
+                 pa_block_manager** out);
+void pa_bm_destroy(pa_block_manager* bm);
+/* A new, empty resident sequence (PA_ERR_SEQ if the id exists). */
+int pa_bm_add_sequence(pa_block_manager* bm, int64_t seq);
+/* Whole-sequence sharing: child starts with all of parent's tokens, on the same blocks. */
+int pa_bm_fork(pa_block_manager* bm, int64_t parent, int64_t child);
+/* New sequence dst whose table is src's logical blocks logical_blocks[0..count-1], in that
+ * order; each must be a full block of src (PA_ERR_SHAPE otherwise).  dst holds count *
+ * block_size tokens.  0..n-1 shares a prefix of n blocks. */
+int pa_bm_share(pa_block_manager* bm, int64_t src, int64_t dst, const int32_t* logical_blocks,
+                int32_t count);
+/* Releases the sequence's blocks (device or host) and forgets it. */
+int pa_bm_free_sequence(pa_block_manager* bm, int64_t seq);
+/* Reserves count new token slots at the end of a resident sequence; slots (host, int64
+ * [count]) receives them in token order.  May take new blocks and record copies. */
+int pa_bm_append_slots(pa_block_manager* bm, int64_t seq, int32_t count, int64_t* slots);
+/* pa_bm_append_slots for seqs[0..num_seqs-1] in order, slots back to back in slot_mapping
+ * (host int64 [sum counts]).  Stops at the first sequence that fails and returns its status;
+ * *num_done = sequences fully served (their slots are valid, the failed one changed nothing). */
+int pa_bm_append_batch(pa_block_manager* bm, const int64_t* seqs, const int32_t* counts,
+                       int32_t num_seqs, int64_t* slot_mapping, int32_t* num_done);
+/* Moves resident sequences to the host pool / swapped-out sequences back to the device. */
+int pa_bm_swap_out(pa_block_manager* bm, const int64_t* seqs, int32_t count);
+int pa_bm_swap_in(pa_block_manager* bm, const int64_t* seqs, int32_t count);
+/* counts[0..2] = pending copies, swap-outs, swap-ins. */
+int pa_bm_pending_moves(const pa_block_manager* bm, int64_t* counts);
+/* Writes the pending pairs as int32 (src, dst) into host arrays of 2 * count entries each
+ * (NULL allowed for an empty list), clears them and releases the blocks held back for them. */
+int pa_bm_take_moves(pa_block_manager* bm, int32_t* copies, int32_t* swap_out, int32_t* swap_in);
+int pa_bm_num_tokens(const pa_block_manager* bm, int64_t seq, int64_t* num_tokens);
+int pa_bm_is_swapped(const pa_block_manager* bm, int64_t seq, int32_t* swapped);
+/* Copies the table (device ids if resident, host ids if swapped out) into table[capacity];
+ * *length is set even when capacity is too small (then PA_ERR_SHAPE). */
+int pa_bm_block_table(const pa_block_manager* bm, int64_t seq, int32_t* table, int32_t capacity,
+                      int32_t* length);
+/* Free blocks of the device pool (host == 0) or the host pool; negative status on error. */
+int64_t pa_bm_num_free(const pa_block_manager* bm, int host);
+/* Attention inputs for resident sequences seqs[0..num_seqs-1], into host arrays:
+ * block_tables int32 [num_seqs, max_blocks_per_seq] (unused entries -1), context_lens int32
+ * [num_seqs], and optionally shared_prefix_blocks int32 [num_seqs] = leading table entries
+ * whose block another sequence also holds (pa_decode's cache hint). */
+int pa_bm_build_batch(const pa_block_manager* bm, const int64_t* seqs, int32_t num_seqs,
+                      int32_t max_blocks_per_seq, int32_t* block_tables, int32_t* context_lens,
+                      int32_t* shared_prefix_blocks);
+/* Checks the invariants (reference counts = table occurrences, free + held-back blocks =
+ * unreferenced ones, table lengths = ceil(tokens / block_size)): PA_OK or PA_ERR_STATE. */
+int pa_bm_check(const pa_block_manager* bm);
 
 /* Human-readable name of a pa_status value (static storage). */
 const char* pa_status_string(int status);

@@ -1,11 +1,24 @@
 """Paged attention for AMD Instinct MI355X (gfx950).
 
-The compute lives in libpa.so (hand-written HIP kernels behind a C ABI declared
-in include/pa.h); `lib` is its thin ctypes binding.
+The compute lives in libpa.so (hand-written HIP kernels and the native block
+manager behind a C ABI declared in include/pa.h); `lib` is its thin ctypes
+binding.
 """
 from . import lib
 from .lib import (pa_decode, pa_decode_splitk_reduce, pa_decode_workspace_bytes,
-                  pa_prefill_chunk, pa_reshape_and_cache, PagedAttentionError)
+                  pa_prefill_chunk, pa_reshape_and_cache, pa_copy_blocks, pa_swap_blocks,
+                  pa_bm_create, pa_bm_destroy, pa_bm_add_sequence, pa_bm_fork, pa_bm_share,
+                  pa_bm_free_sequence, pa_bm_append_slots, pa_bm_append_batch, pa_bm_swap_out,
+                  pa_bm_swap_in, pa_bm_pending_moves, pa_bm_take_moves, pa_bm_num_tokens,
+                  pa_bm_is_swapped, pa_bm_block_table, pa_bm_num_free, pa_bm_build_batch,
+                  pa_bm_check, BlockManager, Busy, OutOfBlocks, PagedAttentionError,
+                  SequenceError, ShapeError)
 
 __all__ = ["lib", "pa_decode", "pa_decode_splitk_reduce", "pa_decode_workspace_bytes",
-           "pa_prefill_chunk", "pa_reshape_and_cache", "PagedAttentionError"]
+           "pa_prefill_chunk", "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks",
+           "pa_bm_create", "pa_bm_destroy", "pa_bm_add_sequence", "pa_bm_fork", "pa_bm_share",
+           "pa_bm_free_sequence", "pa_bm_append_slots", "pa_bm_append_batch", "pa_bm_swap_out",
+           "pa_bm_swap_in", "pa_bm_pending_moves", "pa_bm_take_moves", "pa_bm_num_tokens",
+           "pa_bm_is_swapped", "pa_bm_block_table", "pa_bm_num_free", "pa_bm_build_batch",
+           "pa_bm_check", "BlockManager", "Busy", "OutOfBlocks", "PagedAttentionError",
+           "SequenceError", "ShapeError"]

@@ -39,7 +39,12 @@ const char* pa_status_string(int status) {
     case PA_ERR_SHAPE: return "invalid or inconsistent size argument";
     case PA_ERR_UNSUPPORTED: return "unsupported block_size, head_dim, dtype or group size";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
-    case PA_ERR_LAUNCH: return "kernel launch failed";
+    case PA_ERR_LAUNCH: return "kernel launch or copy failed";
+    case PA_ERR_NO_BLOCKS: return "not enough free blocks";
+    case PA_ERR_SEQ: return "unknown or duplicate sequence, or wrong side of a swap";
+    case PA_ERR_BUSY: return "pending block moves must be taken and run first";
+    case PA_ERR_NO_MEMORY: return "host allocation failed";
+    case PA_ERR_STATE: return "block manager invariant violated";
     default: return "unknown status";
   }
 }
@@ -207,6 +212,60 @@ int pa_prefill_chunk(void* out, const void* query, const void* key_cache, const 
   a.scale_log2 = scale * 1.4426950408889634f;
   if (dtype == PA_BF16) return status_of(pa::launch_prefill_mfma(a, head_dim, stream));
   return status_of(pa::launch_decode(a, head_dim, false, stream));
+}
+
+int pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* block_mapping,
+                   int64_t num_pairs, int num_kv_heads, int head_dim, int block_size,
+                   int64_t num_blocks, pa_dtype dtype, hipStream_t stream) {
+  if (!key_cache || !value_cache) return PA_ERR_NULL;
+  if (num_pairs > 0 && !block_mapping) return PA_ERR_NULL;
+  if (!dtype_ok(dtype) || block_size != kBlockSize || !head_dim_ok(head_dim))
+    return PA_ERR_UNSUPPORTED;
+  if (num_pairs < 0 || num_kv_heads < 1 || num_blocks < 1) return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  pa::CopyArgs a;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_mapping = block_mapping;
+  a.num_pairs = num_pairs;
+  a.block_bytes = (int64_t)num_kv_heads * kBlockSize * head_dim * elem_bytes(dtype);
+  a.num_blocks = num_blocks;
+  return status_of(pa::launch_copy_blocks(a, stream));
+}
+
+int pa_swap_blocks(const void* src_key, const void* src_value, void* dst_key, void* dst_value,
+                   const int32_t* block_mapping, int64_t num_pairs, int64_t src_num_blocks,
+                   int64_t dst_num_blocks, int num_kv_heads, int head_dim, int block_size,
+                   pa_dtype dtype, hipStream_t stream) {
+  if (!src_key || !src_value || !dst_key || !dst_value) return PA_ERR_NULL;
+  if (num_pairs > 0 && !block_mapping) return PA_ERR_NULL;
+  if (!dtype_ok(dtype) || block_size != kBlockSize || !head_dim_ok(head_dim))
+    return PA_ERR_UNSUPPORTED;
+  if (num_pairs < 0 || num_kv_heads < 1 || src_num_blocks < 1 || dst_num_blocks < 1)
+    return PA_ERR_SHAPE;
+  for (int64_t i = 0; i < num_pairs; ++i) {
+    const int32_t s = block_mapping[2 * i], d = block_mapping[2 * i + 1];
+    if (s < 0 || s >= src_num_blocks || d < 0 || d >= dst_num_blocks) return PA_ERR_SHAPE;
+  }
+  const size_t bb = (size_t)num_kv_heads * kBlockSize * head_dim * elem_bytes(dtype);
+  const char* sk = static_cast<const char*>(src_key);
+  const char* sv = static_cast<const char*>(src_value);
+  char* dk = static_cast<char*>(dst_key);
+  char* dv = static_cast<char*>(dst_value);
+  for (int64_t i = 0; i < num_pairs;) {
+    // merge the run of pairs whose source and destination both advance by one
+    const int64_t s0 = block_mapping[2 * i], d0 = block_mapping[2 * i + 1];
+    int64_t n = 1;
+    while (i + n < num_pairs && block_mapping[2 * (i + n)] == s0 + n &&
+           block_mapping[2 * (i + n) + 1] == d0 + n)
+      ++n;
+    if (hipMemcpyAsync(dk + d0 * bb, sk + s0 * bb, n * bb, hipMemcpyDefault, stream) !=
+            hipSuccess ||
+        hipMemcpyAsync(dv + d0 * bb, sv + s0 * bb, n * bb, hipMemcpyDefault, stream) != hipSuccess)
+      return PA_ERR_LAUNCH;
+    i += n;
+  }
+  return PA_OK;
 }
 
 }  // extern "C"

@@ -58,12 +58,22 @@ struct ReduceArgs {
   int max_context_len;
 };
 
+struct CopyArgs {
+  void* key_cache;
+  void* value_cache;
+  const int32_t* block_mapping;   // device, [num_pairs][2] = (src, dst)
+  int64_t num_pairs;
+  int64_t block_bytes;            // bytes of one physical block of one pool
+  int64_t num_blocks;
+};
+
 hipError_t launch_reshape_and_cache(const ScatterArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t stream);
 hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_valu_bf16(const DecodeArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_decode_valu_f32(const DecodeArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_splitk_reduce(const ReduceArgs& a, int head_dim, bool bf16, hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
 hipError_t launch_prefill_mfma(const DecodeArgs& a, int head_dim, hipStream_t stream);
 
 }  // namespace pa

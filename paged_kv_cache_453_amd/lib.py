@@ -20,11 +20,34 @@ PA_BF16 = 1
 _lib: Optional[ctypes.CDLL] = None
 
 
+PA_ERR_SHAPE, PA_ERR_NO_BLOCKS, PA_ERR_SEQ, PA_ERR_BUSY = -2, -6, -7, -8
+
+
 class PagedAttentionError(RuntimeError):
     def __init__(self, fn: str, status: int):
         self.status = status
         msg = _lib.pa_status_string(status).decode() if _lib is not None else str(status)
         super().__init__(f"{fn} returned {status}: {msg}")
+
+
+class OutOfBlocks(PagedAttentionError):
+    """A pool has too few free blocks; the manager changed nothing."""
+
+
+class Busy(PagedAttentionError):
+    """Pending block moves must be taken and run first; nothing changed."""
+
+
+class SequenceError(PagedAttentionError):
+    """Unknown or duplicate sequence id, or the wrong side of a swap."""
+
+
+class ShapeError(PagedAttentionError):
+    """A size or index argument is out of range."""
+
+
+_ERRORS = {PA_ERR_NO_BLOCKS: OutOfBlocks, PA_ERR_BUSY: Busy, PA_ERR_SEQ: SequenceError,
+           PA_ERR_SHAPE: ShapeError}
 
 
 def load() -> ctypes.CDLL:
@@ -52,12 +75,40 @@ def load() -> ctypes.CDLL:
     lib.pa_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                      i32, i64, i32, f32, i32, vp]
     lib.pa_prefill_chunk.restype = i32
+    lib.pa_copy_blocks.argtypes = [vp, vp, vp, i64, i32, i32, i32, i64, i32, vp]
+    lib.pa_copy_blocks.restype = i32
+    lib.pa_swap_blocks.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, vp]
+    lib.pa_swap_blocks.restype = i32
+    pp = ctypes.POINTER(ctypes.c_void_p)
+    for name, args, res in (
+            ("pa_bm_create", [i64, i64, i32, pp], i32),
+            ("pa_bm_destroy", [vp], None),
+            ("pa_bm_add_sequence", [vp, i64], i32),
+            ("pa_bm_fork", [vp, i64, i64], i32),
+            ("pa_bm_share", [vp, i64, i64, vp, i32], i32),
+            ("pa_bm_free_sequence", [vp, i64], i32),
+            ("pa_bm_append_slots", [vp, i64, i32, vp], i32),
+            ("pa_bm_append_batch", [vp, vp, vp, i32, vp, vp], i32),
+            ("pa_bm_swap_out", [vp, vp, i32], i32),
+            ("pa_bm_swap_in", [vp, vp, i32], i32),
+            ("pa_bm_pending_moves", [vp, vp], i32),
+            ("pa_bm_take_moves", [vp, vp, vp, vp], i32),
+            ("pa_bm_num_tokens", [vp, i64, vp], i32),
+            ("pa_bm_is_swapped", [vp, i64, vp], i32),
+            ("pa_bm_block_table", [vp, i64, vp, i32, vp], i32),
+            ("pa_bm_num_free", [vp, i32], i64),
+            ("pa_bm_build_batch", [vp, vp, i32, i32, vp, vp, vp], i32),
+            ("pa_bm_check", [vp], i32)):
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
     _lib = lib
     return lib
 
 
 EXPORTED = ("pa_reshape_and_cache", "pa_decode_workspace_bytes", "pa_decode",
-            "pa_decode_splitk_reduce", "pa_prefill_chunk", "pa_status_string")
+            "pa_decode_splitk_reduce", "pa_prefill_chunk", "pa_copy_blocks", "pa_swap_blocks",
+            "pa_status_string")
 
 
 # --------------------------------------------------------------------------
@@ -94,7 +145,7 @@ def _need(cond: bool, what: str):
 
 def _check(fn: str, status: int):
     if status != 0:
-        raise PagedAttentionError(fn, status)
+        raise _ERRORS.get(status, PagedAttentionError)(fn, status)
 
 
 def _on_gpu(*ts):
@@ -193,3 +244,217 @@ def pa_prefill_chunk(out, query, key_cache, value_cache, block_tables, query_sta
         _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
         _ptr(query_start_loc), _ptr(context_lens), s, tq, hq, hkv, d, bs, block_tables.shape[1],
         nb, int(max_query_len), float(scale), _dtype_code(query), _stream(stream)))
+
+
+# --------------------------------------------------------------------------
+# block data movement
+# --------------------------------------------------------------------------
+def pa_copy_blocks(key_cache, value_cache, block_mapping, stream=None) -> None:
+    """Copy block src onto block dst in both pools for each row (src, dst) of
+    block_mapping (device int32 [n, 2]); pairs must be independent."""
+    torch = _torch()
+    lib = load()
+    _on_gpu(key_cache, value_cache, block_mapping)
+    _need(block_mapping.dtype == torch.int32 and block_mapping.dim() == 2 and
+          block_mapping.shape[1] == 2, "block_mapping must be int32 [n, 2]")
+    _need(key_cache.dtype == value_cache.dtype and key_cache.shape == value_cache.shape,
+          "caches differ")
+    nb, hkv, bs, d = key_cache.shape
+    _check("pa_copy_blocks", lib.pa_copy_blocks(
+        _ptr(key_cache), _ptr(value_cache), _ptr(block_mapping), block_mapping.shape[0], hkv, d,
+        bs, nb, _dtype_code(key_cache), _stream(stream)))
+
+
+def pa_swap_blocks(src_key, src_value, dst_key, dst_value, block_mapping, stream=None) -> None:
+    """Copy block src of (src_key, src_value) onto block dst of (dst_key, dst_value) for each
+    row of block_mapping (host int32 [n, 2]: numpy array or CPU tensor).  Either side may be
+    host memory (pinned for asynchronous copies) or device memory."""
+    import numpy as np
+    lib = load()
+    m = np.ascontiguousarray(np.asarray(block_mapping, dtype=np.int32).reshape(-1, 2))
+    for t in (src_key, src_value, dst_key, dst_value):
+        _need(t.is_contiguous(), "pools must be contiguous")
+    _need(src_key.shape == src_value.shape and dst_key.shape == dst_value.shape and
+          src_key.shape[1:] == dst_key.shape[1:], "pool shapes differ")
+    _need(src_key.dtype == src_value.dtype == dst_key.dtype == dst_value.dtype, "dtype mismatch")
+    nbs, hkv, bs, d = src_key.shape
+    _check("pa_swap_blocks", lib.pa_swap_blocks(
+        _ptr(src_key), _ptr(src_value), _ptr(dst_key), _ptr(dst_value),
+        m.ctypes.data if m.size else None, m.shape[0], nbs, dst_key.shape[0], hkv, d, bs,
+        _dtype_code(src_key), _stream(stream)))
+
+
+# --------------------------------------------------------------------------
+# block manager (host object behind an opaque handle)
+# --------------------------------------------------------------------------
+def _np():
+    import numpy as np
+    return np
+
+
+def _i64s(xs):
+    np = _np()
+    a = np.ascontiguousarray(np.asarray(xs, dtype=np.int64).reshape(-1))
+    return a, (a.ctypes.data if a.size else None)
+
+
+def pa_bm_create(num_blocks: int, num_host_blocks: int = 0, block_size: int = 16):
+    h = ctypes.c_void_p()
+    _check("pa_bm_create", load().pa_bm_create(num_blocks, num_host_blocks, block_size,
+                                               ctypes.byref(h)))
+    return h
+
+
+def pa_bm_destroy(h) -> None:
+    load().pa_bm_destroy(h)
+
+
+def pa_bm_add_sequence(h, seq: int) -> None:
+    _check("pa_bm_add_sequence", load().pa_bm_add_sequence(h, seq))
+
+
+def pa_bm_fork(h, parent: int, child: int) -> None:
+    _check("pa_bm_fork", load().pa_bm_fork(h, parent, child))
+
+
+def pa_bm_share(h, src: int, dst: int, logical_blocks) -> None:
+    np = _np()
+    idx = np.ascontiguousarray(np.asarray(logical_blocks, dtype=np.int32).reshape(-1))
+    _check("pa_bm_share", load().pa_bm_share(h, src, dst, idx.ctypes.data if idx.size else None,
+                                             idx.size))
+
+
+def pa_bm_free_sequence(h, seq: int) -> None:
+    _check("pa_bm_free_sequence", load().pa_bm_free_sequence(h, seq))
+
+
+def pa_bm_append_slots(h, seq: int, count: int):
+    """int64 numpy array of the count reserved slots."""
+    np = _np()
+    slots = np.empty(max(count, 0), dtype=np.int64)
+    _check("pa_bm_append_slots", load().pa_bm_append_slots(
+        h, seq, count, slots.ctypes.data if slots.size else None))
+    return slots
+
+
+def pa_bm_append_batch(h, seqs, counts):
+    """(slot_mapping int64 of the served sequences' slots, num_done, status)."""
+    np = _np()
+    s, sp = _i64s(seqs)
+    c = np.ascontiguousarray(np.asarray(counts, dtype=np.int32).reshape(-1))
+    _need(c.size == s.size, "one count per sequence")
+    out = np.empty(int(c.astype(np.int64).sum()), dtype=np.int64)
+    done = ctypes.c_int32(0)
+    st = load().pa_bm_append_batch(h, sp, c.ctypes.data if c.size else None, s.size,
+                                   out.ctypes.data if out.size else None, ctypes.byref(done))
+    return out[:int(c[:done.value].astype(np.int64).sum())], done.value, st
+
+
+def pa_bm_swap_out(h, seqs) -> None:
+    s, sp = _i64s(seqs)
+    _check("pa_bm_swap_out", load().pa_bm_swap_out(h, sp, s.size))
+
+
+def pa_bm_swap_in(h, seqs) -> None:
+    s, sp = _i64s(seqs)
+    _check("pa_bm_swap_in", load().pa_bm_swap_in(h, sp, s.size))
+
+
+def pa_bm_pending_moves(h):
+    np = _np()
+    c = np.zeros(3, dtype=np.int64)
+    _check("pa_bm_pending_moves", load().pa_bm_pending_moves(h, c.ctypes.data))
+    return tuple(int(x) for x in c)
+
+
+def pa_bm_take_moves(h):
+    """(copies, swap_out, swap_in): int32 numpy arrays [n, 2] of (src, dst)."""
+    np = _np()
+    bufs = [np.empty((n, 2), dtype=np.int32) for n in pa_bm_pending_moves(h)]
+    ptrs = [b.ctypes.data if b.size else None for b in bufs]
+    _check("pa_bm_take_moves", load().pa_bm_take_moves(h, *ptrs))
+    return tuple(bufs)
+
+
+def pa_bm_num_tokens(h, seq: int) -> int:
+    n = ctypes.c_int64()
+    _check("pa_bm_num_tokens", load().pa_bm_num_tokens(h, seq, ctypes.byref(n)))
+    return n.value
+
+
+def pa_bm_is_swapped(h, seq: int) -> bool:
+    v = ctypes.c_int32()
+    _check("pa_bm_is_swapped", load().pa_bm_is_swapped(h, seq, ctypes.byref(v)))
+    return bool(v.value)
+
+
+def pa_bm_block_table(h, seq: int):
+    np = _np()
+    n = ctypes.c_int32()
+    load().pa_bm_block_table(h, seq, None, 0, ctypes.byref(n))
+    t = np.empty(n.value, dtype=np.int32)
+    _check("pa_bm_block_table", load().pa_bm_block_table(
+        h, seq, t.ctypes.data if t.size else None, t.size, ctypes.byref(n)))
+    return t
+
+
+def pa_bm_num_free(h, host: bool = False) -> int:
+    n = load().pa_bm_num_free(h, 1 if host else 0)
+    if n < 0:
+        raise PagedAttentionError("pa_bm_num_free", int(n))
+    return int(n)
+
+
+def pa_bm_build_batch(h, seqs, max_blocks_per_seq: int):
+    """(block_tables int32 [S, MB], context_lens int32 [S], shared_prefix_blocks int32 [S])."""
+    np = _np()
+    s, sp = _i64s(seqs)
+    tables = np.empty((s.size, max_blocks_per_seq), dtype=np.int32)
+    lens = np.empty(s.size, dtype=np.int32)
+    shared = np.empty(s.size, dtype=np.int32)
+    _check("pa_bm_build_batch", load().pa_bm_build_batch(
+        h, sp, s.size, max_blocks_per_seq, tables.ctypes.data, lens.ctypes.data,
+        shared.ctypes.data))
+    return tables, lens, shared
+
+
+def pa_bm_check(h) -> None:
+    _check("pa_bm_check", load().pa_bm_check(h))
+
+
+class BlockManager:
+    """The native block manager as an object (the pa_bm_* calls on one handle)."""
+
+    def __init__(self, num_blocks: int, block_size: int = 16, num_host_blocks: int = 0):
+        self.num_blocks = num_blocks
+        self.num_host_blocks = num_host_blocks
+        self.block_size = block_size
+        self._h = pa_bm_create(num_blocks, num_host_blocks, block_size)
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h and _lib is not None:
+            _lib.pa_bm_destroy(h)
+
+    def add_sequence(self, seq): pa_bm_add_sequence(self._h, seq)
+    def fork(self, parent, child): pa_bm_fork(self._h, parent, child)
+    def share(self, src, dst, logical_blocks): pa_bm_share(self._h, src, dst, logical_blocks)
+    def free_sequence(self, seq): pa_bm_free_sequence(self._h, seq)
+    def append_slots(self, seq, count): return pa_bm_append_slots(self._h, seq, count)
+    def append_batch(self, seqs, counts): return pa_bm_append_batch(self._h, seqs, counts)
+    def swap_out(self, seqs): pa_bm_swap_out(self._h, seqs)
+    def swap_in(self, seqs): pa_bm_swap_in(self._h, seqs)
+    def pending_moves(self): return pa_bm_pending_moves(self._h)
+    def take_moves(self): return pa_bm_take_moves(self._h)
+    def num_tokens(self, seq): return pa_bm_num_tokens(self._h, seq)
+    def is_swapped(self, seq): return pa_bm_is_swapped(self._h, seq)
+    def block_table(self, seq): return pa_bm_block_table(self._h, seq)
+    def num_free(self, host=False): return pa_bm_num_free(self._h, host)
+    def check_invariants(self): pa_bm_check(self._h)
+
+    def build_batch(self, seqs, max_blocks_per_seq):
+        return pa_bm_build_batch(self._h, seqs, max_blocks_per_seq)
+
+    def shared_prefix_blocks(self, seq):
+        n = max(1, len(self.block_table(seq)))
+        return int(self.build_batch([seq], n)[2][0])

@@ -122,3 +122,58 @@ def test_prefill_validation(lib):
     assert call(mql=-1) == PA_ERR_SHAPE
     assert call(nb=0) == PA_ERR_SHAPE
     assert call(S=0, out=None) == PA_OK
+
+
+def test_copy_blocks_validation(lib):
+    f = lib.pa_copy_blocks
+    assert f(None, P, P, 4, 8, 128, 16, 64, BF16, None) == PA_ERR_NULL
+    assert f(P, P, None, 4, 8, 128, 16, 64, BF16, None) == PA_ERR_NULL
+    assert f(P, P, P, -1, 8, 128, 16, 64, BF16, None) == PA_ERR_SHAPE
+    assert f(P, P, P, 4, 0, 128, 16, 64, BF16, None) == PA_ERR_SHAPE
+    assert f(P, P, P, 4, 8, 96, 16, 64, BF16, None) == PA_ERR_UNSUPPORTED
+    assert f(P, P, P, 4, 8, 128, 16, 64, 3, None) == PA_ERR_UNSUPPORTED
+    assert f(P, P, None, 0, 8, 128, 16, 64, BF16, None) == PA_OK   # nothing to copy
+
+
+def test_swap_blocks_checks_every_id_before_copying(lib):
+    import numpy as np
+    f = lib.pa_swap_blocks
+    good = np.array([[0, 1], [3, 2]], dtype=np.int32)
+    for bad in ([[0, 1], [4, 2]], [[0, 1], [3, 9]], [[-1, 0]], [[0, -2]]):
+        m = np.array(bad, dtype=np.int32)
+        assert f(P, P, P, P, m.ctypes.data, len(m), 4, 8, 2, 64, 16, F32, None) == PA_ERR_SHAPE
+    assert f(P, P, None, P, good.ctypes.data, 2, 4, 8, 2, 64, 16, F32, None) == PA_ERR_NULL
+    assert f(P, P, P, P, None, 2, 4, 8, 2, 64, 16, F32, None) == PA_ERR_NULL
+    assert f(P, P, P, P, good.ctypes.data, 2, 4, 8, 2, 64, 32, F32, None) == PA_ERR_UNSUPPORTED
+    assert f(P, P, P, P, None, 0, 4, 8, 2, 64, 16, F32, None) == PA_OK
+
+
+def test_block_manager_rejects_bad_arguments(lib):
+    import ctypes
+    h = ctypes.c_void_p()
+    assert lib.pa_bm_create(16, 0, 8, ctypes.byref(h)) == PA_ERR_UNSUPPORTED and not h.value
+    assert lib.pa_bm_create(0, 0, 16, ctypes.byref(h)) == PA_ERR_SHAPE
+    assert lib.pa_bm_create(16, -1, 16, ctypes.byref(h)) == PA_ERR_SHAPE
+    assert lib.pa_bm_create(16, 0, 16, None) == PA_ERR_NULL
+    for fn, args in (("pa_bm_add_sequence", (0,)), ("pa_bm_fork", (0, 1)),
+                     ("pa_bm_free_sequence", (0,)), ("pa_bm_check", ())):
+        assert getattr(lib, fn)(None, *args) == PA_ERR_NULL
+    assert lib.pa_bm_num_free(None, 0) == PA_ERR_NULL
+    assert lib.pa_bm_create(16, 4, 16, ctypes.byref(h)) == PA_OK and h.value
+    try:
+        assert lib.pa_bm_add_sequence(h, 3) == PA_OK
+        assert lib.pa_bm_add_sequence(h, 3) == -7                 # duplicate id
+        assert lib.pa_bm_append_slots(h, 3, 5, None) == PA_ERR_NULL
+        assert lib.pa_bm_append_slots(h, 3, -1, None) == PA_ERR_SHAPE
+        assert lib.pa_bm_append_slots(h, 3, 0, None) == PA_OK
+        n = ctypes.c_int32()
+        assert lib.pa_bm_share(h, 3, 4, None, 1) == PA_ERR_NULL
+        assert lib.pa_bm_block_table(h, 9, None, 0, ctypes.byref(n)) == -7
+        assert lib.pa_bm_check(h) == PA_OK
+    finally:
+        lib.pa_bm_destroy(h)
+
+
+def test_status_strings_cover_block_manager_codes(lib):
+    for code in range(-10, 1):
+        assert lib.pa_status_string(code) != b"unknown status"
