@@ -42,33 +42,49 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "paged-attn decode KV GB/s (% of HBM peak) + tokens/s at Llama-2-13B shape"
-COUNTERS = os.path.join(ROOT, "profiles", "decode_llama13b_counters.json")
-# sources the measured decode kernel is compiled from
-DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_453_amd", "csrc", f)
-               for f in ("decode_valu.h", "decode_valu_bf16.hip", "pa_device.h")]
+_CSRC = os.path.join(ROOT, "paged_kv_cache_453_amd", "csrc")
+# kernels whose HBM traffic comes from committed counter runs: the summary file,
+# the kernel name prefix in the rocprofv3 CSVs, the sources the kernel is built
+# from, and the bench command the counter runs profiled
+COUNTED = {
+    "decode": {
+        "json": os.path.join(ROOT, "profiles", "decode_llama13b_counters.json"),
+        "kernel": "void pa::decode_valu_kernel<unsigned short, 128, 1, false>",
+        "sources": [os.path.join(_CSRC, f)
+                    for f in ("decode_valu.h", "decode_valu_bf16.hip", "pa_device.h")],
+        "bench": "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+        "dir": "pmc", "out": "bench"},
+    "copy": {
+        "json": os.path.join(ROOT, "profiles", "copy_blocks_13b_counters.json"),
+        "kernel": "void pa::move_blocks_kernel<unsigned int __vector(4), pa::DeviceMapping>",
+        "sources": [os.path.join(_CSRC, f) for f in ("copy_blocks.hip", "pa_device.h")],
+        "bench": "python3 bench.py --workload block_moves --steps 3 --warmup 1 "
+                 "--no-cpu-baseline",
+        "dir": "pmc_bm", "out": "bm"},
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_digest() -> str:
+def source_digest(kind: str) -> str:
     h = hashlib.sha256()
-    for path in DECODE_SRCS:
+    for path in COUNTED[kind]["sources"]:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(per_launch_algo_bytes: float):
-    """HBM bytes per decode launch from committed rocprofv3 counter runs, or None
-    when they are missing or were taken on a different decode kernel source."""
+def measured_traffic(kind: str):
+    """HBM bytes per launch of the counted kernel from committed rocprofv3 counter
+    runs, or None when they are missing or were taken on a different source."""
     try:
-        with open(COUNTERS) as f:
+        with open(COUNTED[kind]["json"]) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
-    if c.get("decode_source_sha256_16") != source_digest():
+    if c.get("source_sha256_16") != source_digest(kind):
         return None
     return c.get("hbm_bytes_per_launch")
 
@@ -131,43 +147,45 @@ def _counter_rows(path: str, kernel_prefix: str):
                 if r["Kernel_Name"].startswith(kernel_prefix)]
 
 
-def digest_counters(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv: str,
-                    copy_bytes: int = 1 << 30) -> int:
-    """Turn four rocprofv3 --pmc runs into HBM bytes per decode launch.
+def digest_counters(kind: str, fetch_csv: str, write_csv: str, copy_fetch_csv: str,
+                    copy_write_csv: str, copy_bytes: int = 1 << 30) -> int:
+    """Turn four rocprofv3 --pmc runs into HBM bytes per launch of a kernel.
 
     FETCH_SIZE and WRITE_SIZE are read in KiB per dispatch.  Each is scaled by
     what the same counter reads for a plain copy of copy_bytes (which reads and
     writes exactly copy_bytes), so the result is in true bytes whatever share of
     the memory channels the counter sees.  Writes the committed summary that
-    bench.py reports as roofline.traffic while the decode kernel sources are
+    bench.py reports as roofline.traffic while the kernel's sources are
     unchanged.
     """
     import statistics
-    dec = "void pa::decode_valu_kernel<unsigned short, 128, 1, false>"
+    spec = COUNTED[kind]
+    k = spec["kernel"]
     copy = "__amd_rocclr_copyBuffer"
-    f_dec = statistics.mean(_counter_rows(fetch_csv, dec))
-    w_dec = statistics.mean(_counter_rows(write_csv, dec))
+    f_k = statistics.mean(_counter_rows(fetch_csv, k))
+    w_k = statistics.mean(_counter_rows(write_csv, k))
     f_copy = statistics.mean(_counter_rows(copy_fetch_csv, copy))
     w_copy = statistics.mean(_counter_rows(copy_write_csv, copy))
     f_scale = copy_bytes / (f_copy * 1024)
     w_scale = copy_bytes / (w_copy * 1024)
-    hbm = f_dec * 1024 * f_scale + w_dec * 1024 * w_scale
-    out = {"kernel": dec, "decode_source_sha256_16": source_digest(),
-           "fetch_kib_per_launch": round(f_dec, 1), "write_kib_per_launch": round(w_dec, 1),
+    hbm = f_k * 1024 * f_scale + w_k * 1024 * w_scale
+    d, o = spec["dir"], spec["out"]
+    out = {"kernel": k, "source_sha256_16": source_digest(kind),
+           "fetch_kib_per_launch": round(f_k, 1), "write_kib_per_launch": round(w_k, 1),
            "copy_bytes": copy_bytes, "copy_fetch_kib": round(f_copy, 1),
            "copy_write_kib": round(w_copy, 1), "fetch_scale": round(f_scale, 4),
            "write_scale": round(w_scale, 4), "hbm_bytes_per_launch": int(round(hbm)),
            "commands": [
-               "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o bench -- "
-               "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
-               "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o bench -- "
-               "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+               f"rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/{d}_fetch -o {o} -- "
+               + spec["bench"],
+               f"rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/{d}_write -o {o} -- "
+               + spec["bench"],
                "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_copy_fetch -o copy -- "
                "python3 bench.py --copy-calibration",
                "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_copy_write -o copy -- "
                "python3 bench.py --copy-calibration"]}
-    os.makedirs(os.path.dirname(COUNTERS), exist_ok=True)
-    with open(COUNTERS, "w") as f:
+    os.makedirs(os.path.dirname(spec["json"]), exist_ok=True)
+    with open(spec["json"], "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out), flush=True)
@@ -354,13 +372,14 @@ def bench_block_moves(args, torch, dev, lib, timer) -> int:
                                "(65536 blocks x 40 kv heads x 16 x 128 bf16, 10 GiB each)",
                    "pairs": pairs_n, "block_bytes_per_pool": block_bytes, "seed": 453},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "copy_blocks_kernel<u32x4>",
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("copy"),
+                     "kernel": "move_blocks_kernel<u32x4, DeviceMapping>",
                      "algorithmic_bytes_per_launch": int(algo)},
         "swap_blocks_256": swaps,
-        "swap_note": "pa_swap_blocks between the device pools and pinned host pools, K and V, "
-                     "GB/s over PCIe; scattered = 256 random block ids (one copy per block "
-                     "and pool), one_run = 256 consecutive ids merged into one copy per pool",
+        "swap_note": "pa_swap_blocks between the device pools and pinned host pools, K and V "
+                     "(2 x 256 x 160 KiB), GB/s over PCIe, one kernel launch per call; "
+                     "scattered = 256 random block ids, one_run = 256 consecutive ids",
         "block_manager_host_us_per_step": round(host_us, 1),
         "block_manager_note": "append_batch (1 token x 256 sequences) + take_moves + "
                               "build_batch (256 x 320 table) through the C ABI from Python",
@@ -383,10 +402,11 @@ def main(argv=None):
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--digest-counters", nargs=4, metavar="CSV",
-                    help="write the committed HBM-traffic summary from four rocprofv3 "
-                         "counter_collection.csv files: decode FETCH_SIZE, decode WRITE_SIZE, "
-                         "copy FETCH_SIZE, copy WRITE_SIZE (no GPU needed)")
+    ap.add_argument("--digest-counters", nargs=5, metavar=("KIND", "CSV", "CSV", "CSV", "CSV"),
+                    help="write the committed HBM-traffic summary of KIND (decode or copy) "
+                         "from four rocprofv3 counter_collection.csv files: the kernel's "
+                         "FETCH_SIZE and WRITE_SIZE runs, then the plain copy's FETCH_SIZE "
+                         "and WRITE_SIZE runs (no GPU needed)")
     args = ap.parse_args(argv)
     if args.digest_counters:
         return digest_counters(*args.digest_counters)
@@ -481,7 +501,7 @@ def main(argv=None):
                   f"decode_valu_kernel<bf16,{w.head_dim},{group}>")
     roofline = {"bound": "hbm", "achieved": round(decode_gbs, 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(decode_gbs / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(kv) if args.workload == "llama13b" else None,
+                "traffic": measured_traffic("decode") if args.workload == "llama13b" else None,
                 "kernel": dec_kernel, "algorithmic_bytes_per_launch": int(kv)}
 
     if w.prefill is not None:

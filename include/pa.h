@@ -205,18 +205,22 @@ int pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* block_mapp
  * 5.1, swap space).
  *
  * For each pair (src, dst) copies block src of src_key / src_value onto block
- * dst of dst_key / dst_value, bit for bit, with the HIP runtime's copy engines
- * (hipMemcpyAsync, direction from the pointers).  Runs of pairs whose sources
- * and destinations both advance by one are merged into one copy.
+ * dst of dst_key / dst_value, bit for bit.  When all four pools can be reached
+ * by a kernel on the current device -- its own memory, or pinned host memory
+ * (hipHostMalloc) that HIP maps at the same address -- one launch per 256 pairs
+ * moves them (the pairs travel in the kernel arguments).  Otherwise (pageable
+ * host memory, another device) the runtime copies them (hipMemcpyAsync, the
+ * direction from the pointers), one copy per run of pairs whose sources and
+ * destinations both advance by one, per pool.
  *
  *  src_key, src_value  [src_num_blocks, num_kv_heads, block_size, head_dim]
  *  dst_key, dst_value  [dst_num_blocks, num_kv_heads, block_size, head_dim]
  *  block_mapping       HOST int32 [num_pairs][2]; every id must be in range
  *                      (else PA_ERR_SHAPE and nothing is copied).
- * Host pools should be pinned (hipHostMalloc): copies from or to pageable
- * memory are not asynchronous.  The pairs must be independent, as for
- * pa_copy_blocks.  A failed copy returns PA_ERR_LAUNCH; copies enqueued
- * before it stay enqueued.
+ * The pools must really hold the stated number of blocks.  Copies from or to
+ * pageable memory are not asynchronous.  The pairs must be independent, as
+ * for pa_copy_blocks.  A failed launch or copy returns PA_ERR_LAUNCH; moves
+ * enqueued before it stay enqueued.
  */
 int pa_swap_blocks(const void* src_key, const void* src_value, void* dst_key, void* dst_value,
                    const int32_t* block_mapping, int64_t num_pairs, int64_t src_num_blocks,

@@ -223,15 +223,47 @@ int pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* block_mapp
     return PA_ERR_UNSUPPORTED;
   if (num_pairs < 0 || num_kv_heads < 1 || num_blocks < 1) return PA_ERR_SHAPE;
   if (num_pairs == 0) return PA_OK;
-  pa::CopyArgs a;
-  a.key_cache = key_cache;
-  a.value_cache = value_cache;
-  a.block_mapping = block_mapping;
-  a.num_pairs = num_pairs;
-  a.block_bytes = (int64_t)num_kv_heads * kBlockSize * head_dim * elem_bytes(dtype);
-  a.num_blocks = num_blocks;
-  return status_of(pa::launch_copy_blocks(a, stream));
+  pa::BlockPools p;
+  p.src_k = p.dst_k = key_cache;
+  p.src_v = p.dst_v = value_cache;
+  p.block_bytes = (int64_t)num_kv_heads * kBlockSize * head_dim * elem_bytes(dtype);
+  p.src_blocks = p.dst_blocks = num_blocks;
+  p.num_pairs = num_pairs;
+  return status_of(pa::launch_copy_blocks(p, block_mapping, stream));
 }
+
+}  // extern "C"
+
+namespace {
+
+// Whether a kernel on the current device may read and write [p, p + bytes):
+// device memory of this device, or pinned host memory that HIP maps at the
+// same address for the device.  Anything else (pageable host memory, another
+// device, memory HIP does not know) is left to the runtime's copies.
+bool kernel_reachable(const void* p, int64_t bytes) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  const char* ends[2] = {static_cast<const char*>(p), static_cast<const char*>(p) + bytes - 1};
+  for (const char* q : ends) {
+    hipPointerAttribute_t at;
+    if (hipPointerGetAttributes(&at, q) != hipSuccess) {
+      (void)hipGetLastError();   // an unknown pointer is an answer here, not an error
+      return false;
+    }
+    if (at.type == hipMemoryTypeDevice) {
+      if (at.device != dev) return false;
+    } else if (at.type == hipMemoryTypeHost) {
+      if (at.devicePointer != q) return false;
+    } else {
+      return false;
+    }
+  }
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
 
 int pa_swap_blocks(const void* src_key, const void* src_value, void* dst_key, void* dst_value,
                    const int32_t* block_mapping, int64_t num_pairs, int64_t src_num_blocks,
@@ -247,7 +279,22 @@ int pa_swap_blocks(const void* src_key, const void* src_value, void* dst_key, vo
     const int32_t s = block_mapping[2 * i], d = block_mapping[2 * i + 1];
     if (s < 0 || s >= src_num_blocks || d < 0 || d >= dst_num_blocks) return PA_ERR_SHAPE;
   }
-  const size_t bb = (size_t)num_kv_heads * kBlockSize * head_dim * elem_bytes(dtype);
+  if (num_pairs == 0) return PA_OK;
+  const int64_t bb = (int64_t)num_kv_heads * kBlockSize * head_dim * elem_bytes(dtype);
+  const int64_t src_bytes = src_num_blocks * bb, dst_bytes = dst_num_blocks * bb;
+  if (kernel_reachable(src_key, src_bytes) && kernel_reachable(src_value, src_bytes) &&
+      kernel_reachable(dst_key, dst_bytes) && kernel_reachable(dst_value, dst_bytes)) {
+    pa::BlockPools p;
+    p.src_k = src_key;
+    p.src_v = src_value;
+    p.dst_k = dst_key;
+    p.dst_v = dst_value;
+    p.block_bytes = bb;
+    p.src_blocks = src_num_blocks;
+    p.dst_blocks = dst_num_blocks;
+    p.num_pairs = num_pairs;
+    return status_of(pa::launch_swap_blocks(p, block_mapping, stream));
+  }
   const char* sk = static_cast<const char*>(src_key);
   const char* sv = static_cast<const char*>(src_value);
   char* dk = static_cast<char*>(dst_key);

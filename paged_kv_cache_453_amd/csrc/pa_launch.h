@@ -58,14 +58,20 @@ struct ReduceArgs {
   int max_context_len;
 };
 
-struct CopyArgs {
-  void* key_cache;
-  void* value_cache;
-  const int32_t* block_mapping;   // device, [num_pairs][2] = (src, dst)
-  int64_t num_pairs;
+// Pools a batch of whole-block moves reads from and writes to (K and V alike).
+struct BlockPools {
+  const void* src_k;
+  const void* src_v;
+  void* dst_k;
+  void* dst_v;
   int64_t block_bytes;            // bytes of one physical block of one pool
-  int64_t num_blocks;
+  int64_t src_blocks;
+  int64_t dst_blocks;
+  int64_t num_pairs;
 };
+
+// Pairs one swap launch carries in its kernel arguments.
+constexpr int kSwapPairsPerLaunch = 256;
 
 hipError_t launch_reshape_and_cache(const ScatterArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t stream);
@@ -73,7 +79,10 @@ hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_valu_bf16(const DecodeArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_decode_valu_f32(const DecodeArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_splitk_reduce(const ReduceArgs& a, int head_dim, bool bf16, hipStream_t stream);
-hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
+hipError_t launch_copy_blocks(const BlockPools& pools, const int32_t* block_mapping,
+                              hipStream_t stream);
+hipError_t launch_swap_blocks(const BlockPools& pools, const int32_t* host_pairs,
+                              hipStream_t stream);
 hipError_t launch_prefill_mfma(const DecodeArgs& a, int head_dim, hipStream_t stream);
 
 }  // namespace pa

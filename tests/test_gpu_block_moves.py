@@ -107,18 +107,25 @@ def test_copy_blocks_13b_pool_1024_pairs(gpu):
     assert np.array_equal(vc[oth].cpu().numpy(), keep_v)
 
 
-@pytest.mark.parametrize("dtype,hkv,d", [("bf16", 8, 128), ("f32", 2, 64)])
-def test_swap_blocks_out_and_back(gpu, dtype, hkv, d):
+def host_pool(arr, dtype, pinned):
+    """A host tensor holding a copy of arr: pinned (kernel path) or pageable
+    (runtime-copy path)."""
+    t = host_to_torch(arr.copy(), dtype, "cpu")
+    return t.pin_memory() if pinned else t
+
+
+@pytest.mark.parametrize("dtype,hkv,d,pinned", [("bf16", 8, 128, True), ("f32", 2, 64, True),
+                                                ("bf16", 8, 128, False)])
+def test_swap_blocks_out_and_back(gpu, dtype, hkv, d, pinned):
     import torch
-    say(f"swap_blocks {dtype} hkv={hkv} d={d}")
+    say(f"swap_blocks {dtype} hkv={hkv} d={d} pinned={pinned}")
     rng = np.random.default_rng(5)
     nb, nh = 128, 48
     shape, hshape = (nb, hkv, BS, d), (nh, hkv, BS, d)
     k0, v0 = random_storage(rng, shape, dtype), random_storage(rng, shape, dtype)
     hk0, hv0 = random_storage(rng, hshape, dtype), random_storage(rng, hshape, dtype)
     kc, vc = host_to_torch(k0, dtype, "cuda"), host_to_torch(v0, dtype, "cuda")
-    hk = host_to_torch(hk0, dtype, "cpu").pin_memory()
-    hv = host_to_torch(hv0, dtype, "cpu").pin_memory()
+    hk, hv = host_pool(hk0, dtype, pinned), host_pool(hv0, dtype, pinned)
     # runs that merge into one copy, single blocks, a run broken by a jump
     out_pairs = np.array([[5, 0], [6, 1], [7, 2], [40, 10], [3, 11], [90, 30], [91, 31],
                           [92, 33], [127, 47]], dtype=np.int32)
@@ -139,8 +146,37 @@ def test_swap_blocks_out_and_back(gpu, dtype, hkv, d):
     kd, vd = torch.zeros_like(kc), torch.zeros_like(vc)
     gpu.pa_swap_blocks(kc, vc, kd, vd, np.array([[100, 3], [101, 4]], dtype=np.int32))
     torch.cuda.synchronize()
-    assert torch.equal(kd[3:5].view(torch.int16 if dtype == "bf16" else torch.int32),
-                       kc[100:102].view(torch.int16 if dtype == "bf16" else torch.int32))
+    iview = torch.int16 if dtype == "bf16" else torch.int32
+    assert torch.equal(kd[3:5].view(iview), kc[100:102].view(iview))
+    assert torch.equal(vd[3:5].view(iview), vc[100:102].view(iview))
+
+
+@pytest.mark.parametrize("pinned", [True, False])
+def test_swap_blocks_many_scattered_pairs(gpu, pinned):
+    """More pairs than one launch carries (256), scattered ids both ways."""
+    import torch
+    say(f"swap_blocks 600 scattered pairs pinned={pinned}")
+    rng = np.random.default_rng(9)
+    nb, nh, hkv, d = 1024, 700, 8, 128
+    k0 = random_storage(rng, (nb, hkv, BS, d), "bf16")
+    v0 = random_storage(rng, (nb, hkv, BS, d), "bf16")
+    hk0 = random_storage(rng, (nh, hkv, BS, d), "bf16")
+    hv0 = random_storage(rng, (nh, hkv, BS, d), "bf16")
+    kc, vc = host_to_torch(k0, "bf16", "cuda"), host_to_torch(v0, "bf16", "cuda")
+    hk, hv = host_pool(hk0, "bf16", pinned), host_pool(hv0, "bf16", pinned)
+    out_pairs = np.stack([rng.choice(nb, 600, replace=False), rng.choice(nh, 600, replace=False)],
+                         1).astype(np.int32)
+    gpu.pa_swap_blocks(kc, vc, hk, hv, out_pairs)
+    torch.cuda.synchronize()
+    hk1, hv1 = oracle.swap_blocks(k0, hk0, out_pairs), oracle.swap_blocks(v0, hv0, out_pairs)
+    assert np.array_equal(torch_to_storage(hk, "bf16"), hk1)
+    assert np.array_equal(torch_to_storage(hv, "bf16"), hv1)
+    in_pairs = np.stack([rng.choice(nh, 600, replace=False), rng.choice(nb, 600, replace=False)],
+                        1).astype(np.int32)
+    gpu.pa_swap_blocks(hk, hv, kc, vc, in_pairs)
+    torch.cuda.synchronize()
+    assert np.array_equal(torch_to_storage(kc, "bf16"), oracle.swap_blocks(hk1, k0, in_pairs))
+    assert np.array_equal(torch_to_storage(vc, "bf16"), oracle.swap_blocks(hv1, v0, in_pairs))
 
 
 class Steps:
