@@ -6,7 +6,8 @@ the benchmark's CPU-baseline leg, never by the product path.
 from .paged_attention import (to_f64, reshape_and_cache, gather, attend, decode,
                               decode_partials, merge_partials, prefill)
 from .block_manager import BlockManager, OutOfBlocks, copy_blocks, swap_blocks
+from . import kv_fp8
 
 __all__ = ["to_f64", "reshape_and_cache", "gather", "attend", "decode", "decode_partials",
            "merge_partials", "prefill", "BlockManager", "OutOfBlocks", "copy_blocks",
-           "swap_blocks"]
+           "swap_blocks", "kv_fp8"]
