@@ -47,7 +47,10 @@
 extern "C" {
 #endif
 
-typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+/* Element types.  PA_FP8_E4M3 names FP8 cache pools for the calls that only
+ * move whole blocks (pa_copy_blocks, pa_swap_blocks); the FP8 attention calls
+ * take uint8_t pools and a pa_dtype for their fp32 / bf16 side. */
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 } pa_dtype;
 
 typedef enum {
   PA_OK = 0,
@@ -178,6 +181,52 @@ int pa_prefill_chunk(void* out, const void* query, const void* key_cache, const 
                      pa_dtype dtype, hipStream_t stream);
 
 /*
+ * FP8 KV cache.  The cache may store K and V as 8-bit floats (OCP E4M3: 1 sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits, no infinities, largest
+ * magnitude 448), one byte per element, which halves the bytes decode streams
+ * -- the resource decode is bound by (xdnf.cn article, section 六.5).  This
+ * recasts the pages' suggestion of choosing a lower precision, fp8 among them,
+ * for attention (intelliparadigm.com article, section 7.1) as a storage
+ * format.  Each pool has one scale: a code c stands for value(c) * scale.
+ * Pools are [num_blocks, num_kv_heads, block_size, head_dim] bytes, 4-byte
+ * aligned; otherwise every convention above holds.
+ */
+
+/*
+ * pa_reshape_and_cache_fp8 -- quantise each new token's K and V into its slot.
+ *
+ * As pa_reshape_and_cache, but key / value hold src_dtype values (fp32 or
+ * bf16) and the caches receive, per element x, the code nearest to
+ * fp32(x * fp32(1 / scale)) -- ties to the even code, magnitudes above 448
+ * saturated to 448, NaN stored as 0x7F -- with k_scale for K and v_scale for
+ * V.  The scales must be positive and finite (else PA_ERR_SHAPE).
+ */
+int pa_reshape_and_cache_fp8(const void* key, const void* value, uint8_t* key_cache,
+                             uint8_t* value_cache, const int64_t* slot_mapping,
+                             int64_t num_tokens, int64_t key_stride, int64_t value_stride,
+                             int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                             pa_dtype src_dtype, float k_scale, float v_scale,
+                             hipStream_t stream);
+
+/*
+ * pa_decode_fp8 -- pa_decode over FP8 caches: softmax(scale * q K^T) V with K
+ * and V the values the codes stand for (code value times k_scale / v_scale).
+ * query and out are dtype (fp32 or bf16); accumulation is fp32.  Split-K
+ * partials use the same workspace layout, merged by pa_decode_splitk_reduce.
+ * Supported groups: any group up to 16 for a bf16 query with head_dim 128
+ * (grouped-query heads run on the matrix cores), else at most 4 query heads
+ * per kv head (PA_ERR_UNSUPPORTED otherwise).  The scales must be positive
+ * and finite (else PA_ERR_SHAPE).
+ */
+int pa_decode_fp8(void* out, const void* query, const uint8_t* key_cache,
+                  const uint8_t* value_cache, const int32_t* block_tables,
+                  const int32_t* context_lens, const int32_t* shared_prefix_blocks,
+                  int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                  int max_blocks_per_seq, int64_t num_blocks, int max_context_len, float scale,
+                  float k_scale, float v_scale, int partition_size, void* workspace,
+                  size_t workspace_bytes, pa_dtype dtype, hipStream_t stream);
+
+/*
  * pa_copy_blocks -- copy whole physical blocks inside the K and V pools.
  *
  * For each pair (src, dst) = (block_mapping[2i], block_mapping[2i+1]) copies
@@ -188,7 +237,8 @@ int pa_prefill_chunk(void* out, const void* query, const void* key_cache, const 
  * pa_bm_take_moves() hands out as copies are made for this call.
  *
  *  key_cache,
- *  value_cache    [num_blocks, num_kv_heads, block_size, head_dim], dtype; updated in place.
+ *  value_cache    [num_blocks, num_kv_heads, block_size, head_dim], dtype (fp32, bf16 or
+ *                 PA_FP8_E4M3 codes); updated in place.
  *  block_mapping  device int32 [num_pairs][2].
  * The pairs must be independent: destinations distinct and none of them a
  * source of the call (they run all at once).  A pair naming a block outside

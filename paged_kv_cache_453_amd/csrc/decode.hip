@@ -85,6 +85,21 @@ hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool bf16, hipStream
               : launch_decode_valu_f32(a, head_dim, stream);
 }
 
+// FP8 caches: grouped-query heads (bf16 query, head_dim 128, group >= 4) on the
+// matrix cores, the rest on the vector ALUs, whose widened accumulators leave
+// room for at most kFp8ValuMaxGroup query heads per kv head.
+bool decode_fp8_supported(int group, int head_dim, bool bf16_query) {
+  return (bf16_query && head_dim == 128 && group >= kMfmaMinGroup) || group <= kFp8ValuMaxGroup;
+}
+
+hipError_t launch_decode_fp8(const DecodeArgs& a, int head_dim, bool bf16_query,
+                             hipStream_t stream) {
+  if (a.num_items == 0) return hipSuccess;
+  if (bf16_query && head_dim == 128 && a.group >= kMfmaMinGroup)
+    return launch_decode_gqa_mfma_fp8(a, stream);
+  return launch_decode_valu_fp8(a, head_dim, bf16_query, stream);
+}
+
 hipError_t launch_splitk_reduce(const ReduceArgs& a, int head_dim, bool bf16, hipStream_t stream) {
   if (a.num_seqs == 0) return hipSuccess;
   const int64_t rows = (int64_t)a.num_seqs * a.num_heads;

@@ -45,6 +45,12 @@
 // Scores are kept in base 2 (scale * log2(e)); probabilities are rounded to
 // bf16 for the p.V product and the running sum adds the rounded values, so
 // numerator and denominator use the same weights.
+//
+// FP8 (E4M3) caches: each lane loads the same token rows and columns as for
+// bf16, 8 bytes instead of 16, and widens the codes to bf16 in registers when
+// it consumes the slab (exact: an E4M3 value has at most 4 significant bits);
+// from there the products are the bf16 ones.  The per-tensor K scale is folded
+// into the score scale, the V scale into the final normalisation.
 #include <math.h>
 
 #include <type_traits>
@@ -80,30 +86,64 @@ __device__ __forceinline__ f32x4 mfma_pv(const u32x2& v, const u32x2& p, const f
 constexpr int kBufferWord3 = 0x00020000;   // raw 32-bit buffer, no format conversion
 constexpr int kStreamPolicy = 2;           // cache-policy bits: nontemporal
 constexpr int kSharedPolicy = 0;           // cache-policy bits: default
-constexpr int kSlabBytes = kBlock * kD * 2;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const bf16_t* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(base), 0, bytes, kBufferWord3);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferWord3);
 }
 template <int POLICY>
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t rsrc, int byte_off) {
   return __builtin_amdgcn_raw_buffer_load_b128(rsrc, byte_off, 0, POLICY);
 }
+template <int POLICY>
+__device__ __forceinline__ u32x2 load8(__amdgpu_buffer_rsrc_t rsrc, int byte_off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rsrc, byte_off, 0, POLICY));
+}
 
-// K and V of one (block, kv head) slab as this lane loads them: token 4g+i,
-// columns 8r .. 8r+7 (16 lanes per contiguous 256-byte row).
+// K and V of one (block, kv head) slab as this lane holds them: token 4g+i,
+// columns 8r .. 8r+7 (16 lanes per contiguous row), as bf16 ...
 struct MfmaSlab {
   u32x4 k[4];
   u32x4 v[4];
 };
+// ... and as loaded from an FP8 cache (8 codes per token row and lane).
+struct MfmaSlabFp8 {
+  u32x2 k[4];
+  u32x2 v[4];
+};
 
-template <int POLICY>
-__device__ __forceinline__ void load_mfma_slab(MfmaSlab& s, __amdgpu_buffer_rsrc_t kr,
+template <typename KV>
+using SlabOf = typename std::conditional<std::is_same<KV, fp8_t>::value, MfmaSlabFp8, MfmaSlab>::type;
+
+template <typename KV, int POLICY>
+__device__ __forceinline__ void load_mfma_slab(SlabOf<KV>& s, __amdgpu_buffer_rsrc_t kr,
                                                __amdgpu_buffer_rsrc_t vr, int r, int g) {
+  constexpr int EB = (int)sizeof(KV);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) s.k[i] = load16<POLICY>(kr, 2 * ((4 * g + i) * kD + 8 * r));
+  for (int i = 0; i < 4; ++i) {
+    const int off = EB * ((4 * g + i) * kD + 8 * r);
+    if constexpr (EB == 1) s.k[i] = load8<POLICY>(kr, off);
+    else s.k[i] = load16<POLICY>(kr, off);
+  }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) s.v[i] = load16<POLICY>(vr, 2 * ((4 * g + i) * kD + 8 * r));
+  for (int i = 0; i < 4; ++i) {
+    const int off = EB * ((4 * g + i) * kD + 8 * r);
+    if constexpr (EB == 1) s.v[i] = load8<POLICY>(vr, off);
+    else s.v[i] = load16<POLICY>(vr, off);
+  }
+}
+
+// The slab as bf16: the loaded registers themselves, or the FP8 codes widened.
+__device__ __forceinline__ MfmaSlab& as_bf16_slab(MfmaSlab& s) { return s; }
+__device__ __forceinline__ MfmaSlab as_bf16_slab(const MfmaSlabFp8& s) {
+  MfmaSlab b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t k0 = s.k[i].x, k1 = s.k[i].y, v0 = s.v[i].x, v1 = s.v[i].y;
+    const u32x2 klo = fp8x4_to_bf16x4(k0), khi = fp8x4_to_bf16x4(k1);
+    const u32x2 vlo = fp8x4_to_bf16x4(v0), vhi = fp8x4_to_bf16x4(v1);
+    b.k[i] = u32x4{klo.x, klo.y, khi.x, khi.y};
+    b.v[i] = u32x4{vlo.x, vlo.y, vhi.x, vhi.y};
+  }
+  return b;
 }
 
 // Per-wave LDS tile that turns K around: 16 token rows of 256 bytes, padded.
@@ -206,9 +246,10 @@ __device__ __forceinline__ void consume_mfma_slab(MfmaSlab& sl, const u32x4 (&qb
 
 }  // namespace
 
-// HINT: the caller passed shared_prefix_blocks, so batches of shared blocks
-// take the caching load path; without it only the streaming path is compiled.
-template <bool HINT>
+// KV: the cache element type (bf16, or fp8 codes).  HINT: the caller passed
+// shared_prefix_blocks, so batches of shared blocks take the caching load path;
+// without it only the streaming path is compiled.
+template <typename KV, bool HINT>
 __global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t sh_k[kHeadsPerWG][kKTileBytes];
   const int hgroups = (a.num_kv_heads + kHeadsPerWG - 1) / kHeadsPerWG;
@@ -272,8 +313,9 @@ __global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(DecodeArgs a) {
 #pragma unroll
   for (int t = 0; t < 8; ++t) st.o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const bf16_t* kpool = static_cast<const bf16_t*>(a.k_cache);
-  const bf16_t* vpool = static_cast<const bf16_t*>(a.v_cache);
+  const KV* kpool = static_cast<const KV*>(a.k_cache);
+  const KV* vpool = static_cast<const KV*>(a.v_cache);
+  constexpr int kSlabBytes = kBlock * kD * (int)sizeof(KV);
   const int32_t* table = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
   const int64_t head_slab = (int64_t)kBlock * kD;
   uint8_t* ktile = sh_k[kvh % kHeadsPerWG];
@@ -295,20 +337,22 @@ __global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(DecodeArgs a) {
     const int myb = lane < cnt ? table[base + lane] : 0;
     const auto run_batch = [&](auto policy) {
       constexpr int P = decltype(policy)::value;
-      const auto load_step = [&](MfmaSlab& sl, int t) {
+      const auto load_step = [&](SlabOf<KV>& sl, int t) {
         const int bid = __builtin_amdgcn_readlane(myb, min(t, cnt - 1));
         const bool in_pool = bid >= 0 && (int64_t)bid < a.num_blocks;
         bad_block |= t < cnt && !in_pool;
         const bool live = t < cnt && in_pool;
         const int64_t off = live ? ((int64_t)bid * a.num_kv_heads + kvh) * head_slab : 0;
         const int bytes = live ? kSlabBytes : 0;
-        load_mfma_slab<P>(sl, slab_rsrc(kpool + off, bytes), slab_rsrc(vpool + off, bytes), r, g);
+        load_mfma_slab<KV, P>(sl, slab_rsrc(kpool + off, bytes), slab_rsrc(vpool + off, bytes), r,
+                              g);
       };
-      const auto consume = [&](MfmaSlab& sl, int t) {
+      const auto consume = [&](SlabOf<KV>& sl, int t) {
         const int nvalid = min(kBlock, tok_end - (base + t) * kBlock);
-        consume_mfma_slab(sl, qb, a.scale_log2, r, g, nvalid, ktile, st);
+        auto&& bs = as_bf16_slab(sl);
+        consume_mfma_slab(bs, qb, a.scale_log2, r, g, nvalid, ktile, st);
       };
-      MfmaSlab sa, sb;
+      SlabOf<KV> sa, sb;
       load_step(sa, 0);
       for (int t = 0; t < cnt; t += 2) {
         load_step(sb, t + 1);
@@ -336,7 +380,8 @@ __global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(DecodeArgs a) {
   lsum += __shfl_xor(lsum, 32, 64);
   const bool poisoned = __builtin_amdgcn_readfirstlane((int)bad_block) != 0;
   if (r >= G) return;
-  const float inv = 1.f / lsum;
+  float inv = 1.f / lsum;
+  if constexpr (std::is_same<KV, fp8_t>::value) inv = a.v_scale / lsum;
   const int h = kvh * G + r;
   if (nparts <= 1) {
     bf16_t* dst = out + ((int64_t)seq * hq + h) * kD;
@@ -368,16 +413,27 @@ __global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(DecodeArgs a) {
   }
 }
 
-hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, hipStream_t stream) {
+template <typename KV>
+hipError_t launch_gqa_mfma(const DecodeArgs& a, hipStream_t stream) {
   if (a.num_items == 0) return hipSuccess;
   const int hgroups = (a.num_kv_heads + kHeadsPerWG - 1) / kHeadsPerWG;
   dim3 grid((unsigned)((int64_t)a.num_items * hgroups),
             a.partition_blocks > 0 ? a.max_partitions : 1);
   if (a.shared_prefix_blocks != nullptr)
-    hipLaunchKernelGGL(decode_gqa_mfma_kernel<true>, grid, dim3(64 * kHeadsPerWG), 0, stream, a);
+    hipLaunchKernelGGL((decode_gqa_mfma_kernel<KV, true>), grid, dim3(64 * kHeadsPerWG), 0,
+                       stream, a);
   else
-    hipLaunchKernelGGL(decode_gqa_mfma_kernel<false>, grid, dim3(64 * kHeadsPerWG), 0, stream, a);
+    hipLaunchKernelGGL((decode_gqa_mfma_kernel<KV, false>), grid, dim3(64 * kHeadsPerWG), 0,
+                       stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, hipStream_t stream) {
+  return launch_gqa_mfma<bf16_t>(a, stream);
+}
+
+hipError_t launch_decode_gqa_mfma_fp8(const DecodeArgs& a, hipStream_t stream) {
+  return launch_gqa_mfma<fp8_t>(a, stream);
 }
 
 }  // namespace pa

@@ -1,8 +1,11 @@
 // Paged-attention decode on the vector ALUs: kernel templates.
 //
-// Included by decode_valu_bf16.hip and decode_valu_f32.hip, which instantiate
-// the kernels for one element type each (they compile in parallel), and by
-// decode.hip for the element traits of the split-K merge.
+// Included by decode_valu_bf16.hip, decode_valu_f32.hip and decode_valu_fp8.hip,
+// which instantiate the kernels for one cache element type each (they compile
+// in parallel), and by decode.hip for the element traits of the split-K merge.
+// T is the query and output type (fp32 or bf16), KV the cache element type:
+// T itself, or an FP8 (E4M3) code whose value is code * scale, the per-tensor
+// scales folded into the score scale (K) and the output (V).
 //
 // What is computed: for every query row, softmax(scale * q K^T) V over the
 // tokens of its sequence, K and V being read through the sequence's block table
@@ -64,6 +67,10 @@ struct ElemTraits<bf16_t> {
   __device__ static float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
   __device__ static bf16_t from_f32(float x) { return f32_to_bf16(x); }
 };
+template <>
+struct ElemTraits<fp8_t> {   // cache codes only: never a query or output type
+  static constexpr int kPerLoad = 16;
+};
 
 // Widen the E elements held in one 16-byte register quad to fp32.
 template <typename T>
@@ -81,14 +88,23 @@ __device__ __forceinline__ void widen<bf16_t>(const u32x4& r, float* out) {
     out[2 * x + 1] = bf16_hi(r[x]);
   }
 }
+template <>
+__device__ __forceinline__ void widen<fp8_t>(const u32x4& r, float* out) {
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const uint32_t w = r[x];
+    fp8x4_to_f32(w, out + 4 * x);
+  }
+}
 
 // Partial q.k over this lane's E elements.  bf16 uses the packed bf16 dot
 // instruction on the raw bits (q kept unscaled in bf16, products exact in fp32),
-// fp32 uses fused multiply-adds on pre-scaled q.
-template <typename T>
+// fp32 uses fused multiply-adds on pre-scaled q.  FP8 keys are widened first,
+// exactly (to bf16 pairs for a bf16 query, to fp32 for an fp32 query).
+template <typename T, typename KV>
 struct QFrag;
 template <>
-struct QFrag<float> {
+struct QFrag<float, float> {
   float q[4];
   __device__ void load(const float* p, float scale_log2) {
     const u32x4 r = *reinterpret_cast<const u32x4*>(p);
@@ -108,7 +124,7 @@ struct QFrag<float> {
   __device__ static float post(float s, float) { return s; }
 };
 template <>
-struct QFrag<bf16_t> {
+struct QFrag<bf16_t, bf16_t> {
   u32x4 q;
   __device__ void load(const bf16_t* p, float) { q = *reinterpret_cast<const u32x4*>(p); }
   __device__ void zero() { q = u32x4{0u, 0u, 0u, 0u}; }
@@ -123,6 +139,60 @@ struct QFrag<bf16_t> {
     return s;
   }
   __device__ static float post(float s, float scale_log2) { return s * scale_log2; }
+};
+template <>
+struct QFrag<bf16_t, fp8_t> {
+  u32x4 q[2];   // 16 bf16 query elements, unscaled
+  __device__ void load(const bf16_t* p, float) {
+    q[0] = *reinterpret_cast<const u32x4*>(p);
+    q[1] = *reinterpret_cast<const u32x4*>(p + 8);
+  }
+  __device__ void zero() { q[0] = q[1] = u32x4{0u, 0u, 0u, 0u}; }
+  __device__ float dot(const u32x4& k) const {
+    float s = 0.f;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const uint32_t kw = k[x];
+      const u32x2 kb = fp8x4_to_bf16x4(kw);
+      const uint32_t q0 = q[x / 2][2 * (x % 2)];
+      const uint32_t q1 = q[x / 2][2 * (x % 2) + 1];
+      const uint32_t k0 = kb.x;
+      const uint32_t k1 = kb.y;
+      s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q0), as_bf16x2(k0), s, false);
+      s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q1), as_bf16x2(k1), s, false);
+    }
+    return s;
+  }
+  __device__ static float post(float s, float scale_log2) { return s * scale_log2; }
+};
+template <>
+struct QFrag<float, fp8_t> {
+  float q[16];  // 16 fp32 query elements, pre-scaled
+  __device__ void load(const float* p, float scale_log2) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const u32x4 r = *reinterpret_cast<const u32x4*>(p + 4 * x);
+#pragma unroll
+      for (int y = 0; y < 4; ++y) q[4 * x + y] = __uint_as_float(r[y]) * scale_log2;
+    }
+  }
+  __device__ void zero() {
+#pragma unroll
+    for (int x = 0; x < 16; ++x) q[x] = 0.f;
+  }
+  __device__ float dot(const u32x4& k) const {
+    float s = 0.f;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      float f[4];
+      const uint32_t kw = k[x];
+      fp8x4_to_f32(kw, f);
+#pragma unroll
+      for (int y = 0; y < 4; ++y) s = fmaf(q[4 * x + y], f[y], s);
+    }
+    return s;
+  }
+  __device__ static float post(float s, float) { return s; }
 };
 
 // One (block, kv head) slab of K and of V as this lane holds it: NLD
@@ -155,13 +225,13 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t rsrc, int byte_of
   return __builtin_amdgcn_raw_buffer_load_b128(rsrc, byte_off, 0, POLICY);
 }
 
-template <typename T, int D, int POLICY>
-__device__ __forceinline__ void load_slab(Slab<kBlock * D / (kWave * ElemTraits<T>::kPerLoad)>& s,
+template <typename KV, int D, int POLICY>
+__device__ __forceinline__ void load_slab(Slab<kBlock * D / (kWave * ElemTraits<KV>::kPerLoad)>& s,
                                           __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
                                           int lane_byte_off) {
-  constexpr int RPL = kWave / (D / ElemTraits<T>::kPerLoad);
+  constexpr int RPL = kWave / (D / ElemTraits<KV>::kPerLoad);
   constexpr int NLD = kBlock / RPL;
-  constexpr int STEP = RPL * D * (int)sizeof(T);
+  constexpr int STEP = RPL * D * (int)sizeof(KV);
 #pragma unroll
   for (int i = 0; i < NLD; ++i) s.k[i] = load16<POLICY>(kr, lane_byte_off + i * STEP);
 #pragma unroll
@@ -173,12 +243,12 @@ __device__ __forceinline__ void load_slab(Slab<kBlock * D / (kWave * ElemTraits<
 // past nvalid are skipped -- their scores never enter the max, their weights
 // are 0 and their V values are replaced by 0 before use, since they may hold
 // anything (NaN included) and 0 * NaN is NaN.
-template <typename T, int D, int GP, bool MASKED>
+template <typename T, typename KV, int D, int GP, bool MASKED>
 __device__ __forceinline__ void consume_slab(
-    const Slab<kBlock * D / (kWave * ElemTraits<T>::kPerLoad)>& sl, const QFrag<T> (&q)[GP],
+    const Slab<kBlock * D / (kWave * ElemTraits<KV>::kPerLoad)>& sl, const QFrag<T, KV> (&q)[GP],
     float scale_log2, int r, int nvalid, float (&m)[GP], float (&l)[GP],
-    float (&acc)[GP][ElemTraits<T>::kPerLoad]) {
-  constexpr int E = ElemTraits<T>::kPerLoad;
+    float (&acc)[GP][ElemTraits<KV>::kPerLoad]) {
+  constexpr int E = ElemTraits<KV>::kPerLoad;
   constexpr int LPR = D / E;
   constexpr int RPL = kWave / LPR;
   constexpr int NLD = kBlock / RPL;
@@ -189,7 +259,7 @@ __device__ __forceinline__ void consume_slab(
   for (int g = 0; g < GP; ++g)
 #pragma unroll
     for (int i = 0; i < NLD; ++i)
-      s[g][i] = QFrag<T>::post(group_sum<LPR>(q[g].dot(sl.k[i])), scale_log2);
+      s[g][i] = QFrag<T, KV>::post(group_sum<LPR>(q[g].dot(sl.k[i])), scale_log2);
 
   bool valid[NLD];
 #pragma unroll
@@ -221,7 +291,7 @@ __device__ __forceinline__ void consume_slab(
     u32x4 vr = sl.v[i];
     if (MASKED) vr = valid[i] ? vr : u32x4{0u, 0u, 0u, 0u};
     float v[E];
-    widen<T>(vr, v);
+    widen<KV>(vr, v);
 #pragma unroll
     for (int g = 0; g < GP; ++g)
 #pragma unroll
@@ -264,9 +334,9 @@ __device__ __forceinline__ bool locate_item(const DecodeArgs& a, int item, ItemI
 
 // HINT: the caller passed shared_prefix_blocks, so batches of shared blocks
 // take the caching load path; without it only the streaming path is compiled.
-template <typename T, int D, int GP, bool HINT>
+template <typename T, typename KV, int D, int GP, bool HINT>
 __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
-  constexpr int E = ElemTraits<T>::kPerLoad;   // elements per 16-byte load
+  constexpr int E = ElemTraits<KV>::kPerLoad;  // cache elements per 16-byte load
   constexpr int LPR = D / E;                   // lanes per token row
   constexpr int RPL = kWave / LPR;             // token rows per wave-wide load
   constexpr int NLD = kBlock / RPL;            // loads per block slab per lane
@@ -327,7 +397,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   }
 
   // Query fragments of the group's heads: this lane's E elements of each.
-  QFrag<T> q[GP];
+  QFrag<T, KV> q[GP];
 #pragma unroll
   for (int g = 0; g < GP; ++g) {
     if (g < G)
@@ -346,8 +416,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     for (int e = 0; e < E; ++e) acc[g][e] = 0.f;
   }
 
-  const T* kpool = static_cast<const T*>(a.k_cache);
-  const T* vpool = static_cast<const T*>(a.v_cache);
+  const KV* kpool = static_cast<const KV*>(a.k_cache);
+  const KV* vpool = static_cast<const KV*>(a.v_cache);
   const int32_t* table = a.block_tables + (int64_t)it.seq * a.max_blocks_per_seq;
   const int64_t head_slab = (int64_t)kBlock * D;
   const int lane_off = r * D + c * E;     // elements from the slab start
@@ -362,8 +432,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   // pool reads as zeros and poisons the result.  Batches never mix shared and
   // private blocks, so each batch runs with one cache policy.
   const int nb_w = (je - jb - w + NW - 1) / NW;
-  const int slab_bytes = kBlock * D * (int)sizeof(T);
-  const int lane_byte_off = lane_off * (int)sizeof(T);
+  const int slab_bytes = kBlock * D * (int)sizeof(KV);
+  const int lane_byte_off = lane_off * (int)sizeof(KV);
   const int nshared = HINT ? a.shared_prefix_blocks[it.seq] : 0;
   const int shared_ahead = nshared - jb - w;   // this wave's block idx is shared iff idx < idx_shared
   const int idx_shared = shared_ahead > 0 ? min(nb_w, (shared_ahead + NW - 1) / NW) : 0;
@@ -380,16 +450,16 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
         const bool live = t < cnt && in_pool;
         const int64_t off = live ? ((int64_t)bid * a.num_kv_heads + kvh) * head_slab : 0;
         const int bytes = live ? slab_bytes : 0;
-        load_slab<T, D, P>(sl, slab_rsrc(kpool + off, bytes), slab_rsrc(vpool + off, bytes),
-                           lane_byte_off);
+        load_slab<KV, D, P>(sl, slab_rsrc(kpool + off, bytes), slab_rsrc(vpool + off, bytes),
+                            lane_byte_off);
       };
       const auto consume = [&](const Slab<NLD>& sl, int t) {
         const int j = jb + w + NW * (base + t);
         const int nvalid = min(kBlock, tok_end - j * kBlock);
         if (nvalid == kBlock)
-          consume_slab<T, D, GP, false>(sl, q, a.scale_log2, r, nvalid, m, l, acc);
+          consume_slab<T, KV, D, GP, false>(sl, q, a.scale_log2, r, nvalid, m, l, acc);
         else
-          consume_slab<T, D, GP, true>(sl, q, a.scale_log2, r, nvalid, m, l, acc);
+          consume_slab<T, KV, D, GP, true>(sl, q, a.scale_log2, r, nvalid, m, l, acc);
       };
       Slab<NLD> sa, sb;
       load_step(sa, 0);
@@ -457,6 +527,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
       o = fmaf(sh_acc[x][g][d], f, o);
     }
     o = poisoned ? __builtin_nanf("") : o / lsum;
+    if constexpr (std::is_same<KV, fp8_t>::value) o *= a.v_scale;
     const int h = kvh * G + g;
     if (nparts <= 1) {
       out[((int64_t)item * hq + h) * D + d] = ElemTraits<T>::from_f32(o);
@@ -468,30 +539,37 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   }
 }
 
-template <typename T, int D, bool HINT>
+// Query heads per kv head the vector-ALU kernel takes for an FP8 cache: its
+// widened fp32 accumulators (16 per head and lane) leave no room for more.
+constexpr int kFp8ValuMaxGroup = 4;
+
+template <typename T, typename KV, int D, bool HINT>
 inline void launch_decode_group(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
   const dim3 block(256);
   const int G = a.group;
   if (G <= 1)
-    hipLaunchKernelGGL((decode_valu_kernel<T, D, 1, HINT>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_valu_kernel<T, KV, D, 1, HINT>), grid, block, 0, stream, a);
   else if (G <= 2)
-    hipLaunchKernelGGL((decode_valu_kernel<T, D, 2, HINT>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_valu_kernel<T, KV, D, 2, HINT>), grid, block, 0, stream, a);
   else if (G <= 4)
-    hipLaunchKernelGGL((decode_valu_kernel<T, D, 4, HINT>), grid, block, 0, stream, a);
-  else if (G <= 8)
-    hipLaunchKernelGGL((decode_valu_kernel<T, D, 8, HINT>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_valu_kernel<T, D, 16, HINT>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_valu_kernel<T, KV, D, 4, HINT>), grid, block, 0, stream, a);
+  else if constexpr (!std::is_same<KV, fp8_t>::value) {
+    if (G <= 8)
+      hipLaunchKernelGGL((decode_valu_kernel<T, KV, D, 8, HINT>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_valu_kernel<T, KV, D, 16, HINT>), grid, block, 0, stream, a);
+  }
 }
 
-template <typename T, int D>
+template <typename T, typename KV, int D>
 inline hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+  if (std::is_same<KV, fp8_t>::value && a.group > kFp8ValuMaxGroup) return hipErrorInvalidValue;
   dim3 grid((unsigned)((int64_t)a.num_items * a.num_kv_heads),
             a.partition_blocks > 0 ? a.max_partitions : 1);
   if (a.shared_prefix_blocks != nullptr)
-    launch_decode_group<T, D, true>(a, grid, stream);
+    launch_decode_group<T, KV, D, true>(a, grid, stream);
   else
-    launch_decode_group<T, D, false>(a, grid, stream);
+    launch_decode_group<T, KV, D, false>(a, grid, stream);
   return hipGetLastError();
 }
 

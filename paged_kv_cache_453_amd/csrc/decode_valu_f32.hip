@@ -4,7 +4,8 @@
 namespace pa {
 
 hipError_t launch_decode_valu_f32(const DecodeArgs& a, int head_dim, hipStream_t stream) {
-  return head_dim == 64 ? launch_decode_t<float, 64>(a, stream) : launch_decode_t<float, 128>(a, stream);
+  return head_dim == 64 ? launch_decode_t<float, float, 64>(a, stream)
+                        : launch_decode_t<float, float, 128>(a, stream);
 }
 
 }  // namespace pa

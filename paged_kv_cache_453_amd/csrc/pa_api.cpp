@@ -4,6 +4,7 @@
 // HIP call; a bad argument returns a negative pa_status and launches nothing.
 // Launches go to the caller's stream; nothing here allocates or synchronises.
 #include <limits.h>
+#include <math.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -18,7 +19,8 @@ constexpr int64_t kMaxGridY = 65535;
 
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
 bool dtype_ok(pa_dtype t) { return t == PA_F32 || t == PA_BF16; }
-int elem_bytes(pa_dtype t) { return t == PA_F32 ? 4 : 2; }
+bool pool_dtype_ok(pa_dtype t) { return dtype_ok(t) || t == PA_FP8_E4M3; }
+int elem_bytes(pa_dtype t) { return t == PA_F32 ? 4 : t == PA_BF16 ? 2 : 1; }
 
 int max_partitions(int max_context_len, int partition_size) {
   if (partition_size <= 0) return 1;
@@ -27,6 +29,68 @@ int max_partitions(int max_context_len, int partition_size) {
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
+
+bool scale_ok(float s) { return s > 0.f && s < INFINITY; }
+
+// Shared by pa_decode and pa_decode_fp8: checks, then the kernel choice.
+int decode_impl(void* out, const void* query, const void* key_cache, const void* value_cache,
+                const int32_t* block_tables, const int32_t* context_lens,
+                const int32_t* shared_prefix_blocks, int num_seqs, int num_heads,
+                int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                int64_t num_blocks, int max_context_len, float scale, int partition_size,
+                void* workspace, size_t workspace_bytes, pa_dtype dtype, bool fp8,
+                float k_scale, float v_scale, hipStream_t stream) {
+  if (num_seqs < 0) return PA_ERR_SHAPE;
+  if (num_seqs > 0 && (!out || !query || !key_cache || !value_cache || !block_tables ||
+                       !context_lens))
+    return PA_ERR_NULL;
+  if (!dtype_ok(dtype) || block_size != kBlockSize || !head_dim_ok(head_dim))
+    return PA_ERR_UNSUPPORTED;
+  if (num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads != 0 ||
+      num_kv_heads > kMaxGridY || max_blocks_per_seq < 1 || num_blocks < 1 ||
+      max_context_len < 0 || partition_size < 0 || partition_size % kBlockSize != 0)
+    return PA_ERR_SHAPE;
+  if (fp8 && (!scale_ok(k_scale) || !scale_ok(v_scale))) return PA_ERR_SHAPE;
+  const int group = num_heads / num_kv_heads;
+  if (group > kMaxGroup) return PA_ERR_UNSUPPORTED;
+  if (fp8 && !pa::decode_fp8_supported(group, head_dim, dtype == PA_BF16))
+    return PA_ERR_UNSUPPORTED;
+  const int nparts = max_partitions(max_context_len, partition_size);
+  if (nparts > kMaxGridY || (int64_t)num_seqs * num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;
+  if (partition_size > 0) {
+    const size_t need = pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len,
+                                                  partition_size);
+    if (num_seqs > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+  }
+  if (num_seqs == 0) return PA_OK;
+  pa::DecodeArgs a = {};
+  a.out = out;
+  a.query = query;
+  a.k_cache = key_cache;
+  a.v_cache = value_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start_loc = nullptr;
+  a.shared_prefix_blocks = shared_prefix_blocks;
+  const size_t rows = (size_t)num_seqs * num_heads * nparts;
+  a.part_o = partition_size > 0 ? static_cast<float*>(workspace) : nullptr;
+  a.part_lse = partition_size > 0 ? static_cast<float*>(workspace) + rows * head_dim : nullptr;
+  a.num_seqs = num_seqs;
+  a.num_items = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.max_context_len = max_context_len;
+  a.partition_blocks = partition_size / kBlockSize;
+  a.max_partitions = nparts;
+  a.max_query_len = 1;
+  a.scale_log2 = (fp8 ? scale * k_scale : scale) * 1.4426950408889634f;
+  a.v_scale = fp8 ? v_scale : 1.f;
+  if (fp8) return status_of(pa::launch_decode_fp8(a, head_dim, dtype == PA_BF16, stream));
+  return status_of(pa::launch_decode(a, head_dim, dtype == PA_BF16, stream));
+}
 
 }  // namespace
 
@@ -62,7 +126,7 @@ int pa_reshape_and_cache(const void* key, const void* value, void* key_cache, vo
   const int64_t row = (int64_t)num_kv_heads * head_dim;
   if (key_stride < row || value_stride < row) return PA_ERR_SHAPE;
   if (num_tokens == 0) return PA_OK;
-  pa::ScatterArgs a;
+  pa::ScatterArgs a = {};
   a.key = key;
   a.value = value;
   a.key_cache = key_cache;
@@ -75,6 +139,44 @@ int pa_reshape_and_cache(const void* key, const void* value, void* key_cache, vo
   a.head_dim = head_dim;
   a.num_blocks = num_blocks;
   a.elem_bytes = elem_bytes(dtype);
+  a.fp8 = false;
+  return status_of(pa::launch_reshape_and_cache(a, stream));
+}
+
+int pa_reshape_and_cache_fp8(const void* key, const void* value, uint8_t* key_cache,
+                             uint8_t* value_cache, const int64_t* slot_mapping,
+                             int64_t num_tokens, int64_t key_stride, int64_t value_stride,
+                             int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                             pa_dtype src_dtype, float k_scale, float v_scale,
+                             hipStream_t stream) {
+  if (!key_cache || !value_cache) return PA_ERR_NULL;
+  if (num_tokens > 0 && (!key || !value || !slot_mapping)) return PA_ERR_NULL;
+  if (!dtype_ok(src_dtype) || block_size != kBlockSize || !head_dim_ok(head_dim))
+    return PA_ERR_UNSUPPORTED;
+  if (((reinterpret_cast<uintptr_t>(key_cache) | reinterpret_cast<uintptr_t>(value_cache)) & 3) != 0)
+    return PA_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_tokens > INT32_MAX || num_kv_heads < 1 || num_blocks < 1)
+    return PA_ERR_SHAPE;
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (key_stride < row || value_stride < row) return PA_ERR_SHAPE;
+  if (!scale_ok(k_scale) || !scale_ok(v_scale)) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  pa::ScatterArgs a = {};
+  a.key = key;
+  a.value = value;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.key_stride = key_stride;
+  a.value_stride = value_stride;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = num_blocks;
+  a.elem_bytes = elem_bytes(src_dtype);
+  a.fp8 = true;
+  a.k_inv_scale = 1.f / k_scale;
+  a.v_inv_scale = 1.f / v_scale;
   return status_of(pa::launch_reshape_and_cache(a, stream));
 }
 
@@ -95,50 +197,24 @@ int pa_decode(void* out, const void* query, const void* key_cache, const void* v
               int max_blocks_per_seq, int64_t num_blocks, int max_context_len, float scale,
               int partition_size, void* workspace, size_t workspace_bytes, pa_dtype dtype,
               hipStream_t stream) {
-  if (num_seqs < 0) return PA_ERR_SHAPE;
-  if (num_seqs > 0 && (!out || !query || !key_cache || !value_cache || !block_tables ||
-                       !context_lens))
-    return PA_ERR_NULL;
-  if (!dtype_ok(dtype) || block_size != kBlockSize || !head_dim_ok(head_dim))
-    return PA_ERR_UNSUPPORTED;
-  if (num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads != 0 ||
-      num_kv_heads > kMaxGridY || max_blocks_per_seq < 1 || num_blocks < 1 ||
-      max_context_len < 0 || partition_size < 0 || partition_size % kBlockSize != 0)
-    return PA_ERR_SHAPE;
-  if (num_heads / num_kv_heads > kMaxGroup) return PA_ERR_UNSUPPORTED;
-  const int nparts = max_partitions(max_context_len, partition_size);
-  if (nparts > kMaxGridY || (int64_t)num_seqs * num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;
-  if (partition_size > 0) {
-    const size_t need = pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len,
-                                                  partition_size);
-    if (num_seqs > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
-  }
-  if (num_seqs == 0) return PA_OK;
-  pa::DecodeArgs a = {};
-  a.out = out;
-  a.query = query;
-  a.k_cache = key_cache;
-  a.v_cache = value_cache;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.query_start_loc = nullptr;
-  a.shared_prefix_blocks = shared_prefix_blocks;
-  const size_t rows = (size_t)num_seqs * num_heads * nparts;
-  a.part_o = partition_size > 0 ? static_cast<float*>(workspace) : nullptr;
-  a.part_lse = partition_size > 0 ? static_cast<float*>(workspace) + rows * head_dim : nullptr;
-  a.num_seqs = num_seqs;
-  a.num_items = num_seqs;
-  a.num_heads = num_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.group = num_heads / num_kv_heads;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.num_blocks = num_blocks;
-  a.max_context_len = max_context_len;
-  a.partition_blocks = partition_size / kBlockSize;
-  a.max_partitions = nparts;
-  a.max_query_len = 1;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  return status_of(pa::launch_decode(a, head_dim, dtype == PA_BF16, stream));
+  return decode_impl(out, query, key_cache, value_cache, block_tables, context_lens,
+                     shared_prefix_blocks, num_seqs, num_heads, num_kv_heads, head_dim,
+                     block_size, max_blocks_per_seq, num_blocks, max_context_len, scale,
+                     partition_size, workspace, workspace_bytes, dtype, false, 1.f, 1.f, stream);
+}
+
+int pa_decode_fp8(void* out, const void* query, const uint8_t* key_cache,
+                  const uint8_t* value_cache, const int32_t* block_tables,
+                  const int32_t* context_lens, const int32_t* shared_prefix_blocks,
+                  int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                  int max_blocks_per_seq, int64_t num_blocks, int max_context_len, float scale,
+                  float k_scale, float v_scale, int partition_size, void* workspace,
+                  size_t workspace_bytes, pa_dtype dtype, hipStream_t stream) {
+  return decode_impl(out, query, key_cache, value_cache, block_tables, context_lens,
+                     shared_prefix_blocks, num_seqs, num_heads, num_kv_heads, head_dim,
+                     block_size, max_blocks_per_seq, num_blocks, max_context_len, scale,
+                     partition_size, workspace, workspace_bytes, dtype, true, k_scale, v_scale,
+                     stream);
 }
 
 int pa_decode_splitk_reduce(void* out, const void* workspace, size_t workspace_bytes,
@@ -210,6 +286,7 @@ int pa_prefill_chunk(void* out, const void* query, const void* key_cache, const 
   a.max_partitions = 1;
   a.max_query_len = max_query_len;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.v_scale = 1.f;
   if (dtype == PA_BF16) return status_of(pa::launch_prefill_mfma(a, head_dim, stream));
   return status_of(pa::launch_decode(a, head_dim, false, stream));
 }
@@ -219,7 +296,7 @@ int pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* block_mapp
                    int64_t num_blocks, pa_dtype dtype, hipStream_t stream) {
   if (!key_cache || !value_cache) return PA_ERR_NULL;
   if (num_pairs > 0 && !block_mapping) return PA_ERR_NULL;
-  if (!dtype_ok(dtype) || block_size != kBlockSize || !head_dim_ok(head_dim))
+  if (!pool_dtype_ok(dtype) || block_size != kBlockSize || !head_dim_ok(head_dim))
     return PA_ERR_UNSUPPORTED;
   if (num_pairs < 0 || num_kv_heads < 1 || num_blocks < 1) return PA_ERR_SHAPE;
   if (num_pairs == 0) return PA_OK;
@@ -271,7 +348,7 @@ int pa_swap_blocks(const void* src_key, const void* src_value, void* dst_key, vo
                    pa_dtype dtype, hipStream_t stream) {
   if (!src_key || !src_value || !dst_key || !dst_value) return PA_ERR_NULL;
   if (num_pairs > 0 && !block_mapping) return PA_ERR_NULL;
-  if (!dtype_ok(dtype) || block_size != kBlockSize || !head_dim_ok(head_dim))
+  if (!pool_dtype_ok(dtype) || block_size != kBlockSize || !head_dim_ok(head_dim))
     return PA_ERR_UNSUPPORTED;
   if (num_pairs < 0 || num_kv_heads < 1 || src_num_blocks < 1 || dst_num_blocks < 1)
     return PA_ERR_SHAPE;

@@ -40,6 +40,46 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
+// ---- fp8 (OCP E4M3) <-> fp32 ------------------------------------------------
+// An E4M3 code (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+// infinities, NaN = S.1111.111, largest magnitude 448) kept as its byte.
+typedef uint8_t fp8_t;
+constexpr float kFp8Max = 448.f;
+
+// Four codes of one word (byte i = element i) -> four fp32 values, exact; the
+// gfx950 conversion reads the OCP E4M3 format.
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* out) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  out[0] = lo.x;
+  out[1] = lo.y;
+  out[2] = hi.x;
+  out[3] = hi.y;
+}
+
+// Four codes -> four bf16 (two words, element 0 in the low half of word 0).
+// Exact: every E4M3 value has at most 4 significant bits.
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
+  float f[4];
+  fp8x4_to_f32(w, f);
+  return u32x2{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])};
+}
+
+// Four fp32 values -> four codes (element i in byte i): nearest, ties to even
+// (the hardware conversion), after saturating magnitudes above 448 to 448 (the
+// hardware would give NaN there); NaN gives 0x7F.
+__device__ __forceinline__ uint32_t f32x4_to_fp8x4(float a, float b, float c, float d) {
+  const auto sat = [](float x) { return fminf(fmaxf(x, -kFp8Max), kFp8Max); };
+  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat(a), sat(b), 0, false);
+  w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat(c), sat(d), (int)w, true);
+  const float x[4] = {a, b, c, d};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (isnan(x[i])) w = (w & ~(0xFFu << (8 * i))) | (0x7Fu << (8 * i));
+  return w;
+}
+
 // ---- cross-lane sums inside groups of 2/4/8/16 lanes (DPP, no LDS) --------
 // quad_perm [1,0,3,2] swaps neighbours, [2,3,0,1] swaps pairs, half-row mirror
 // maps lane i of an 8-lane half onto 7-i, row mirror maps lane i of a 16-lane

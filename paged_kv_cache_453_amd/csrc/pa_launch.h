@@ -18,7 +18,11 @@ struct ScatterArgs {
   int num_kv_heads;
   int head_dim;
   int64_t num_blocks;
-  int elem_bytes;
+  int elem_bytes;         // of key/value (and of the caches, unless FP8)
+  // FP8 caches: codes = E4M3(x * inv_scale), x widened to fp32 from key/value
+  bool fp8;
+  float k_inv_scale;
+  float v_inv_scale;
 };
 
 struct DecodeArgs {
@@ -43,7 +47,8 @@ struct DecodeArgs {
   int partition_blocks;   // 0 = one workgroup walks the whole context
   int max_partitions;
   int max_query_len;
-  float scale_log2;       // softmax scale * log2(e)
+  float scale_log2;       // softmax scale * log2(e) (times the K scale for FP8 caches)
+  float v_scale;          // FP8 caches: the V scale, applied to the output
 };
 
 struct ReduceArgs {
@@ -75,9 +80,16 @@ constexpr int kSwapPairsPerLaunch = 256;
 
 hipError_t launch_reshape_and_cache(const ScatterArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t stream);
+// FP8 caches: which (group, head_dim, query type) combinations have a kernel.
+bool decode_fp8_supported(int group, int head_dim, bool bf16_query);
+hipError_t launch_decode_fp8(const DecodeArgs& a, int head_dim, bool bf16_query,
+                             hipStream_t stream);
 hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_valu_bf16(const DecodeArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_decode_valu_f32(const DecodeArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_decode_valu_fp8(const DecodeArgs& a, int head_dim, bool bf16_query,
+                                  hipStream_t stream);
+hipError_t launch_decode_gqa_mfma_fp8(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_splitk_reduce(const ReduceArgs& a, int head_dim, bool bf16, hipStream_t stream);
 hipError_t launch_copy_blocks(const BlockPools& pools, const int32_t* block_mapping,
                               hipStream_t stream);

@@ -41,8 +41,51 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(ScatterArgs a) {
   }
 }
 
+// FP8 (E4M3) caches: the token's fp32 (or bf16-widened) values are multiplied
+// by the inverse per-tensor scale, rounded once to fp32, and encoded (nearest,
+// ties to even, saturating at 448).  Each thread handles 4 consecutive
+// elements of one head row and writes their 4 codes as one word.
+template <typename S>
+__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(ScatterArgs a) {
+  const int64_t tok = blockIdx.x;
+  const int64_t slot = a.slot_mapping[tok];
+  if (slot < 0 || slot >= a.num_blocks * kBlock) return;
+  const int64_t blk = slot / kBlock;
+  const int row = (int)(slot % kBlock);
+  const int quads = a.head_dim / 4;                    // 4-element groups per head row
+  const int total = a.num_kv_heads * quads;
+  const S* ksrc = static_cast<const S*>(a.key) + tok * a.key_stride;
+  const S* vsrc = static_cast<const S*>(a.value) + tok * a.value_stride;
+  uint32_t* kdst = static_cast<uint32_t*>(a.key_cache);
+  uint32_t* vdst = static_cast<uint32_t*>(a.value_cache);
+  const int64_t base = (blk * a.num_kv_heads * kBlock + row) * (int64_t)quads;
+  const auto widen = [](S x) {
+    if constexpr (sizeof(S) == 2) return __uint_as_float((uint32_t)x << 16);
+    else return x;
+  };
+  for (int i = threadIdx.x; i < total; i += blockDim.x) {
+    const int h = i / quads;
+    const int u = i - h * quads;
+    const int64_t d = base + (int64_t)h * kBlock * quads + u;
+    const S* k = ksrc + 4 * i;
+    const S* v = vsrc + 4 * i;
+    kdst[d] = f32x4_to_fp8x4(widen(k[0]) * a.k_inv_scale, widen(k[1]) * a.k_inv_scale,
+                             widen(k[2]) * a.k_inv_scale, widen(k[3]) * a.k_inv_scale);
+    vdst[d] = f32x4_to_fp8x4(widen(v[0]) * a.v_inv_scale, widen(v[1]) * a.v_inv_scale,
+                             widen(v[2]) * a.v_inv_scale, widen(v[3]) * a.v_inv_scale);
+  }
+}
+
 hipError_t launch_reshape_and_cache(const ScatterArgs& a, hipStream_t stream) {
   if (a.num_tokens == 0) return hipSuccess;
+  if (a.fp8) {
+    const dim3 grid((unsigned)a.num_tokens), block(256);
+    if (a.elem_bytes == 4)
+      hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<float>, grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<bf16_t>, grid, block, 0, stream, a);
+    return hipGetLastError();
+  }
   const auto aligned16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
   const bool vec = aligned16(a.key) && aligned16(a.value) && aligned16(a.key_cache) &&
                    aligned16(a.value_cache) && (a.key_stride * a.elem_bytes) % 16 == 0 &&

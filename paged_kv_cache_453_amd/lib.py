@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libpa.so")
 
 PA_F32 = 0
 PA_BF16 = 1
+PA_FP8_E4M3 = 2
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -75,6 +76,12 @@ def load() -> ctypes.CDLL:
     lib.pa_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                      i32, i64, i32, f32, i32, vp]
     lib.pa_prefill_chunk.restype = i32
+    lib.pa_reshape_and_cache_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32,
+                                             i64, i32, f32, f32, vp]
+    lib.pa_reshape_and_cache_fp8.restype = i32
+    lib.pa_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64,
+                                  i32, f32, f32, f32, i32, vp, sz, i32, vp]
+    lib.pa_decode_fp8.restype = i32
     lib.pa_copy_blocks.argtypes = [vp, vp, vp, i64, i32, i32, i32, i64, i32, vp]
     lib.pa_copy_blocks.restype = i32
     lib.pa_swap_blocks.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, vp]
@@ -107,8 +114,8 @@ def load() -> ctypes.CDLL:
 
 
 EXPORTED = ("pa_reshape_and_cache", "pa_decode_workspace_bytes", "pa_decode",
-            "pa_decode_splitk_reduce", "pa_prefill_chunk", "pa_copy_blocks", "pa_swap_blocks",
-            "pa_status_string")
+            "pa_decode_splitk_reduce", "pa_prefill_chunk", "pa_reshape_and_cache_fp8",
+            "pa_decode_fp8", "pa_copy_blocks", "pa_swap_blocks", "pa_status_string")
 
 
 # --------------------------------------------------------------------------
@@ -119,13 +126,16 @@ def _torch():
     return torch
 
 
-def _dtype_code(t) -> int:
+def _dtype_code(t, fp8_ok: bool = False) -> int:
     torch = _torch()
     if t.dtype == torch.float32:
         return PA_F32
     if t.dtype == torch.bfloat16:
         return PA_BF16
-    raise TypeError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16")
+    if fp8_ok and t.dtype == torch.uint8:
+        return PA_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16"
+                    + (" (or uint8 FP8 codes)" if fp8_ok else ""))
 
 
 def _ptr(t) -> Optional[int]:
@@ -247,6 +257,67 @@ def pa_prefill_chunk(out, query, key_cache, value_cache, block_tables, query_sta
 
 
 # --------------------------------------------------------------------------
+# FP8 (E4M3) KV cache
+# --------------------------------------------------------------------------
+def pa_reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping, k_scale: float,
+                             v_scale: float, stream=None) -> None:
+    """key/value [T, Hkv, D] fp32 or bf16; caches uint8 [NB, Hkv, 16, D] (E4M3 codes);
+    slot_mapping int64 [T]; code = E4M3(x / scale)."""
+    torch = _torch()
+    lib = load()
+    _on_gpu(key_cache, value_cache, slot_mapping)
+    _need(key.is_cuda and value.is_cuda, "key/value must be on the GPU")
+    _need(key.dim() == 3 and value.shape == key.shape, "key/value must be [T, Hkv, D]")
+    _need(key.stride(2) == 1 and key.stride(1) == key.shape[2] and value.stride(2) == 1 and
+          value.stride(1) == value.shape[2], "heads must be contiguous inside a token")
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.numel() == key.shape[0],
+          "slot_mapping must be int64 [T]")
+    _need(key.dtype == value.dtype, "key and value dtypes differ")
+    _need(key_cache.dtype == torch.uint8 and value_cache.dtype == torch.uint8,
+          "FP8 caches are uint8 tensors of E4M3 codes")
+    nb, hkv, bs, d = key_cache.shape
+    _need(tuple(value_cache.shape) == (nb, hkv, bs, d), "cache shapes differ")
+    _need(key.shape[1] == hkv and key.shape[2] == d, "key shape does not match the cache")
+    _check("pa_reshape_and_cache_fp8", lib.pa_reshape_and_cache_fp8(
+        _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(slot_mapping),
+        key.shape[0], key.stride(0), value.stride(0), hkv, d, bs, nb, _dtype_code(key),
+        float(k_scale), float(v_scale), _stream(stream)))
+
+
+def pa_decode_fp8(out, query, key_cache, value_cache, block_tables, context_lens, scale: float,
+                  k_scale: float, v_scale: float, max_context_len: int, partition_size: int = 0,
+                  workspace=None, stream=None, shared_prefix_blocks=None) -> None:
+    """pa_decode over uint8 E4M3 caches whose codes stand for value * k_scale / v_scale."""
+    torch = _torch()
+    lib = load()
+    _on_gpu(out, query, key_cache, value_cache, block_tables, context_lens)
+    _need(block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32,
+          "block_tables and context_lens must be int32")
+    _need(key_cache.dtype == torch.uint8 and value_cache.dtype == torch.uint8,
+          "FP8 caches are uint8 tensors of E4M3 codes")
+    s, hq, d = query.shape
+    nb, hkv, bs, d2 = key_cache.shape
+    _need(d2 == d and tuple(out.shape) == (s, hq, d) and value_cache.shape == key_cache.shape,
+          "shape mismatch")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == s and context_lens.numel() == s,
+          "block_tables must be [S, MB] and context_lens [S]")
+    _need(out.dtype == query.dtype, "query and output dtypes differ")
+    if shared_prefix_blocks is not None:
+        _on_gpu(shared_prefix_blocks)
+        _need(shared_prefix_blocks.dtype == torch.int32 and shared_prefix_blocks.numel() == s,
+              "shared_prefix_blocks must be int32 [S]")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _on_gpu(workspace)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check("pa_decode_fp8", lib.pa_decode_fp8(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), _ptr(shared_prefix_blocks), s, hq, hkv, d, bs, block_tables.shape[1],
+        nb, int(max_context_len), float(scale), float(k_scale), float(v_scale),
+        int(partition_size), ws_ptr, ws_bytes, _dtype_code(query), _stream(stream)))
+
+
+# --------------------------------------------------------------------------
 # block data movement
 # --------------------------------------------------------------------------
 def pa_copy_blocks(key_cache, value_cache, block_mapping, stream=None) -> None:
@@ -262,7 +333,7 @@ def pa_copy_blocks(key_cache, value_cache, block_mapping, stream=None) -> None:
     nb, hkv, bs, d = key_cache.shape
     _check("pa_copy_blocks", lib.pa_copy_blocks(
         _ptr(key_cache), _ptr(value_cache), _ptr(block_mapping), block_mapping.shape[0], hkv, d,
-        bs, nb, _dtype_code(key_cache), _stream(stream)))
+        bs, nb, _dtype_code(key_cache, fp8_ok=True), _stream(stream)))
 
 
 def pa_swap_blocks(src_key, src_value, dst_key, dst_value, block_mapping, stream=None) -> None:
@@ -281,7 +352,7 @@ def pa_swap_blocks(src_key, src_value, dst_key, dst_value, block_mapping, stream
     _check("pa_swap_blocks", lib.pa_swap_blocks(
         _ptr(src_key), _ptr(src_value), _ptr(dst_key), _ptr(dst_value),
         m.ctypes.data if m.size else None, m.shape[0], nbs, dst_key.shape[0], hkv, d, bs,
-        _dtype_code(src_key), _stream(stream)))
+        _dtype_code(src_key, fp8_ok=True), _stream(stream)))
 
 
 # --------------------------------------------------------------------------

@@ -177,3 +177,41 @@ def test_block_manager_rejects_bad_arguments(lib):
 def test_status_strings_cover_block_manager_codes(lib):
     for code in range(-10, 1):
         assert lib.pa_status_string(code) != b"unknown status"
+
+
+def test_fp8_validation(lib):
+    f = lib.pa_reshape_and_cache_fp8
+    base = [P, P, P, P, P, 4, 1024, 1024, 8, 128, 16, 64, BF16, 0.1, 0.1, None]
+
+    def scat(**kw):
+        a = list(base)
+        idx = dict(kc=2, T=5, d=9, bs=10, src=12, ks=13, vs=14)
+        for k, v in kw.items():
+            a[idx[k]] = v
+        return f(*a)
+
+    assert scat(kc=None) == PA_ERR_NULL
+    assert scat(kc=P + 2) == PA_ERR_UNSUPPORTED                   # pools must be 4-byte aligned
+    assert scat(src=2) == PA_ERR_UNSUPPORTED                      # the source is fp32 or bf16
+    assert scat(ks=0.0) == PA_ERR_SHAPE
+    assert scat(vs=float("inf")) == PA_ERR_SHAPE
+    assert scat(vs=float("nan")) == PA_ERR_SHAPE
+    assert scat(T=0) == PA_OK
+
+    g = lib.pa_decode_fp8
+    dbase = [P, P, P, P, P, P, None, 4, 8, 8, 128, 16, 4, 64, 64, 0.1, 0.5, 0.5, 0, None, 0,
+             BF16, None]
+
+    def dec(**kw):
+        a = list(dbase)
+        idx = dict(S=7, hq=8, hkv=9, d=10, ks=16, vs=17, dtype=21)
+        for k, v in kw.items():
+            a[idx[k]] = v
+        return g(*a)
+
+    assert dec(ks=-1.0) == PA_ERR_SHAPE
+    assert dec(vs=0.0) == PA_ERR_SHAPE
+    assert dec(hq=32, hkv=4, dtype=F32) == PA_ERR_UNSUPPORTED     # fp32 query, 8 per kv head
+    assert dec(hq=32, hkv=4, d=64) == PA_ERR_UNSUPPORTED          # bf16 but head_dim 64
+    assert dec(dtype=2) == PA_ERR_UNSUPPORTED                     # the query is fp32 or bf16
+    assert dec(S=0) == PA_OK

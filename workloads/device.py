@@ -88,6 +88,22 @@ def upload_pools(w: Workload, device="cuda"):
     return k, v
 
 
+def upload_fp8_pools(w: Workload, k_codes: np.ndarray, v_codes: np.ndarray, device="cuda"):
+    """uint8 device pools [num_blocks, Hkv, 16, D]: the NaN code everywhere, the
+    host code rows at w.host_ids."""
+    import torch
+    shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
+    k = torch.full(shape, 0x7F, dtype=torch.uint8, device=device)
+    v = torch.full(shape, 0x7F, dtype=torch.uint8, device=device)
+    ids = torch.from_numpy(w.host_ids).to(device)
+    step = 4096
+    for lo in range(0, w.host_ids.shape[0], step):
+        hi = min(w.host_ids.shape[0], lo + step)
+        k[ids[lo:hi]] = torch.from_numpy(np.ascontiguousarray(k_codes[lo:hi])).to(device)
+        v[ids[lo:hi]] = torch.from_numpy(np.ascontiguousarray(v_codes[lo:hi])).to(device)
+    return k, v
+
+
 def _group(g, dtype, hq, d, device):
     import torch
     q = host_to_torch(g.query, dtype, device)

@@ -121,6 +121,53 @@ def _normal(shape, dtype: str, seed_seq: np.random.SeedSequence) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# FP8 (E4M3) cache contents: random codes, drawn directly as bytes
+# --------------------------------------------------------------------------
+FP8_NAN_CODE = np.uint8(0x7F)
+
+
+def fp8_codes(shape, seed_seq: np.random.SeedSequence, max_exp_field: int = 9) -> np.ndarray:
+    """Random E4M3 codes: random sign, exponent field uniform in [0, max_exp_field],
+    mantissa uniform in [0, 7] -- magnitudes up to 2^(max_exp_field-7) * 1.875,
+    never NaN for max_exp_field < 15.  Chunked with child seeds, so the result
+    does not depend on the number of threads."""
+    out = np.empty(shape, dtype=np.uint8)
+    flat = out.reshape(-1)
+    n = flat.shape[0]
+    chunk = 1 << 24
+    kids = seed_seq.spawn(max(1, math.ceil(n / chunk)))
+
+    def work(c: int) -> None:
+        lo, hi = c * chunk, min(n, (c + 1) * chunk)
+        rng = np.random.default_rng(kids[c])
+        sign = rng.integers(0, 2, hi - lo, dtype=np.uint8) << 7
+        e = rng.integers(0, max_exp_field + 1, hi - lo, dtype=np.uint8) << 3
+        m = rng.integers(0, 8, hi - lo, dtype=np.uint8)
+        flat[lo:hi] = sign | e | m
+
+    if len(kids) == 1:
+        work(0)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(work, range(len(kids))))
+    return out
+
+
+def fp8_pools(w: "Workload", seed: int):
+    """Host code pools shaped like w.k_host / w.v_host: random codes where w's
+    pools hold data, the NaN code where they hold NaN (unused rows, slots a
+    scatter fills), so the same rows stay poisoned."""
+    kids = np.random.SeedSequence(seed).spawn(2)
+    out = []
+    for src, kid in ((w.k_host, kids[0]), (w.v_host, kids[1])):
+        codes = fp8_codes(src.shape, kid)
+        poison = np.isnan(src) if w.dtype == "f32" else (src == BF16_NAN)
+        codes[poison] = FP8_NAN_CODE
+        out.append(codes)
+    return out[0], out[1]
+
+
+# --------------------------------------------------------------------------
 # the workload record
 # --------------------------------------------------------------------------
 @dataclass
