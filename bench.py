@@ -13,6 +13,10 @@ shuffled pool) with split-K partitions and their merge.
   mixed     chunked prefill of 4 x 512-token chunks over paged prefixes, then
             decode of 192 sequences sharing 2048-token prefixes in groups of 3
             (also timed with prefill and decode on two streams)
+  llama13b_fp8, gqa_fp8
+            the llama13b and gqa steps over an FP8 (OCP E4M3) cache with one
+            scale per pool: quantising scatter (llama13b), decode, merge; KV
+            bytes count one byte per element
   block_moves  the data movement around the step at the Llama-2-13B pool shape:
             copy-on-write block copies (pa_copy_blocks, 1024 pairs in one call;
             the metric of that line is its read + write GB/s), swaps to and
@@ -49,7 +53,7 @@ _CSRC = os.path.join(ROOT, "paged_kv_cache_453_amd", "csrc")
 COUNTED = {
     "decode": {
         "json": os.path.join(ROOT, "profiles", "decode_llama13b_counters.json"),
-        "kernel": "void pa::decode_valu_kernel<unsigned short, 128, 1, false>",
+        "kernel": "void pa::decode_valu_kernel<unsigned short, unsigned short, 128, 1, false>",
         "sources": [os.path.join(_CSRC, f)
                     for f in ("decode_valu.h", "decode_valu_bf16.hip", "pa_device.h")],
         "bench": "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
@@ -89,26 +93,36 @@ def measured_traffic(kind: str):
     return c.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s: float = 10.0):
+FP8_K_SCALE, FP8_V_SCALE = 0.07, 0.11
+
+
+def cpu_baseline(w, budget_s: float = 10.0, fp8_pools=None):
     """The fp64 oracle on a bounded sample of the same workload, one host thread.
 
     Decode: the first sequences in order (scatter included where the workload
     has one) until budget_s of CPU time.  Prefill (mixed workload): the first
     chunk first, then decode sequences.  Reported in the metric's unit, KV GB/s
-    of decode over the sample.
+    of decode over the sample.  fp8_pools: (k codes, v codes) of an FP8 cache,
+    run through the FP8 oracle instead.
     """
     from threadpoolctl import threadpool_limits
 
     import oracle
+    from oracle import kv_fp8
     from workloads import accounting
 
-    k, v = w.k_host, w.v_host
+    fp8 = fp8_pools is not None
+    k, v = fp8_pools if fp8 else (w.k_host, w.v_host)
     t_total = 0.0
     notes = []
     with threadpool_limits(1):
         if w.slot_mapping is not None:
             t0 = time.perf_counter()
-            k, v = oracle.reshape_and_cache(k, v, w.new_k, w.new_v, w.host_slots())
+            if fp8:
+                k, v = kv_fp8.reshape_and_cache(k, v, w.new_k, w.new_v, w.host_slots(), w.dtype,
+                                                FP8_K_SCALE, FP8_V_SCALE)
+            else:
+                k, v = oracle.reshape_and_cache(k, v, w.new_k, w.new_v, w.host_slots())
             t_total += time.perf_counter() - t0
             notes.append(f"scatter of {len(w.slot_mapping)} tokens")
         if w.prefill is not None:
@@ -127,12 +141,16 @@ def cpu_baseline(w, budget_s: float = 10.0):
         while done < g.num_seqs and t_total + t_dec < budget_s:
             hi = min(g.num_seqs, done + 8)
             t0 = time.perf_counter()
-            oracle.decode(g.query[done:hi], k, v, tables[done:hi], g.context_lens[done:hi],
-                          w.scale, w.dtype)
+            if fp8:
+                kv_fp8.decode(g.query[done:hi], k, v, tables[done:hi], g.context_lens[done:hi],
+                              w.scale, FP8_K_SCALE, FP8_V_SCALE, w.dtype)
+            else:
+                oracle.decode(g.query[done:hi], k, v, tables[done:hi], g.context_lens[done:hi],
+                              w.scale, w.dtype)
             t_dec += time.perf_counter() - t0
             done = hi
     kv = accounting.decode_kv_bytes(g.context_lens[:done], w.num_kv_heads, w.head_dim,
-                                    w.elem_bytes)
+                                    1 if fp8 else w.elem_bytes)
     notes.append(f"decode of the first {done} of {g.num_seqs} sequences "
                  f"({int(g.context_lens[:done].sum())} tokens, {t_dec:.1f} s)")
     return {"value": round(kv / t_dec / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
@@ -250,7 +268,7 @@ class StepTimer:
                 for k, (name, _) in enumerate(launches)}
 
 
-WORKLOADS = ("llama13b", "llama7b", "gqa", "mixed", "block_moves")
+WORKLOADS = ("llama13b", "llama7b", "gqa", "mixed", "llama13b_fp8", "gqa_fp8", "block_moves")
 COPY_METRIC = "paged KV block copy GB/s (copy-on-write, read + write bytes) at Llama-2-13B pool shape"
 
 
@@ -428,18 +446,30 @@ def main(argv=None):
         return copy_calibration(torch, dev)
     lib.load()
     ps = args.partition_size
-    if ps is None:
-        ps = 512 if args.workload == "gqa" else 2048
-
     if args.workload == "block_moves":
         return bench_block_moves(args, torch, dev, lib, StepTimer(torch))
+    fp8 = args.workload.endswith("_fp8")
+    base = args.workload[:-len("_fp8")] if fp8 else args.workload
+    if ps is None:
+        ps = 512 if base == "gqa" else 2048
 
     log(f"bench: generating the {args.workload} workload")
     t0 = time.time()
-    w, cfg = build_workload(args.workload, ps)
+    w, cfg = build_workload(base, ps)
     g = w.decode
+    codes = None
+    if fp8:
+        from workloads import fp8_pools
+        from workloads.device import upload_fp8_pools
+        codes = fp8_pools(w, 453)
+        cfg["workload"] = cfg["workload"].replace("paged decode", "paged decode over an FP8 "
+                                                  "(E4M3) cache")
+        cfg["kv_cache"] = (f"fp8 e4m3 codes, random sign / exponent field 0..9 / mantissa; "
+                           f"k_scale {FP8_K_SCALE}, v_scale {FP8_V_SCALE}")
     log(f"bench: generated in {time.time() - t0:.1f} s; uploading")
-    dw = to_device(w, device=dev)
+    dw = to_device(w, device=dev, pools=not fp8)
+    if fp8:
+        dw.k_cache, dw.v_cache = upload_fp8_pools(w, codes[0], codes[1], device=dev)
     dg = dw.decode
     ws_bytes = lib.pa_decode_workspace_bytes(g.num_seqs, w.num_heads, w.head_dim,
                                              g.max_context_len, ps)
@@ -449,13 +479,23 @@ def main(argv=None):
     timer = StepTimer(torch)
 
     def scatter():
-        lib.pa_reshape_and_cache(dw.new_k, dw.new_v, dw.k_cache, dw.v_cache, dw.slot_mapping,
-                                 stream=stream)
+        if fp8:
+            lib.pa_reshape_and_cache_fp8(dw.new_k, dw.new_v, dw.k_cache, dw.v_cache,
+                                         dw.slot_mapping, FP8_K_SCALE, FP8_V_SCALE, stream=stream)
+        else:
+            lib.pa_reshape_and_cache(dw.new_k, dw.new_v, dw.k_cache, dw.v_cache,
+                                     dw.slot_mapping, stream=stream)
 
     def decode(s=stream):
-        lib.pa_decode(dg.out, dg.query, dw.k_cache, dw.v_cache, dg.block_tables,
-                      dg.context_lens, w.scale, g.max_context_len, ps, ws if ps else None,
-                      stream=s, shared_prefix_blocks=dg.shared_prefix_blocks)
+        if fp8:
+            lib.pa_decode_fp8(dg.out, dg.query, dw.k_cache, dw.v_cache, dg.block_tables,
+                              dg.context_lens, w.scale, FP8_K_SCALE, FP8_V_SCALE,
+                              g.max_context_len, ps, ws if ps else None, stream=s,
+                              shared_prefix_blocks=dg.shared_prefix_blocks)
+        else:
+            lib.pa_decode(dg.out, dg.query, dw.k_cache, dw.v_cache, dg.block_tables,
+                          dg.context_lens, w.scale, g.max_context_len, ps, ws if ps else None,
+                          stream=s, shared_prefix_blocks=dg.shared_prefix_blocks)
 
     def reduce(s=stream):
         if ps:
@@ -491,14 +531,16 @@ def main(argv=None):
     log("bench: step %.1f us (%s)" % (ms_per_step * 1e3, ", ".join(
         f"{k} {v * 1e3:.1f}" for k, v in kernel_ms.items())))
 
-    kv = accounting.decode_kv_bytes(g.context_lens, w.num_kv_heads, w.head_dim, w.elem_bytes)
+    kv_elem = 1 if fp8 else w.elem_bytes
+    kv = accounting.decode_kv_bytes(g.context_lens, w.num_kv_heads, w.head_dim, kv_elem)
     gbs = kv / (ms_per_step * 1e-3) / 1e9
     decode_gbs = kv / (kernel_ms["decode"] * 1e-3) / 1e9
     tokens = g.num_seqs
     extra = {}
     group = w.num_heads // w.num_kv_heads
-    dec_kernel = ("decode_gqa_mfma_kernel" if group >= 4 else
-                  f"decode_valu_kernel<bf16,{w.head_dim},{group}>")
+    kv_name = "fp8" if fp8 else "bf16"
+    dec_kernel = (f"decode_gqa_mfma_kernel<{kv_name}>" if group >= 4 else
+                  f"decode_valu_kernel<bf16,{kv_name},{w.head_dim},{group}>")
     roofline = {"bound": "hbm", "achieved": round(decode_gbs, 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(decode_gbs / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic("decode") if args.workload == "llama13b" else None,
@@ -559,7 +601,7 @@ def main(argv=None):
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a sample")
-        cpu = cpu_baseline(w)
+        cpu = cpu_baseline(w, fp8_pools=codes)
 
     config = {"workload": cfg.pop("workload"), "num_seqs": g.num_seqs,
               "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
@@ -578,7 +620,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8_e4m3 kv / bf16 q" if fp8 else "bf16",
         "data": "synthetic",
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(tokens / (ms_per_step * 1e-3), 1),
@@ -586,6 +628,7 @@ def main(argv=None):
                              "where present) per step, one attention layer",
         "kv_bytes_per_step": int(kv),
         "value_note": "KV bytes of the step / step time" + (
+            "; FP8 cache: one byte per K/V element" if fp8 else "") + (
             "; unique (physical) bytes: shared prefix rows count once"
             if w.prefill is not None else ""),
         "kernel_us": {k: round(v * 1e3, 2) for k, v in kernel_ms.items()},

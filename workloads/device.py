@@ -123,9 +123,11 @@ def _group(g, dtype, hq, d, device):
         max_query_len=g.max_query_len)
 
 
-def to_device(w: Workload, device="cuda", workspace_bytes: Optional[int] = None) -> DeviceWorkload:
+def to_device(w: Workload, device="cuda", workspace_bytes: Optional[int] = None,
+              pools: bool = True) -> DeviceWorkload:
+    """Upload a workload; pools=False leaves the caches out (k_cache / v_cache None)."""
     import torch
-    k, v = upload_pools(w, device)
+    k, v = upload_pools(w, device) if pools else (None, None)
     dw = DeviceWorkload(w=w, k_cache=k, v_cache=v)
     if w.decode is not None:
         dw.decode = _group(w.decode, w.dtype, w.num_heads, w.head_dim, device)
