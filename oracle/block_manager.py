@@ -59,6 +59,32 @@ policy):
       reserved slots cannot be forked, shared from or swapped out (Busy): a
       copy of its blocks would miss those tokens.
 
+Prefix caching (xdnf.cn article, section 六.3: a hash per KV block; a new
+request whose prefix blocks hit reuses them and skips their prefill; a hit
+needs the same model, precision, quantisation and adapter, the same tokens
+from position 0, and whole blocks -- a partial tail is never reused):
+* P1  A block's key is a chained hash: FNV-1a 64 over (the previous block's
+      key, the cache salt, the block's 16 token ids), little-endian, with key
+      0 before the first block.  The salt stands for everything besides the
+      tokens that must match (model, precision, quantisation, adapter).
+* P2  A sequence's full blocks enter the cache when they fill with known
+      tokens (append_tokens) -- at the end of that batch (take_moves), once
+      the caller is committed to writing them, and only if the sequence that
+      filled the block still holds it (a sequence freed in the same batch
+      never writes its tokens).  A hit is verified exactly, not by the key
+      alone: same salt, same 16 tokens, and a parent that is the block the
+      previous hit matched (none for the first), so a prefix is shared only if
+      it is identical token for token.  A key whose entry fails that check is
+      taken over by the newly filled block.
+* P3  A prompt reuses at most the full blocks before its last token, which
+      is always left to compute.
+* P4  A cached block nobody holds stays cached.  Allocation takes blocks
+      without cached contents first (R1); only when none is left it evicts
+      the cached block released longest ago.
+* P5  Only sequences created from a prompt (add_prompt) or forked from one
+      know their tokens and fill the cache; shares of chosen blocks and blocks
+      brought back by a swap-in are never entered.
+
 Data movement: copy_blocks copies whole physical blocks within a pool (the
 copy-on-write step); swap_blocks copies whole blocks between two pools (device
 and host).  A physical block of a [num_blocks, num_heads, block_size,
@@ -80,28 +106,79 @@ class Busy(RuntimeError):
     pass
 
 
+FNV64_OFFSET = 0xCBF29CE484222325
+FNV64_PRIME = 0x100000001B3
+
+
+def fnv1a64(data: bytes, h: int = FNV64_OFFSET) -> int:
+    """FNV-1a, 64 bits: for each byte, xor it in, then multiply by the prime."""
+    for byte in data:
+        h ^= byte
+        h = (h * FNV64_PRIME) & 0xFFFFFFFFFFFFFFFF
+    return h
+
+
+def block_key(parent_key: int, salt: int, tokens) -> int:
+    """Chained key of one full block (P1)."""
+    data = (int(parent_key).to_bytes(8, "little") + (int(salt) & (2**64 - 1)).to_bytes(8, "little")
+            + b"".join(int(t).to_bytes(4, "little", signed=True) for t in tokens))
+    return fnv1a64(data)
+
+
+def prefix_keys(tokens, salt: int = 0, block_size: int = 16) -> List[int]:
+    """Keys of all full blocks of a token sequence."""
+    keys, key = [], 0
+    for j in range(len(tokens) // block_size):
+        key = block_key(key, salt, tokens[j * block_size:(j + 1) * block_size])
+        keys.append(key)
+    return keys
+
+
 class _Pool:
     """Free stack and reference counts of one pool."""
 
     def __init__(self, n: int):
         self.free: List[int] = list(range(n - 1, -1, -1))    # top = end of list
+        self.lru: List[int] = []                             # idle cached blocks, oldest first (P4)
         self.ref = [0] * n
         self.held: List[int] = []                            # released while pending (R6)
         self.pending: set = set()                            # named by a pending pair
         self.pending_dst: set = set()
+        self.is_cached = lambda b: False
+        self.evict = lambda b: None
+
+    def num_idle(self) -> int:
+        return len(self.free) + len(self.lru)
 
     def take(self) -> int:
-        b = self.free.pop()
+        if self.free:
+            b = self.free.pop()
+        else:
+            b = self.lru.pop(0)
+            self.evict(b)
         self.ref[b] = 1
         return b
+
+    def park(self, b: int) -> None:
+        """An unreferenced block that no pending move names goes idle."""
+        (self.lru if self.is_cached(b) else self.free).append(b)
 
     def release(self, b: int) -> None:
         self.ref[b] -= 1
         if self.ref[b] == 0:
-            (self.held if b in self.pending else self.free).append(b)
+            if b in self.pending:
+                self.held.append(b)
+            else:
+                self.park(b)
+
+    def revive(self, b: int) -> None:
+        """An idle (or held-back) cached block is taken again by a cache hit."""
+        (self.held if b in self.held else self.lru).remove(b)
+        self.ref[b] = 1
 
     def settle(self) -> None:
-        self.free.extend(self.held)
+        for b in self.held:
+            self.park(b)
         self.held = []
         self.pending = set()
         self.pending_dst = set()
@@ -123,6 +200,17 @@ class BlockManager:
         self.copies: List[Tuple[int, int]] = []
         self.swapped_out: List[Tuple[int, int]] = []
         self.swapped_in: List[Tuple[int, int]] = []
+        # prefix cache (P1-P5)
+        self.cache: Dict[int, int] = {}                      # key -> device block
+        self.meta: Dict[int, tuple] = {}                     # block -> (key, parent, salt, tokens)
+        self.tok: Dict[int, List[int]] = {}                  # seq -> token ids (cache-aware seqs)
+        self.salt: Dict[int, int] = {}
+        self.keys: Dict[int, List[int]] = {}                 # seq -> keys of its full blocks
+        self.serial: Dict[int, int] = {}                     # seq -> creation number
+        self.next_serial = 0
+        self.to_register: List[tuple] = []                   # blocks filled in this batch (P2)
+        self.dev.is_cached = lambda b: b in self.meta
+        self.dev.evict = self._evict
 
     # convenience views of the device pool (tests read them)
     @property
@@ -146,6 +234,8 @@ class BlockManager:
     def _new(self, seq: int) -> None:
         if seq in self.tables:
             raise KeyError(f"sequence {seq} exists")
+        self.serial[seq] = self.next_serial
+        self.next_serial += 1
 
     # ---- sequences ----
     def add_sequence(self, seq: int) -> None:
@@ -165,6 +255,10 @@ class BlockManager:
         self.on_host[child] = False
         for b in self.tables[child]:
             self.dev.ref[b] += 1
+        if parent in self.tok:
+            self.tok[child] = list(self.tok[parent])
+            self.salt[child] = self.salt[parent]
+            self.keys[child] = list(self.keys[parent])
 
     def share(self, src: int, dst: int, logical_blocks) -> None:
         """New sequence dst made of the listed full logical blocks of src (R5):
@@ -191,6 +285,8 @@ class BlockManager:
         del self.ntok[seq]
         del self.on_host[seq]
         self.dirty.discard(seq)
+        for d in (self.tok, self.salt, self.keys, self.serial):
+            d.pop(seq, None)
 
     # ---- allocation ----
     def _cow_needed(self, seq: int, n: int) -> bool:
@@ -211,9 +307,9 @@ class BlockManager:
             raise ValueError("negative token count")
         if self._cow_needed(seq, n) and self.tables[seq][-1] in self.dev.pending_dst:
             raise Busy("the block to copy is the destination of a pending move")
-        if self.blocks_needed(seq, n) > len(self.dev.free):
+        if self.blocks_needed(seq, n) > self.dev.num_idle():
             raise OutOfBlocks(f"sequence {seq} needs {self.blocks_needed(seq, n)} blocks, "
-                              f"{len(self.dev.free)} free")
+                              f"{self.dev.num_idle()} free")
         bs = self.block_size
         table = self.tables[seq]
         slots = []
@@ -253,8 +349,8 @@ class BlockManager:
                     distinct.append(b)
         if any(b in src.pending_dst for b in distinct):
             raise Busy("a block to move is the destination of a pending move")
-        if len(distinct) > len(dst.free):
-            raise OutOfBlocks(f"{len(distinct)} blocks needed, {len(dst.free)} free")
+        if len(distinct) > dst.num_idle():
+            raise OutOfBlocks(f"{len(distinct)} blocks needed, {dst.num_idle()} free")
         moved = {}
         record = self.swapped_out if to_host else self.swapped_in
         for s in seqs:
@@ -285,6 +381,7 @@ class BlockManager:
         out = (self.copies, self.swapped_out, self.swapped_in)
         self.copies, self.swapped_out, self.swapped_in = [], [], []
         self.dirty = set()
+        self._commit_registrations()
         self.dev.settle()
         self.host.settle()
         return out
@@ -292,6 +389,89 @@ class BlockManager:
     def take_copies(self) -> List[Tuple[int, int]]:
         """Device copies only (for callers that never swap)."""
         return self.take_moves()[0]
+
+    # ---- prefix cache ----
+    def _evict(self, b: int) -> None:
+        key = self.meta.pop(b)[0]
+        del self.cache[key]
+
+    def _uncache(self, b: int) -> None:
+        """b loses its cache entry; if it is idle it moves to the plain free stack."""
+        del self.meta[b]
+        if b in self.dev.lru:
+            self.dev.lru.remove(b)
+            self.dev.free.append(b)
+
+    def _lookup(self, tokens, salt: int, max_blocks: int):
+        """Blocks of the longest verified cached prefix (P2, P3) and their keys."""
+        bs = self.block_size
+        hits, keys = [], []
+        key, parent = 0, -1
+        for j in range(max_blocks):
+            blk = tuple(int(t) for t in tokens[j * bs:(j + 1) * bs])
+            key = block_key(key, salt, blk)
+            b = self.cache.get(key)
+            if b is None or self.meta[b][1:] != (parent, salt, blk):
+                break
+            hits.append(b)
+            keys.append(key)
+            parent = b
+        return hits, keys
+
+    def add_prompt(self, seq: int, tokens, salt: int = 0) -> int:
+        """New sequence for a prompt: it starts on the longest cached prefix of
+        whole blocks (P3) and returns how many tokens that covers; the caller
+        appends the rest with append_tokens."""
+        self._new(seq)
+        tokens = [int(t) for t in tokens]
+        hits, keys = self._lookup(tokens, salt, max(0, (len(tokens) - 1) // self.block_size))
+        for b in hits:
+            if self.dev.ref[b] == 0:
+                self.dev.revive(b)
+            else:
+                self.dev.ref[b] += 1
+        n = len(hits) * self.block_size
+        self.tables[seq] = hits
+        self.ntok[seq] = n
+        self.on_host[seq] = False
+        self.tok[seq] = tokens[:n]
+        self.salt[seq] = salt
+        self.keys[seq] = keys
+        return n
+
+    def append_tokens(self, seq: int, tokens) -> List[int]:
+        """append_slots for known tokens; blocks they fill enter the cache (P2)."""
+        if seq not in self.tok:
+            raise KeyError(f"sequence {seq} does not track its tokens")
+        tokens = [int(t) for t in tokens]
+        slots = self.append_slots(seq, len(tokens))
+        self.tok[seq].extend(tokens)
+        bs = self.block_size
+        table, keys, salt = self.tables[seq], self.keys[seq], self.salt[seq]
+        while (len(keys) + 1) * bs <= self.ntok[seq]:
+            j = len(keys)
+            blk = tuple(self.tok[seq][j * bs:(j + 1) * bs])
+            parent = table[j - 1] if j else -1
+            key = block_key(keys[-1] if keys else 0, salt, blk)
+            keys.append(key)
+            self.to_register.append((self.serial[seq], seq, j, table[j], key, parent, salt, blk))
+        return slots
+
+    def _commit_registrations(self) -> None:
+        for serial, seq, j, b, key, parent, salt, blk in self.to_register:
+            if self.serial.get(seq) != serial or self.on_host[seq] or self.tables[seq][j] != b:
+                continue                      # freed (or moved) before its tokens were written
+            old = self.cache.get(key)
+            if old is not None and self.meta[old][1:] == (parent, salt, blk):
+                continue                      # the same prefix is cached in another block
+            if old is not None:
+                self._uncache(old)            # a stale or colliding entry gives way
+            self.cache[key] = b
+            self.meta[b] = (key, parent, salt, blk)
+        self.to_register = []
+
+    def num_cached_blocks(self) -> int:
+        return len(self.cache)
 
     # ---- queries ----
     def block_table(self, seq: int) -> List[int]:
@@ -304,7 +484,8 @@ class BlockManager:
         return self.on_host[seq]
 
     def num_free(self, host: bool = False) -> int:
-        return len((self.host if host else self.dev).free)
+        """Blocks an allocation can take (idle cached blocks included)."""
+        return (self.host if host else self.dev).num_idle()
 
     def shared_prefix_blocks(self, seq: int) -> int:
         """Leading table entries whose block another sequence also holds."""
@@ -327,9 +508,14 @@ class BlockManager:
                     for b in t:
                         count[b] += 1
             assert count == pool.ref
-            idle = pool.free + pool.held
+            idle = pool.free + pool.lru + pool.held
             assert sorted(idle) == [b for b in range(n) if count[b] == 0]
             assert len(set(idle)) == len(idle)
+        for key, b in self.cache.items():
+            assert self.meta[b][0] == key
+        assert len(self.meta) == len(self.cache)
+        assert all(b in self.meta for b in self.dev.lru)
+        assert not any(b in self.meta for b in self.dev.free)
         for seq, t in self.tables.items():
             assert len(t) == -(-self.ntok[seq] // self.block_size), seq
 

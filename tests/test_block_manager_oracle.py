@@ -95,9 +95,14 @@ class Cache:
             assert self.read(s) == self.hist[s], s
 
 
+def _data(d):
+    return {k: v for k, v in d.items() if not callable(v)}
+
+
 def _state(bm):
-    return copy.deepcopy((bm.dev.__dict__, bm.host.__dict__, bm.tables, bm.ntok, bm.on_host,
-                          bm.dirty, bm.copies, bm.swapped_out, bm.swapped_in))
+    return copy.deepcopy((_data(bm.dev.__dict__), _data(bm.host.__dict__), bm.tables, bm.ntok,
+                          bm.on_host, bm.dirty, bm.copies, bm.swapped_out, bm.swapped_in,
+                          bm.cache, bm.meta, bm.tok, bm.salt, bm.keys, bm.serial, bm.to_register))
 
 
 def run_random_workload(seed, steps=120, num_blocks=96, num_host_blocks=48):
