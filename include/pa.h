@@ -370,8 +370,46 @@ int pa_bm_build_batch(const pa_block_manager* bm, const int64_t* seqs, int32_t n
                       int32_t max_blocks_per_seq, int32_t* block_tables, int32_t* context_lens,
                       int32_t* shared_prefix_blocks);
 /* Checks the invariants (reference counts = table occurrences, free + held-back blocks =
- * unreferenced ones, table lengths = ceil(tokens / block_size)): PA_OK or PA_ERR_STATE. */
+ * unreferenced ones, table lengths = ceil(tokens / block_size), cache entries consistent):
+ * PA_OK or PA_ERR_STATE. */
 int pa_bm_check(const pa_block_manager* bm);
+
+/*
+ * Prefix cache.  Requests that share a prefix -- a system prompt, a fixed
+ * document, few-shot examples, earlier turns -- reuse its KV blocks and skip
+ * their prefill (xdnf.cn article, section 六.3).  A hit needs the same model,
+ * precision, quantisation and adapter (the caller folds them into `salt`), the
+ * same tokens from position 0, and whole blocks: a partly filled tail is never
+ * reused.
+ *
+ *  - Key of full block j: FNV-1a 64 over (key of block j-1, or 0 for j = 0;
+ *    salt; the block's 16 token ids), each as little-endian bytes (8, 8, 4 x 16).
+ *  - A sequence created from a prompt, or forked from one, knows its tokens;
+ *    each of its blocks that fills (pa_bm_append_tokens) enters the cache when
+ *    the batch ends (pa_bm_take_moves), if the sequence still holds it -- its
+ *    tokens are then about to be written.
+ *  - A hit is verified exactly, not by the key: same salt, same 16 tokens, and
+ *    a parent that is the block matched just before (none for block 0).  A key
+ *    whose entry fails that check is taken over by the newly filled block.
+ *  - Cached blocks nobody holds stay cached.  Allocation takes idle blocks
+ *    without cached contents first, then evicts the cached block that has
+ *    been idle longest.  Blocks brought back by a swap-in, and sequences made
+ *    by pa_bm_share or pa_bm_add_sequence, are never entered.
+ */
+/* keys[j] = key of full block j of tokens[0..num_tokens-1] (num_tokens / 16 keys). */
+int pa_bm_prefix_keys(const int32_t* tokens, int64_t num_tokens, uint64_t salt, uint64_t* keys);
+/* New sequence for a prompt: it starts on the longest cached prefix of whole blocks, at most
+ * the blocks before the prompt's last token (which is always left to compute), and
+ * *num_cached_tokens says how many tokens that covers.  Append the rest of the prompt with
+ * pa_bm_append_tokens; prefill only those. */
+int pa_bm_add_prompt(pa_block_manager* bm, int64_t seq, const int32_t* tokens,
+                     int64_t num_tokens, uint64_t salt, int64_t* num_cached_tokens);
+/* pa_bm_append_slots for a sequence that knows its tokens, with their ids (PA_ERR_SEQ for a
+ * sequence that does not). */
+int pa_bm_append_tokens(pa_block_manager* bm, int64_t seq, const int32_t* tokens, int32_t count,
+                        int64_t* slots);
+/* Cache entries (blocks that can be hit); negative status on error. */
+int64_t pa_bm_num_cached_blocks(const pa_block_manager* bm);
 
 /* Human-readable name of a pa_status value (static storage). */
 const char* pa_status_string(int status);

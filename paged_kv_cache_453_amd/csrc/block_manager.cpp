@@ -23,6 +23,20 @@
 //    batch never overlap and can run in any order -- all at once on the GPU;
 //  * a sequence that reserved slots since the last take cannot be forked,
 //    shared from or swapped out, since its new tokens are not in its blocks yet.
+//
+// Prefix cache (xdnf.cn article, section 六.3: a hash per KV block; a request
+// whose prefix blocks hit reuses them; a hit needs the same model, precision,
+// quantisation and adapter, the same tokens from position 0, and whole
+// blocks):
+//  * a block's key chains FNV-1a 64 over (previous key, salt, its 16 token
+//    ids); the salt stands for everything besides the tokens that must match;
+//  * a full block enters the cache at the end of the batch that filled it,
+//    if the sequence that filled it still holds it; a hit is verified exactly
+//    (salt, the 16 tokens, and the parent being the previous hit), and a key
+//    whose entry fails that check is taken over by the new block;
+//  * a prompt reuses at most the full blocks before its last token;
+//  * cached blocks nobody holds stay cached; allocation takes uncached idle
+//    blocks first and only then evicts the cached block idle the longest.
 #include <stdint.h>
 
 #include <algorithm>
@@ -36,12 +50,20 @@
 namespace {
 
 struct Pool {
-  std::vector<int32_t> free_stack;   // back() is the top
+  std::vector<int32_t> free_stack;   // idle blocks without cached contents; back() is the top
   std::vector<int32_t> ref;
   std::vector<int32_t> held;         // released while named by a pending pair
   std::vector<uint8_t> pending;      // named by a pending pair
   std::vector<uint8_t> pending_dst;  // destination of a pending pair
   std::vector<int32_t> marked;       // blocks whose pending flags are set
+  // idle blocks with cached contents, oldest first: a doubly linked list
+  std::vector<int32_t> lru_prev, lru_next;
+  std::vector<uint8_t> in_lru;
+  int32_t lru_head = -1, lru_tail = -1;
+  int64_t lru_size = 0;
+  const std::vector<uint8_t>* cached = nullptr;   // per block: holds a cache entry
+  void (*evict)(void*, int32_t) = nullptr;        // drops a block's cache entry
+  void* evict_ctx = nullptr;
 
   void init(int64_t n) {
     free_stack.resize((size_t)n);
@@ -49,16 +71,53 @@ struct Pool {
     ref.assign((size_t)n, 0);
     pending.assign((size_t)n, 0);
     pending_dst.assign((size_t)n, 0);
+    lru_prev.assign((size_t)n, -1);
+    lru_next.assign((size_t)n, -1);
+    in_lru.assign((size_t)n, 0);
   }
   int64_t size() const { return (int64_t)ref.size(); }
+  int64_t num_idle() const { return (int64_t)free_stack.size() + lru_size; }
+  bool is_cached(int32_t b) const { return cached && (*cached)[b]; }
+  void lru_push(int32_t b) {
+    lru_prev[b] = lru_tail;
+    lru_next[b] = -1;
+    if (lru_tail >= 0) lru_next[lru_tail] = b; else lru_head = b;
+    lru_tail = b;
+    in_lru[b] = 1;
+    ++lru_size;
+  }
+  void lru_remove(int32_t b) {
+    const int32_t p = lru_prev[b], n = lru_next[b];
+    if (p >= 0) lru_next[p] = n; else lru_head = n;
+    if (n >= 0) lru_prev[n] = p; else lru_tail = p;
+    in_lru[b] = 0;
+    --lru_size;
+  }
   int32_t take() {
-    const int32_t b = free_stack.back();
-    free_stack.pop_back();
+    int32_t b;
+    if (!free_stack.empty()) {
+      b = free_stack.back();
+      free_stack.pop_back();
+    } else {
+      b = lru_head;
+      lru_remove(b);
+      evict(evict_ctx, b);
+    }
     ref[b] = 1;
     return b;
   }
+  void park(int32_t b) {
+    if (is_cached(b)) lru_push(b); else free_stack.push_back(b);
+  }
   void release(int32_t b) {
-    if (--ref[b] == 0) (pending[b] ? held : free_stack).push_back(b);
+    if (--ref[b] == 0) {
+      if (pending[b]) held.push_back(b); else park(b);
+    }
+  }
+  void revive(int32_t b) {
+    const auto it = std::find(held.begin(), held.end(), b);
+    if (it != held.end()) held.erase(it); else lru_remove(b);
+    ref[b] = 1;
   }
   void mark(int32_t b, bool dst) {
     if (!pending[b]) {
@@ -68,7 +127,7 @@ struct Pool {
     if (dst) pending_dst[b] = 1;
   }
   void settle() {
-    free_stack.insert(free_stack.end(), held.begin(), held.end());
+    for (int32_t b : held) park(b);
     held.clear();
     for (int32_t b : marked) pending[b] = pending_dst[b] = 0;
     marked.clear();
@@ -80,11 +139,51 @@ struct Sequence {
   int64_t num_tokens = 0;
   bool on_host = false;
   bool dirty = false;  // reserved slots since the last take of the moves
+  uint64_t serial = 0;  // creation number
+  // prefix cache: the token ids (sequences created from a prompt, or forked
+  // from one), the salt and the keys of the full blocks
+  bool tracks_tokens = false;
+  std::vector<int32_t> tokens;
+  uint64_t salt = 0;
+  std::vector<uint64_t> keys;
 };
 
 using Pair = std::pair<int32_t, int32_t>;
+constexpr int kBs = 16;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// FNV-1a, 64 bits: for each byte, xor it in, then multiply by the prime.
+constexpr uint64_t kFnvOffset = 0xCBF29CE484222325ull;
+constexpr uint64_t kFnvPrime = 0x100000001B3ull;
+uint64_t fnv1a64_bytes(const uint8_t* p, size_t n, uint64_t h = kFnvOffset) {
+  for (size_t i = 0; i < n; ++i) {
+    h ^= p[i];
+    h *= kFnvPrime;
+  }
+  return h;
+}
+
+// Chained key of one full block: FNV-1a over the parent key, the salt (both
+// 8 bytes) and the 16 token ids (4 bytes each), little-endian.
+uint64_t block_key(uint64_t parent, uint64_t salt, const int32_t* tokens) {
+  uint8_t buf[16 + 4 * kBs];
+  for (int i = 0; i < 8; ++i) {
+    buf[i] = (uint8_t)(parent >> (8 * i));
+    buf[8 + i] = (uint8_t)(salt >> (8 * i));
+  }
+  for (int t = 0; t < kBs; ++t)
+    for (int i = 0; i < 4; ++i) buf[16 + 4 * t + i] = (uint8_t)((uint32_t)tokens[t] >> (8 * i));
+  return fnv1a64_bytes(buf, sizeof buf);
+}
+
+struct Registration {     // a block filled in the current batch
+  uint64_t serial;
+  int64_t seq;
+  int32_t j, block, parent;
+  uint64_t key, salt;
+  int32_t tokens[kBs];
+};
 
 }  // namespace
 
@@ -94,6 +193,48 @@ struct pa_block_manager {
   std::unordered_map<int64_t, Sequence> seqs;
   std::vector<int64_t> dirty;
   std::vector<Pair> copies, swapped_out, swapped_in;
+  uint64_t next_serial = 0;
+  // prefix cache over the device pool
+  std::unordered_map<uint64_t, int32_t> cache;   // key -> block
+  std::vector<uint8_t> cached;                   // per block: holds a cache entry
+  std::vector<uint64_t> meta_key, meta_salt;
+  std::vector<int32_t> meta_parent, meta_tokens; // meta_tokens: 16 per block
+  std::vector<Registration> to_register;
+
+  void init_cache(int64_t n) {
+    cached.assign((size_t)n, 0);
+    meta_key.assign((size_t)n, 0);
+    meta_salt.assign((size_t)n, 0);
+    meta_parent.assign((size_t)n, -1);
+    meta_tokens.assign((size_t)n * kBs, 0);
+    dev.cached = &cached;
+    dev.evict = [](void* ctx, int32_t b) { static_cast<pa_block_manager*>(ctx)->evict_block(b); };
+    dev.evict_ctx = this;
+  }
+  void evict_block(int32_t b) {
+    cache.erase(meta_key[b]);
+    cached[b] = 0;
+  }
+  // b loses its entry; an idle b moves from the cached list to the plain stack
+  void uncache(int32_t b) {
+    cached[b] = 0;
+    if (dev.in_lru[b]) {
+      dev.lru_remove(b);
+      dev.free_stack.push_back(b);
+    }
+  }
+  bool meta_matches(int32_t b, int32_t parent, uint64_t salt, const int32_t* tokens) const {
+    return meta_parent[b] == parent && meta_salt[b] == salt &&
+           std::equal(tokens, tokens + kBs, meta_tokens.begin() + (size_t)b * kBs);
+  }
+  Sequence& create(int64_t id) {
+    Sequence& s = seqs[id];
+    s.serial = next_serial++;
+    return s;
+  }
+  void lookup(const int32_t* tokens, int64_t max_blocks, uint64_t salt,
+              std::vector<int32_t>& hits, std::vector<uint64_t>& keys) const;
+  void commit_registrations();
 
   Sequence* find(int64_t id) {
     auto it = seqs.find(id);
@@ -121,13 +262,47 @@ struct pa_block_manager {
   int swap(const int64_t* ids, int32_t count, bool to_host);
 };
 
+void pa_block_manager::lookup(const int32_t* tokens, int64_t max_blocks, uint64_t salt,
+                              std::vector<int32_t>& hits, std::vector<uint64_t>& keys) const {
+  uint64_t key = 0;
+  int32_t parent = -1;
+  for (int64_t j = 0; j < max_blocks; ++j) {
+    const int32_t* blk = tokens + j * kBs;
+    key = block_key(key, salt, blk);
+    const auto it = cache.find(key);
+    if (it == cache.end() || !meta_matches(it->second, parent, salt, blk)) break;
+    hits.push_back(it->second);
+    keys.push_back(key);
+    parent = it->second;
+  }
+}
+
+void pa_block_manager::commit_registrations() {
+  for (const Registration& r : to_register) {
+    const Sequence* s = find(r.seq);
+    if (!s || s->serial != r.serial || s->on_host || s->table[(size_t)r.j] != r.block) continue;
+    const auto it = cache.find(r.key);
+    if (it != cache.end()) {
+      if (meta_matches(it->second, r.parent, r.salt, r.tokens)) continue;
+      uncache(it->second);          // a stale or colliding entry gives way
+    }
+    cache[r.key] = r.block;
+    cached[r.block] = 1;
+    meta_key[r.block] = r.key;
+    meta_salt[r.block] = r.salt;
+    meta_parent[r.block] = r.parent;
+    std::copy(r.tokens, r.tokens + kBs, meta_tokens.begin() + (size_t)r.block * kBs);
+  }
+  to_register.clear();
+}
+
 int pa_block_manager::append(int64_t id, int64_t n, int64_t* slots) {
   Sequence* s = find(id);
   if (!s || s->on_host) return PA_ERR_SEQ;
   if (n < 0) return PA_ERR_SHAPE;
   if (n > 0 && !slots) return PA_ERR_NULL;
   if (cow_needed(*s, n) && dev.pending_dst[s->table.back()]) return PA_ERR_BUSY;
-  if (blocks_needed(*s, n) > (int64_t)dev.free_stack.size()) return PA_ERR_NO_BLOCKS;
+  if (blocks_needed(*s, n) > dev.num_idle()) return PA_ERR_NO_BLOCKS;
   const int64_t bs = block_size;
   for (int64_t i = 0; i < n; ++i) {
     const int64_t pos = s->num_tokens;
@@ -171,7 +346,7 @@ int pa_block_manager::swap(const int64_t* ids, int32_t count, bool to_host) {
         if (src.pending_dst[b]) return PA_ERR_BUSY;
         ++distinct;
       }
-  if (distinct > (int64_t)dst.free_stack.size()) return PA_ERR_NO_BLOCKS;
+  if (distinct > dst.num_idle()) return PA_ERR_NO_BLOCKS;
   std::vector<Pair>& record = to_host ? swapped_out : swapped_in;
   for (Sequence* s : list) {
     for (int32_t& b : s->table) {
@@ -208,6 +383,7 @@ int pa_bm_create(int64_t num_blocks, int64_t num_host_blocks, int block_size,
     bm->block_size = block_size;
     bm->dev.init(num_blocks);
     bm->host.init(num_host_blocks);
+    bm->init_cache(num_blocks);
   } catch (...) {
     delete bm;
     return PA_ERR_NO_MEMORY;
@@ -220,8 +396,9 @@ void pa_bm_destroy(pa_block_manager* bm) { delete bm; }
 
 int pa_bm_add_sequence(pa_block_manager* bm, int64_t seq) {
   if (!bm) return PA_ERR_NULL;
+  if (bm->find(seq)) return PA_ERR_SEQ;
   try {
-    if (!bm->seqs.emplace(seq, Sequence()).second) return PA_ERR_SEQ;
+    bm->create(seq);
   } catch (...) {
     return PA_ERR_NO_MEMORY;
   }
@@ -235,11 +412,16 @@ int pa_bm_fork(pa_block_manager* bm, int64_t parent, int64_t child) {
   if (p->dirty) return PA_ERR_BUSY;
   if (bm->find(child)) return PA_ERR_SEQ;
   try {
-    Sequence c;
-    c.table = p->table;
-    c.num_tokens = p->num_tokens;
-    bm->seqs.emplace(child, std::move(c));
+    const Sequence parent_copy = *p;
+    Sequence& c = bm->create(child);
+    c.table = parent_copy.table;
+    c.num_tokens = parent_copy.num_tokens;
+    c.tracks_tokens = parent_copy.tracks_tokens;
+    c.tokens = parent_copy.tokens;
+    c.salt = parent_copy.salt;
+    c.keys = parent_copy.keys;
   } catch (...) {
+    bm->seqs.erase(child);
     return PA_ERR_NO_MEMORY;
   }
   for (int32_t b : bm->find(child)->table) ++bm->dev.ref[b];
@@ -259,12 +441,14 @@ int pa_bm_share(pa_block_manager* bm, int64_t src, int64_t dst, const int32_t* l
   for (int32_t i = 0; i < count; ++i)
     if (logical_blocks[i] < 0 || logical_blocks[i] >= full) return PA_ERR_SHAPE;
   try {
-    Sequence d;
-    d.table.reserve((size_t)count);
-    for (int32_t i = 0; i < count; ++i) d.table.push_back(s->table[(size_t)logical_blocks[i]]);
+    std::vector<int32_t> table;
+    table.reserve((size_t)count);
+    for (int32_t i = 0; i < count; ++i) table.push_back(s->table[(size_t)logical_blocks[i]]);
+    Sequence& d = bm->create(dst);
+    d.table = std::move(table);
     d.num_tokens = (int64_t)count * bm->block_size;
-    bm->seqs.emplace(dst, std::move(d));
   } catch (...) {
+    bm->seqs.erase(dst);
     return PA_ERR_NO_MEMORY;
   }
   for (int32_t b : bm->find(dst)->table) ++bm->dev.ref[b];
@@ -367,6 +551,7 @@ int pa_bm_take_moves(pa_block_manager* bm, int32_t* copies, int32_t* swap_out, i
     if (s) s->dirty = false;
   }
   bm->dirty.clear();
+  bm->commit_registrations();
   bm->dev.settle();
   bm->host.settle();
   return PA_OK;
@@ -404,7 +589,85 @@ int pa_bm_block_table(const pa_block_manager* bm, int64_t seq, int32_t* table, i
 
 int64_t pa_bm_num_free(const pa_block_manager* bm, int host) {
   if (!bm) return PA_ERR_NULL;
-  return (int64_t)(host ? bm->host : bm->dev).free_stack.size();
+  return (host ? bm->host : bm->dev).num_idle();
+}
+
+int pa_bm_prefix_keys(const int32_t* tokens, int64_t num_tokens, uint64_t salt, uint64_t* keys) {
+  if (num_tokens < 0) return PA_ERR_SHAPE;
+  const int64_t nb = num_tokens / kBs;
+  if (nb > 0 && (!tokens || !keys)) return PA_ERR_NULL;
+  uint64_t key = 0;
+  for (int64_t j = 0; j < nb; ++j) keys[j] = key = block_key(key, salt, tokens + j * kBs);
+  return PA_OK;
+}
+
+int pa_bm_add_prompt(pa_block_manager* bm, int64_t seq, const int32_t* tokens,
+                     int64_t num_tokens, uint64_t salt, int64_t* num_cached_tokens) {
+  if (!bm || !num_cached_tokens) return PA_ERR_NULL;
+  if (num_tokens < 0) return PA_ERR_SHAPE;
+  if (num_tokens > 0 && !tokens) return PA_ERR_NULL;
+  if (bm->find(seq)) return PA_ERR_SEQ;
+  try {
+    std::vector<int32_t> hits;
+    std::vector<uint64_t> keys;
+    const int64_t max_blocks = num_tokens > 0 ? (num_tokens - 1) / kBs : 0;
+    bm->lookup(tokens, max_blocks, salt, hits, keys);
+    Sequence s;
+    s.num_tokens = (int64_t)hits.size() * kBs;
+    s.tracks_tokens = true;
+    s.tokens.assign(tokens, tokens + s.num_tokens);
+    s.salt = salt;
+    s.keys = std::move(keys);
+    s.table = hits;
+    s.serial = bm->next_serial;
+    bm->seqs.emplace(seq, std::move(s));
+    ++bm->next_serial;
+    for (int32_t b : hits) {
+      if (bm->dev.ref[b] == 0) bm->dev.revive(b); else ++bm->dev.ref[b];
+    }
+    *num_cached_tokens = (int64_t)hits.size() * kBs;
+  } catch (...) {
+    return PA_ERR_NO_MEMORY;
+  }
+  return PA_OK;
+}
+
+int pa_bm_append_tokens(pa_block_manager* bm, int64_t seq, const int32_t* tokens, int32_t count,
+                        int64_t* slots) {
+  if (!bm) return PA_ERR_NULL;
+  Sequence* s = bm->find(seq);
+  if (!s || !s->tracks_tokens) return PA_ERR_SEQ;
+  if (count > 0 && !tokens) return PA_ERR_NULL;
+  try {
+    s->tokens.reserve(s->tokens.size() + (size_t)std::max<int32_t>(count, 0));
+    bm->to_register.reserve(bm->to_register.size() + (size_t)std::max<int32_t>(count, 0) / kBs + 1);
+    const int st = bm->append(seq, count, slots);
+    if (st != PA_OK) return st;
+    s->tokens.insert(s->tokens.end(), tokens, tokens + count);
+    while ((int64_t)(s->keys.size() + 1) * kBs <= s->num_tokens) {
+      const size_t j = s->keys.size();
+      Registration r;
+      r.serial = s->serial;
+      r.seq = seq;
+      r.j = (int32_t)j;
+      r.block = s->table[j];
+      r.parent = j ? s->table[j - 1] : -1;
+      r.salt = s->salt;
+      std::copy(s->tokens.begin() + (ptrdiff_t)(j * kBs), s->tokens.begin() + (ptrdiff_t)((j + 1) * kBs),
+                r.tokens);
+      r.key = block_key(j ? s->keys.back() : 0, s->salt, r.tokens);
+      s->keys.push_back(r.key);
+      bm->to_register.push_back(r);
+    }
+  } catch (...) {
+    return PA_ERR_NO_MEMORY;
+  }
+  return PA_OK;
+}
+
+int64_t pa_bm_num_cached_blocks(const pa_block_manager* bm) {
+  if (!bm) return PA_ERR_NULL;
+  return (int64_t)bm->cache.size();
 }
 
 int pa_bm_build_batch(const pa_block_manager* bm, const int64_t* seqs, int32_t num_seqs,
@@ -448,11 +711,21 @@ int pa_bm_check(const pa_block_manager* bm) {
       }
     }
     std::vector<uint8_t> idle((size_t)pool.size(), 0);
-    for (const std::vector<int32_t>* v : {&pool.free_stack, &pool.held})
+    std::vector<int32_t> lru;
+    for (int32_t b = pool.lru_head; b >= 0; b = pool.lru_next[b]) {
+      if ((int64_t)lru.size() > pool.size()) return PA_ERR_STATE;
+      lru.push_back(b);
+    }
+    if ((int64_t)lru.size() != pool.lru_size) return PA_ERR_STATE;
+    for (const std::vector<int32_t>* v : {&pool.free_stack, &pool.held, (const std::vector<int32_t>*)&lru})
       for (int32_t b : *v) {
         if (b < 0 || b >= pool.size() || idle[(size_t)b]) return PA_ERR_STATE;
         idle[(size_t)b] = 1;
       }
+    for (int32_t b : lru)
+      if (!pool.is_cached(b)) return PA_ERR_STATE;
+    for (int32_t b : pool.free_stack)
+      if (pool.is_cached(b)) return PA_ERR_STATE;
     for (int64_t b = 0; b < pool.size(); ++b) {
       if (count[(size_t)b] != pool.ref[(size_t)b]) return PA_ERR_STATE;
       if ((count[(size_t)b] == 0) != (idle[(size_t)b] == 1)) return PA_ERR_STATE;
@@ -460,6 +733,12 @@ int pa_bm_check(const pa_block_manager* bm) {
   }
   for (const auto& kv : bm->seqs)
     if ((int64_t)kv.second.table.size() != ceil_div(kv.second.num_tokens, bm->block_size))
+      return PA_ERR_STATE;
+  int64_t ncached = 0;
+  for (uint8_t c : bm->cached) ncached += c;
+  if (ncached != (int64_t)bm->cache.size()) return PA_ERR_STATE;
+  for (const auto& kv : bm->cache)
+    if (!bm->cached[(size_t)kv.second] || bm->meta_key[(size_t)kv.second] != kv.first)
       return PA_ERR_STATE;
   return PA_OK;
 }

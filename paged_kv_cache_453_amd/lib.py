@@ -105,7 +105,11 @@ def load() -> ctypes.CDLL:
             ("pa_bm_block_table", [vp, i64, vp, i32, vp], i32),
             ("pa_bm_num_free", [vp, i32], i64),
             ("pa_bm_build_batch", [vp, vp, i32, i32, vp, vp, vp], i32),
-            ("pa_bm_check", [vp], i32)):
+            ("pa_bm_check", [vp], i32),
+            ("pa_bm_prefix_keys", [vp, i64, ctypes.c_uint64, vp], i32),
+            ("pa_bm_add_prompt", [vp, i64, vp, i64, ctypes.c_uint64, vp], i32),
+            ("pa_bm_append_tokens", [vp, i64, vp, i32, vp], i32),
+            ("pa_bm_num_cached_blocks", [vp], i64)):
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = res
@@ -493,6 +497,46 @@ def pa_bm_check(h) -> None:
     _check("pa_bm_check", load().pa_bm_check(h))
 
 
+def _i32s(xs):
+    np = _np()
+    a = np.ascontiguousarray(np.asarray(xs, dtype=np.int32).reshape(-1))
+    return a, (a.ctypes.data if a.size else None)
+
+
+def pa_bm_prefix_keys(tokens, salt: int = 0):
+    """uint64 numpy array: chained keys of the full 16-token blocks of tokens."""
+    np = _np()
+    t, tp = _i32s(tokens)
+    keys = np.empty(t.size // 16, dtype=np.uint64)
+    _check("pa_bm_prefix_keys", load().pa_bm_prefix_keys(
+        tp, t.size, int(salt) & 0xFFFFFFFFFFFFFFFF, keys.ctypes.data if keys.size else None))
+    return keys
+
+
+def pa_bm_add_prompt(h, seq: int, tokens, salt: int = 0) -> int:
+    t, tp = _i32s(tokens)
+    n = ctypes.c_int64()
+    _check("pa_bm_add_prompt", load().pa_bm_add_prompt(
+        h, seq, tp, t.size, int(salt) & 0xFFFFFFFFFFFFFFFF, ctypes.byref(n)))
+    return n.value
+
+
+def pa_bm_append_tokens(h, seq: int, tokens):
+    np = _np()
+    t, tp = _i32s(tokens)
+    slots = np.empty(t.size, dtype=np.int64)
+    _check("pa_bm_append_tokens", load().pa_bm_append_tokens(
+        h, seq, tp, t.size, slots.ctypes.data if slots.size else None))
+    return slots
+
+
+def pa_bm_num_cached_blocks(h) -> int:
+    n = load().pa_bm_num_cached_blocks(h)
+    if n < 0:
+        raise PagedAttentionError("pa_bm_num_cached_blocks", int(n))
+    return int(n)
+
+
 class BlockManager:
     """The native block manager as an object (the pa_bm_* calls on one handle)."""
 
@@ -522,6 +566,9 @@ class BlockManager:
     def block_table(self, seq): return pa_bm_block_table(self._h, seq)
     def num_free(self, host=False): return pa_bm_num_free(self._h, host)
     def check_invariants(self): pa_bm_check(self._h)
+    def add_prompt(self, seq, tokens, salt=0): return pa_bm_add_prompt(self._h, seq, tokens, salt)
+    def append_tokens(self, seq, tokens): return pa_bm_append_tokens(self._h, seq, tokens)
+    def num_cached_blocks(self): return pa_bm_num_cached_blocks(self._h)
 
     def build_batch(self, seqs, max_blocks_per_seq):
         return pa_bm_build_batch(self._h, seqs, max_blocks_per_seq)

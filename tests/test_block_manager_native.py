@@ -147,3 +147,75 @@ def test_build_batch_tables_lengths_and_hint():
         n.build_batch([0], 2)                     # table longer than max_blocks_per_seq
     with pytest.raises(L.SequenceError):
         n.build_batch([7], 4)
+
+
+def test_native_prefix_keys_match_reference():
+    rng = np.random.default_rng(9)
+    for n, salt in ((0, 0), (15, 1), (16, 2), (100, 2**63 + 5), (333, 12345)):
+        toks = [int(x) for x in rng.integers(-2**31, 2**31, n)]
+        want = ref.prefix_keys(toks, salt)
+        got = [int(x) for x in L.pa_bm_prefix_keys(toks, salt)]
+        assert got == want
+
+
+def prompt_lockstep(seed, steps, num_blocks, num_host_blocks):
+    rng = np.random.default_rng(seed)
+    o = ref.BlockManager(num_blocks, BS, num_host_blocks)
+    n = L.BlockManager(num_blocks, BS, num_host_blocks)
+    systems = [[int(x) for x in rng.integers(0, 40, int(rng.integers(10, 60)))] for _ in range(3)]
+    live, nxt, hits = [], 0, 0
+    seen = set()
+    for _ in range(steps):
+        for _ in range(int(rng.integers(1, 7))):
+            op = int(rng.integers(0, 10))
+            pick = (lambda: int(rng.choice(live))) if live else (lambda: 10**9)
+            if op < 3 or not live:
+                toks = systems[int(rng.integers(0, 3))] + \
+                    [int(x) for x in rng.integers(0, 40, int(rng.integers(0, 30)))]
+                args = ("add_prompt", nxt, toks, int(rng.integers(0, 2)))
+            elif op < 6:
+                args = ("append_tokens", pick(),
+                        [int(x) for x in rng.integers(0, 40, int(rng.integers(0, 20)))])
+            elif op == 6:
+                args = ("fork", pick(), nxt)
+            elif op == 7:
+                args = ("free_sequence", pick())
+            elif op == 8:
+                args = ("swap_out", [pick()])
+            else:
+                args = ("swap_in", [pick()])
+            name, rest = args[0], args[1:]
+            ko, ro = outcome(getattr(o, name), *rest)
+            kn, rn = outcome(getattr(n, name), *rest)
+            assert ko == kn, (name, ko, kn)
+            seen.add((name, ko))
+            if ko == "ok":
+                if name == "add_prompt":
+                    assert ro == rn
+                    hits += ro
+                    live.append(nxt)
+                    nxt += 1
+                    toks = rest[1]
+                    k1, r1 = outcome(o.append_tokens, rest[0], toks[ro:])
+                    k2, r2 = outcome(n.append_tokens, rest[0], toks[ro:])
+                    assert k1 == k2 and (k1 != "ok" or list(r1) == [int(x) for x in r2])
+                elif name == "append_tokens":
+                    assert list(ro) == [int(x) for x in rn]
+                elif name == "fork":
+                    live.append(nxt)
+                    nxt += 1
+                elif name == "free_sequence":
+                    live.remove(rest[0])
+            compare(o, n, live)
+            assert o.num_cached_blocks() == n.num_cached_blocks()
+        moves_equal(o.take_moves(), n.take_moves())
+        compare(o, n, live)
+        assert o.num_cached_blocks() == n.num_cached_blocks()
+    return hits, seen
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_native_prefix_cache_matches_reference(seed):
+    hits, seen = prompt_lockstep(seed, steps=80, num_blocks=48, num_host_blocks=16)
+    assert hits > 0
+    assert ("add_prompt", "ok") in seen and ("append_tokens", "out") in seen
