@@ -17,6 +17,11 @@ shuffled pool) with split-K partitions and their merge.
             the llama13b and gqa steps over an FP8 (OCP E4M3) cache with one
             scale per pool: quantising scatter (llama13b), decode, merge; KV
             bytes count one byte per element
+  prefix_cache  32 prompts at Llama-2-13B shape sharing a 2048-token system
+            prompt, each with 256 tokens of its own: the chunked prefill of
+            all 32 with prefix-cache hits (256 query tokens each over the
+            cached 2048) against the same prompts prefilled whole, and the
+            block manager's host time to look the prompts up
   block_moves  the data movement around the step at the Llama-2-13B pool shape:
             copy-on-write block copies (pa_copy_blocks, 1024 pairs in one call;
             the metric of that line is its read + write GB/s), swaps to and
@@ -268,7 +273,10 @@ class StepTimer:
                 for k, (name, _) in enumerate(launches)}
 
 
-WORKLOADS = ("llama13b", "llama7b", "gqa", "mixed", "llama13b_fp8", "gqa_fp8", "block_moves")
+WORKLOADS = ("llama13b", "llama7b", "gqa", "mixed", "llama13b_fp8", "gqa_fp8", "prefix_cache",
+             "block_moves")
+PREFIX_METRIC = ("prefill us for 32 prompts sharing a 2048-token system prompt, with prefix-cache "
+                 "hits, at Llama-2-13B shape")
 COPY_METRIC = "paged KV block copy GB/s (copy-on-write, read + write bytes) at Llama-2-13B pool shape"
 
 
@@ -407,6 +415,122 @@ def bench_block_moves(args, torch, dev, lib, timer) -> int:
     return 0
 
 
+def bench_prefix_cache(args, torch, dev, lib, timer) -> int:
+    """Chunked prefill with and without prefix-cache hits, and the lookups."""
+    import numpy as np
+
+    from workloads import accounting
+
+    hq = hkv = 40
+    d, n, sys_len, own = 128, 32, 2048, 256
+    total = sys_len + own
+    scale = float(np.float32(1 / np.sqrt(d)))
+    rng = np.random.default_rng(453)
+    system = rng.integers(0, 32000, sys_len).astype(np.int32)
+    prompts = [np.concatenate([system, rng.integers(0, 32000, own).astype(np.int32)])
+               for _ in range(n + 1)]
+
+    # the block manager: an earlier request with the same system prompt fills
+    # the cache, then the 32 prompts are looked up
+    nb = 16384
+    bm = lib.BlockManager(nb)
+    bm.add_prompt(0, prompts[n])
+    bm.append_tokens(0, prompts[n])
+    bm.take_moves()
+    t0 = time.perf_counter()
+    cached = []
+    for i in range(1, n + 1):
+        c = bm.add_prompt(i, prompts[i - 1])
+        bm.append_tokens(i, prompts[i - 1][c:])
+        cached.append(c)
+    bm.take_moves()
+    host_us = (time.perf_counter() - t0) * 1e6
+    mb = total // 16
+    hit_tables, hit_lens, _ = bm.build_batch(list(range(1, n + 1)), mb)
+    assert all(c == sys_len for c in cached), cached
+
+    # pools of random bf16 contents, every block any table names
+    g = torch.Generator(device=dev).manual_seed(453)
+    kc = torch.randn((nb, hkv, 16, d), generator=g, device=dev).to(torch.bfloat16)
+    vc = torch.randn((nb, hkv, 16, d), generator=g, device=dev).to(torch.bfloat16)
+    # whole prompts: each its own 144 blocks
+    whole_tables = np.arange(n * mb, dtype=np.int32).reshape(n, mb) + 1024
+
+    def batch(tables, chunk):
+        qsl = np.arange(n + 1, dtype=np.int32) * chunk
+        lens = np.full(n, total, dtype=np.int32)
+        q = torch.randn((n * chunk, hq, d), generator=g, device=dev).to(torch.bfloat16)
+        return (q, torch.empty_like(q), torch.from_numpy(np.ascontiguousarray(tables)).to(dev),
+                torch.from_numpy(qsl).to(dev), torch.from_numpy(lens).to(dev), qsl, lens)
+
+    hit = batch(hit_tables, own)
+    whole = batch(whole_tables, total)
+    stream = torch.cuda.current_stream()
+
+    def run(b, chunk):
+        lib.pa_prefill_chunk(b[1], b[0], kc, vc, b[2], b[3], b[4], scale, chunk, stream=stream)
+
+    for _ in range(args.warmup):
+        run(hit, own)
+        run(whole, total)
+    torch.cuda.synchronize()
+    log(f"bench: timing {args.steps} prefills with and without prefix hits")
+    ms = timer.per_launch([("with_hits", lambda: run(hit, own)),
+                           ("whole", lambda: run(whole, total))], args.steps, stream)
+    flops_hit = accounting.prefill_flops(hit[5], hit[6], hq, d)
+    flops_whole = accounting.prefill_flops(whole[5], whole[6], hq, d)
+    tf = flops_hit / (ms["with_hits"] * 1e-3) / 1e12
+    result = {
+        "metric": PREFIX_METRIC, "value": round(ms["with_hits"] * 1e3, 2), "unit": "us",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms["with_hits"], 5), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "32 prompts sharing a 2048-token system prompt + 256 own tokens, "
+                               "40 = 40 heads, head_dim 128, bf16, block size 16",
+                   "cached_tokens_per_prompt": sys_len, "seed": 453},
+        "whole_prompt_prefill_us": round(ms["whole"] * 1e3, 2),
+        "prefill_speedup": round(ms["whole"] / ms["with_hits"], 2),
+        "prefill_tokens_per_step": {"with_hits": n * own, "whole": n * total},
+        "kv_blocks": {"with_hits": int(len(set(hit_tables[hit_tables >= 0].tolist()))),
+                      "whole": n * mb},
+        "block_manager_host_us": round(host_us, 1),
+        "block_manager_note": "add_prompt + append_tokens of 32 prompts of 2304 tokens (hashing, "
+                              "lookup, slots) and the batch's take_moves, through the C ABI",
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "prefill_mfma_kernel<128,32>",
+                     "algorithmic_flops_per_launch": int(flops_hit),
+                     "whole_prompt_flops": int(flops_whole)},
+        "cpu_baseline": None if args.no_cpu_baseline else prefix_cpu_baseline(d, hq, own, total),
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def prefix_cpu_baseline(d: int, hq: int, own: int, total: int, n: int = 32):
+    """The fp64 prefill oracle on one prompt's chunk (own query tokens over a
+    total-token context), one host thread, scaled to the 32-prompt batch."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from workloads.generate import f32_to_bf16_bits
+
+    rng = np.random.default_rng(454)
+    nblk = total // 16
+    k = f32_to_bf16_bits(rng.standard_normal((nblk, hq, 16, d)).astype(np.float32))
+    v = f32_to_bf16_bits(rng.standard_normal((nblk, hq, 16, d)).astype(np.float32))
+    q = f32_to_bf16_bits(rng.standard_normal((own, hq, d)).astype(np.float32))
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        oracle.prefill(q, k, v, np.arange(nblk)[None, :], np.array([0, own], dtype=np.int32),
+                       np.array([total], dtype=np.int32), np.float32(1 / np.sqrt(d)), "bf16")
+        t = time.perf_counter() - t0
+    return {"value": round(t * n * 1e6, 1), "unit": "us", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 numpy prefill oracle, 1 thread: one prompt's {own}-token chunk over "
+                      f"{total} tokens of context, {hq} heads ({t:.2f} s), times {n} prompts"}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -448,6 +572,8 @@ def main(argv=None):
     ps = args.partition_size
     if args.workload == "block_moves":
         return bench_block_moves(args, torch, dev, lib, StepTimer(torch))
+    if args.workload == "prefix_cache":
+        return bench_prefix_cache(args, torch, dev, lib, StepTimer(torch))
     fp8 = args.workload.endswith("_fp8")
     base = args.workload[:-len("_fp8")] if fp8 else args.workload
     if ps is None:
