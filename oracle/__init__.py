@@ -7,8 +7,8 @@ from .paged_attention import (to_f64, reshape_and_cache, gather, attend, decode,
                               decode_partials, merge_partials, prefill)
 from .block_manager import (BlockManager, OutOfBlocks, copy_blocks, swap_blocks, fnv1a64,
                             block_key, prefix_keys)
-from . import kv_fp8
+from . import kv_fp8, sampler
 
 __all__ = ["to_f64", "reshape_and_cache", "gather", "attend", "decode", "decode_partials",
            "merge_partials", "prefill", "BlockManager", "OutOfBlocks", "copy_blocks",
-           "swap_blocks", "fnv1a64", "block_key", "prefix_keys", "kv_fp8"]
+           "swap_blocks", "fnv1a64", "block_key", "prefix_keys", "kv_fp8", "sampler"]
