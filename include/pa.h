@@ -411,6 +411,35 @@ int pa_bm_append_tokens(pa_block_manager* bm, int64_t seq, const int32_t* tokens
 /* Cache entries (blocks that can be hit); negative status on error. */
 int64_t pa_bm_num_cached_blocks(const pa_block_manager* bm);
 
+/*
+ * pa_sample -- draw the next token of each row: temperature, top-k, top-p,
+ * then a draw from what is left, fused in one kernel with no sort ("vLLM
+ * 基本原理", section FlashInfer 采样器: temperature scaling, top-k keeps the K
+ * most probable tokens, top-p the most probable ones whose cumulative
+ * probability reaches P, the next token is drawn from the rest).
+ *
+ * For row r: z = logits[r] / temperature[r] (NaN counts as -inf).  If
+ * 0 < top_k[r] < vocab_size, tokens whose z is below the top_k[r]-th largest
+ * are dropped (ties with it stay).  Then, on the probabilities renormalised over
+ * the rest, a token stays if the mass of the tokens strictly more probable than
+ * it is below top_p[r] (top_p[r] = 1 keeps all).  tokens[r] is the first token,
+ * in vocabulary order, at which the cumulative probability of what stayed
+ * exceeds uniform[r]: the inverse of the distribution function, so the draw is
+ * a deterministic function of the caller's uniform number.  Weights are kept
+ * in fixed point with 40 fraction bits (64-bit integer sums, exact in any
+ * order), so probabilities below about 1e-12 of the largest count as zero.
+ *
+ *  tokens       device int32 [num_rows]: the drawn token, or -1 for a row with
+ *               no finite logit or out-of-range parameters (temperature <= 0,
+ *               top_p outside (0, 1], uniform outside [0, 1)).
+ *  logits       device [num_rows, row_stride], dtype fp32 or bf16; vocab_size
+ *               <= 36864 (the row is staged in LDS), else PA_ERR_UNSUPPORTED.
+ *  temperature, top_p, uniform  device float [num_rows]; top_k device int32 [num_rows].
+ */
+int pa_sample(int32_t* tokens, const void* logits, int64_t row_stride, int num_rows,
+              int vocab_size, const float* temperature, const int32_t* top_k,
+              const float* top_p, const float* uniform, pa_dtype dtype, hipStream_t stream);
+
 /* Human-readable name of a pa_status value (static storage). */
 const char* pa_status_string(int status);
 

@@ -24,7 +24,8 @@ Readings where the pages are silent (listed with the design notes):
   token, in vocabulary order, whose cumulative probability exceeds u (the
   inverse of the distribution function): a sampler that is deterministic
   given u, so it can be compared draw by draw.
-* NaN logits count as -inf.  A row with no finite logit returns -1.
+* NaN logits count as -inf; tokens with +inf logits share all the
+  probability equally.  A row with no finite logit returns -1.
 """
 from __future__ import annotations
 
@@ -43,7 +44,10 @@ def probabilities(logits, temperature: float, top_k: int, top_p: float) -> np.nd
     live = z > -np.inf
     if not live.any():
         return np.zeros(v)
-    w = np.where(live, np.exp(z - z[live].max()), 0.0)
+    if np.isposinf(z).any():
+        w = np.isposinf(z).astype(np.float64)
+    else:
+        w = np.where(live, np.exp(z - z[live].max()), 0.0)
     keep = live.copy()
     if 0 < top_k < v:
         kth = np.sort(z)[::-1][top_k - 1]

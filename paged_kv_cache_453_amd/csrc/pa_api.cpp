@@ -392,4 +392,27 @@ int pa_swap_blocks(const void* src_key, const void* src_value, void* dst_key, vo
   return PA_OK;
 }
 
+int pa_sample(int32_t* tokens, const void* logits, int64_t row_stride, int num_rows,
+              int vocab_size, const float* temperature, const int32_t* top_k,
+              const float* top_p, const float* uniform, pa_dtype dtype, hipStream_t stream) {
+  if (num_rows < 0) return PA_ERR_SHAPE;
+  if (num_rows > 0 && (!tokens || !logits || !temperature || !top_k || !top_p || !uniform))
+    return PA_ERR_NULL;
+  if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
+  if (vocab_size < 1 || row_stride < vocab_size) return PA_ERR_SHAPE;
+  if (vocab_size > pa::kMaxSampleVocab) return PA_ERR_UNSUPPORTED;
+  if (num_rows == 0) return PA_OK;
+  pa::SampleArgs a;
+  a.logits = logits;
+  a.row_stride = row_stride;
+  a.vocab = vocab_size;
+  a.num_rows = num_rows;
+  a.temperature = temperature;
+  a.top_k = top_k;
+  a.top_p = top_p;
+  a.uniform = uniform;
+  a.tokens = tokens;
+  return status_of(pa::launch_sample(a, dtype == PA_BF16, stream));
+}
+
 }  // extern "C"

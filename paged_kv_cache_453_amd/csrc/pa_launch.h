@@ -63,6 +63,20 @@ struct ReduceArgs {
   int max_context_len;
 };
 
+// Next-token sampling, one row of logits per workgroup.
+constexpr int kMaxSampleVocab = 36864;   // the row lives in LDS
+struct SampleArgs {
+  const void* logits;      // [num_rows, row_stride], fp32 or bf16
+  int64_t row_stride;      // elements between rows
+  int vocab;
+  int num_rows;
+  const float* temperature;
+  const int32_t* top_k;
+  const float* top_p;
+  const float* uniform;    // one draw in [0, 1) per row
+  int32_t* tokens;
+};
+
 // Pools a batch of whole-block moves reads from and writes to (K and V alike).
 struct BlockPools {
   const void* src_k;
@@ -95,6 +109,7 @@ hipError_t launch_copy_blocks(const BlockPools& pools, const int32_t* block_mapp
                               hipStream_t stream);
 hipError_t launch_swap_blocks(const BlockPools& pools, const int32_t* host_pairs,
                               hipStream_t stream);
+hipError_t launch_sample(const SampleArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_prefill_mfma(const DecodeArgs& a, int head_dim, hipStream_t stream);
 
 }  // namespace pa

@@ -82,6 +82,8 @@ def load() -> ctypes.CDLL:
     lib.pa_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64,
                                   i32, f32, f32, f32, i32, vp, sz, i32, vp]
     lib.pa_decode_fp8.restype = i32
+    lib.pa_sample.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp, vp, i32, vp]
+    lib.pa_sample.restype = i32
     lib.pa_copy_blocks.argtypes = [vp, vp, vp, i64, i32, i32, i32, i64, i32, vp]
     lib.pa_copy_blocks.restype = i32
     lib.pa_swap_blocks.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, vp]
@@ -119,7 +121,7 @@ def load() -> ctypes.CDLL:
 
 EXPORTED = ("pa_reshape_and_cache", "pa_decode_workspace_bytes", "pa_decode",
             "pa_decode_splitk_reduce", "pa_prefill_chunk", "pa_reshape_and_cache_fp8",
-            "pa_decode_fp8", "pa_copy_blocks", "pa_swap_blocks", "pa_status_string")
+            "pa_decode_fp8", "pa_sample", "pa_copy_blocks", "pa_swap_blocks", "pa_status_string")
 
 
 # --------------------------------------------------------------------------
@@ -319,6 +321,27 @@ def pa_decode_fp8(out, query, key_cache, value_cache, block_tables, context_lens
         _ptr(context_lens), _ptr(shared_prefix_blocks), s, hq, hkv, d, bs, block_tables.shape[1],
         nb, int(max_context_len), float(scale), float(k_scale), float(v_scale),
         int(partition_size), ws_ptr, ws_bytes, _dtype_code(query), _stream(stream)))
+
+
+# --------------------------------------------------------------------------
+# next-token sampling
+# --------------------------------------------------------------------------
+def pa_sample(tokens, logits, temperature, top_k, top_p, uniform, stream=None) -> None:
+    """tokens int32 [S]; logits [S, V] fp32/bf16 (row stride may exceed V); temperature,
+    top_p, uniform float32 [S]; top_k int32 [S] -- all on the GPU."""
+    torch = _torch()
+    lib = load()
+    _on_gpu(tokens, temperature, top_k, top_p, uniform)
+    _need(logits.is_cuda and logits.dim() == 2 and logits.stride(1) == 1,
+          "logits must be a [S, V] GPU tensor with contiguous rows")
+    s, v = logits.shape
+    _need(tokens.dtype == torch.int32 and tokens.numel() == s, "tokens must be int32 [S]")
+    _need(top_k.dtype == torch.int32 and top_k.numel() == s, "top_k must be int32 [S]")
+    for t in (temperature, top_p, uniform):
+        _need(t.dtype == torch.float32 and t.numel() == s, "per-row parameters must be float32 [S]")
+    _check("pa_sample", lib.pa_sample(
+        _ptr(tokens), _ptr(logits), logits.stride(0), s, v, _ptr(temperature), _ptr(top_k),
+        _ptr(top_p), _ptr(uniform), _dtype_code(logits), _stream(stream)))
 
 
 # --------------------------------------------------------------------------

@@ -215,3 +215,24 @@ def test_fp8_validation(lib):
     assert dec(hq=32, hkv=4, d=64) == PA_ERR_UNSUPPORTED          # bf16 but head_dim 64
     assert dec(dtype=2) == PA_ERR_UNSUPPORTED                     # the query is fp32 or bf16
     assert dec(S=0) == PA_OK
+
+
+def test_sample_validation(lib):
+    f = lib.pa_sample
+    base = [P, P, 32000, 4, 32000, P, P, P, P, F32, None]
+
+    def call(**kw):
+        a = list(base)
+        idx = dict(tok=0, stride=2, S=3, V=4, temp=5, dtype=9)
+        for k, v in kw.items():
+            a[idx[k]] = v
+        return f(*a)
+
+    assert call(tok=None) == PA_ERR_NULL
+    assert call(temp=None) == PA_ERR_NULL
+    assert call(S=-1) == PA_ERR_SHAPE
+    assert call(V=0) == PA_ERR_SHAPE
+    assert call(stride=100) == PA_ERR_SHAPE                   # rows overlap
+    assert call(V=40000, stride=40000) == PA_ERR_UNSUPPORTED  # beyond the LDS row
+    assert call(dtype=2) == PA_ERR_UNSUPPORTED
+    assert call(S=0, tok=None) == PA_OK

@@ -74,6 +74,8 @@ def test_closed_forms():
     np.testing.assert_allclose(sampler.probabilities(flat, 1.0, 3, 1.0), np.full(10, 0.1))
     assert sampler.sample([-np.inf, np.nan, -np.inf], 1.0, 0, 1.0, 0.5) == -1
     assert sampler.sample([-np.inf, 2.0, np.nan], 1.0, 0, 1.0, 0.5) == 1
+    np.testing.assert_array_equal(sampler.probabilities([np.inf, 3.0, np.inf], 1.0, 0, 1.0),
+                                  [0.5, 0.0, 0.5])
 
 
 def test_inverse_distribution_function():

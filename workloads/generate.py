@@ -168,6 +168,32 @@ def fp8_pools(w: "Workload", seed: int):
 
 
 # --------------------------------------------------------------------------
+# next-token sampling inputs
+# --------------------------------------------------------------------------
+# (temperature, top_k, top_p): the pages' example first, then a spread
+SAMPLER_PARAMS = [(0.7, 50, 0.9), (1.0, 0, 1.0), (0.5, 1, 1.0), (1.2, 1000, 0.8),
+                  (0.9, 0, 0.5), (2.0, 32000, 0.99), (0.3, 20, 1.0), (1.0, 40, 0.95)]
+
+
+def sampler_inputs(num_rows: int, vocab: int, seed: int):
+    """Logits shaped like a language model's: N(0, 1.5) over the vocabulary plus
+    a few strong candidates per row (N(6, 1.5) on 8 random tokens); per-row
+    parameters cycling through SAMPLER_PARAMS; one uniform draw in [0, 1) per
+    row.  Returns (logits fp32 [S, V], temperature f32, top_k i32, top_p f32, u f32)."""
+    rng = np.random.default_rng(seed)
+    logits = rng.normal(0.0, 1.5, (num_rows, vocab)).astype(np.float32)
+    for r in range(num_rows):
+        hot = rng.choice(vocab, size=min(8, vocab), replace=False)
+        logits[r, hot] = rng.normal(6.0, 1.5, hot.size).astype(np.float32)
+    par = [SAMPLER_PARAMS[r % len(SAMPLER_PARAMS)] for r in range(num_rows)]
+    temperature = np.array([p[0] for p in par], dtype=np.float32)
+    top_k = np.array([p[1] for p in par], dtype=np.int32)
+    top_p = np.array([p[2] for p in par], dtype=np.float32)
+    u = rng.random(num_rows).astype(np.float32)
+    return logits, temperature, top_k, top_p, u
+
+
+# --------------------------------------------------------------------------
 # the workload record
 # --------------------------------------------------------------------------
 @dataclass
