@@ -22,6 +22,9 @@ shuffled pool) with split-K partitions and their merge.
             all 32 with prefix-cache hits (256 query tokens each over the
             cached 2048) against the same prompts prefilled whole, and the
             block manager's host time to look the prompts up
+  sampler   the next-token draw for 256 rows of a 32000-token vocabulary (Llama 2),
+            fp32 logits, temperature / top-k / top-p cycling through the
+            pages' example (0.7, 50, 0.9) and other settings
   block_moves  the data movement around the step at the Llama-2-13B pool shape:
             copy-on-write block copies (pa_copy_blocks, 1024 pairs in one call;
             the metric of that line is its read + write GB/s), swaps to and
@@ -274,7 +277,9 @@ class StepTimer:
 
 
 WORKLOADS = ("llama13b", "llama7b", "gqa", "mixed", "llama13b_fp8", "gqa_fp8", "prefix_cache",
-             "block_moves")
+             "sampler", "block_moves")
+SAMPLER_BUFFERS = 9
+SAMPLER_METRIC = "next-token sampling rows/s (temperature + top-k + top-p + draw), 32000-token vocabulary"
 PREFIX_METRIC = ("prefill us for 32 prompts sharing a 2048-token system prompt, with prefix-cache "
                  "hits, at Llama-2-13B shape")
 COPY_METRIC = "paged KV block copy GB/s (copy-on-write, read + write bytes) at Llama-2-13B pool shape"
@@ -531,6 +536,70 @@ def prefix_cpu_baseline(d: int, hq: int, own: int, total: int, n: int = 32):
                       f"{total} tokens of context, {hq} heads ({t:.2f} s), times {n} prompts"}
 
 
+def bench_sampler(args, torch, dev, lib, timer) -> int:
+    """pa_sample over 256 rows of 32000 fp32 logits."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from workloads import sampler_inputs
+
+    s, v = 256, 32000
+    logits, t, k, p, u = sampler_inputs(s, v, 453)
+    f = lambda a: torch.from_numpy(np.asarray(a)).to(dev)
+    # Launches cycle through SAMPLER_BUFFERS distinct logits batches (295 MB in
+    # all, more than the GPU's 256 MB last-level cache), so that every launch
+    # reads its logits from HBM.
+    host = [logits] + [sampler_inputs(s, v, 453 + i)[0] for i in range(1, SAMPLER_BUFFERS)]
+    lgs = [f(x) for x in host]
+    tt, kk, pp, uu = f(t), f(k), f(p), f(u)
+    tok = torch.empty(s, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    turn = [0]
+
+    def run():
+        lib.pa_sample(tok, lgs[turn[0] % SAMPLER_BUFFERS], tt, kk, pp, uu, stream=stream)
+        turn[0] += 1
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    log(f"bench: timing {args.steps} sampler launches")
+    ms = timer.per_launch([("sample", run)], args.steps, stream)["sample"]
+    algo = s * v * 4 + s * 20                        # logits, per-row parameters and the token
+    gbs = algo / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle.sampler as osamp
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            rows = 0
+            while rows < s * SAMPLER_BUFFERS and time.perf_counter() - t0 < 10.0:
+                r = rows % s
+                osamp.sample(host[rows // s][r], float(t[r]), int(k[r]), float(p[r]), float(u[r]))
+                rows += 1
+            el = time.perf_counter() - t0
+        cpu = {"value": round(rows / el, 1), "unit": "rows/s", "cores": 1, "kind": "oracle",
+               "sample": f"reference sampler (numpy float64, sorts the row) on the first {rows} "
+                         f"rows of the {SAMPLER_BUFFERS} logits batches, {el:.2f} s, one thread"}
+    result = {
+        "metric": SAMPLER_METRIC, "value": round(s / (ms * 1e-3), 1), "unit": "rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "256 rows x 32000 fp32 logits, N(0, 1.5) plus 8 strong "
+                               "candidates per row; (temperature, top_k, top_p) cycling through "
+                               "the pages' (0.7, 50, 0.9) and 7 other settings", "seed": 453,
+                   "logits_batches": SAMPLER_BUFFERS},
+        "us_per_launch": round(ms * 1e3, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "sample_kernel<float, 32>", "algorithmic_bytes_per_launch": int(algo)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -574,6 +643,8 @@ def main(argv=None):
         return bench_block_moves(args, torch, dev, lib, StepTimer(torch))
     if args.workload == "prefix_cache":
         return bench_prefix_cache(args, torch, dev, lib, StepTimer(torch))
+    if args.workload == "sampler":
+        return bench_sampler(args, torch, dev, lib, StepTimer(torch))
     fp8 = args.workload.endswith("_fp8")
     base = args.workload[:-len("_fp8")] if fp8 else args.workload
     if ps is None:

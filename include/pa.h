@@ -425,15 +425,16 @@ int64_t pa_bm_num_cached_blocks(const pa_block_manager* bm);
  * it is below top_p[r] (top_p[r] = 1 keeps all).  tokens[r] is the first token,
  * in vocabulary order, at which the cumulative probability of what stayed
  * exceeds uniform[r]: the inverse of the distribution function, so the draw is
- * a deterministic function of the caller's uniform number.  Weights are kept
- * in fixed point with 40 fraction bits (64-bit integer sums, exact in any
- * order), so probabilities below about 1e-12 of the largest count as zero.
+ * a deterministic function of the caller's uniform number.  Weights
+ * exp(z - max z) are kept in fixed point with 32 fraction bits (64-bit integer
+ * sums, exact in any order): a token more than 2^32 times less likely than
+ * the most likely one counts as probability zero and takes no part in top-k.
  *
  *  tokens       device int32 [num_rows]: the drawn token, or -1 for a row with
  *               no finite logit or out-of-range parameters (temperature <= 0,
  *               top_p outside (0, 1], uniform outside [0, 1)).
  *  logits       device [num_rows, row_stride], dtype fp32 or bf16; vocab_size
- *               <= 36864 (the row is staged in LDS), else PA_ERR_UNSUPPORTED.
+ *               <= 32768 (the row is held in registers), else PA_ERR_UNSUPPORTED.
  *  temperature, top_p, uniform  device float [num_rows]; top_k device int32 [num_rows].
  */
 int pa_sample(int32_t* tokens, const void* logits, int64_t row_stride, int num_rows,

@@ -64,7 +64,7 @@ struct ReduceArgs {
 };
 
 // Next-token sampling, one row of logits per workgroup.
-constexpr int kMaxSampleVocab = 36864;   // the row lives in LDS
+constexpr int kMaxSampleVocab = 32768;   // 32 tokens in registers per thread of 1024
 struct SampleArgs {
   const void* logits;      // [num_rows, row_stride], fp32 or bf16
   int64_t row_stride;      // elements between rows
