@@ -120,7 +120,46 @@ def test_edge_cases(gpu):
     assert one.tolist() == [0]                                      # a vocabulary of one
 
 
-def test_rejects_vocabularies_beyond_the_lds_row(gpu):
+def test_gathered_list_overflow_falls_back_to_the_row(gpu):
+    """Rows whose radix buckets hold more tokens than one wave's share of the
+    LDS list: the remaining digits go over the whole row again."""
+    say("sampler: list overflow fallbacks")
+    v = 32000
+    rng = np.random.default_rng(94)
+    rows, params = [], []
+    flat = np.zeros(v, dtype=np.float32)
+    for u in (0.0, 0.37, 0.999):
+        rows.append(flat)
+        params.append((1.0, 5, 1.0, u))           # top-k bucket = the whole row, all tied
+        rows.append(flat)
+        params.append((1.0, 0, 0.3, u))           # top-p over a flat row
+        rows.append(flat)
+        params.append((1.0, 7, 0.5, u))           # top-k then top-p, nothing gathered in full
+    crowd = rng.normal(0, 1.5, v).astype(np.float32)
+    crowd[:2048] += 8.0                            # the top 1500 all in the first wave's span
+    for u in (0.11, 0.52, 0.93):
+        rows.append(crowd)
+        params.append((1.0, 1500, 0.8, u))
+        rows.append(crowd)
+        params.append((0.7, 1500, 1.0, u))
+    bf = np.round(rng.normal(0, 1.5, v) * 4).astype(np.float32) / 4   # many exact ties
+    for k, p in ((3000, 0.9), (0, 0.95), (40, 1.0)):
+        rows.append(bf)
+        params.append((1.0, k, p, 0.61))
+    x = np.stack(rows)
+    t, k, p, u = (np.array(c) for c in zip(*params))
+    t, p, u = (c.astype(np.float32) for c in (t, p, u))   # what the GPU receives
+    got = run(gpu, x, t, k, p, u)
+    exact = 0
+    for r in range(len(got)):
+        want = sampler.sample(x[r].astype(np.float64), float(t[r]), int(k[r]), float(p[r]), float(u[r]))
+        exact += int(got[r] == want)
+        assert got[r] in admissible(x[r].astype(np.float64), float(t[r]), int(k[r]), float(p[r]),
+                                    float(u[r])), (r, got[r], want)
+    assert exact >= len(got) - 1
+
+
+def test_rejects_vocabularies_beyond_the_register_row(gpu):
     import torch
     lg = torch.zeros((1, 40000), device="cuda")
     one = torch.ones(1, device="cuda")
