@@ -243,20 +243,30 @@ class StepTimer:
         self.torch = torch
 
     def per_step(self, step, steps: int, streams) -> float:
-        """Milliseconds per step of `step()` over `steps` calls, all streams joined."""
+        """Milliseconds per step of `step()` over `steps` calls, all streams joined.
+        Events between the steps (on the first stream) also give each step's own
+        time; their 10th, 50th and 90th percentiles are kept in `self.spread`."""
         torch = self.torch
         main = streams[0]
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         a.record(main)
-        for _ in range(steps):
+        for i in range(steps):
             step()
+            if len(streams) == 1:
+                marks[i].record(main)
         for s in streams[1:]:
             e = torch.cuda.Event()
             e.record(s)
             main.wait_event(e)
         b.record(main)
         torch.cuda.synchronize()
+        if len(streams) == 1:
+            each = sorted([a.elapsed_time(marks[0])] +
+                          [marks[i - 1].elapsed_time(marks[i]) for i in range(1, steps)])
+            pick = lambda q: each[min(len(each) - 1, int(q * len(each)))]
+            self.spread = [round(pick(0.1), 5), round(pick(0.5), 5), round(pick(0.9), 5)]
         return a.elapsed_time(b) / steps
 
     def per_launch(self, launches, steps: int, stream):
@@ -815,6 +825,7 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step_p10_p50_p90": timer.spread,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
