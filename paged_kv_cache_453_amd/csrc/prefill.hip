@@ -22,13 +22,16 @@
 // reduction slots of a lane pair key groups {4g..4g+3} and {16+4g..16+4g+3} of
 // a 32-key step; any order works if V uses the same one).
 //  - K (A operand, key r in row r) is read from LDS with one 16-byte read per
-//    lane and k-step: chunk 4ks+g of key row r.  Rows are padded by 16 bytes,
-//    so the 16 lanes reading one column of 16 rows hit distinct banks.
-//  - V (A operand of O^T = V^T P^T) stays row-major too: row r of d-tile t
-//    stands for column D/16*r + t, so lane (r, g) reads columns
-//    D/16*r .. D/16*(r+1)-1 of its 8 key rows (contiguous across the 16 lanes
-//    of a group) and takes element t of each as its operand for tile t -- a
-//    register-local repack instead of a transposed copy.
+//    lane and k-step: chunk 4ks+g of key row r.  K rows are padded by 16
+//    bytes, so the 16 lanes reading one column of 16 rows hit distinct banks.
+//  - V (A operand of O^T = V^T P^T, row r of d-tile t = column 16t + r) stays
+//    row-major too and is read with the LDS transpose read (ds_read_b64_tr_b16):
+//    in each group of 16 lanes, lane r receives element r & 3 of the 8-byte
+//    pieces that lanes 4k + (r >> 2) address, k = 0..3.  So lanes 4k + q of
+//    group g address columns 16t + 4q .. 16t + 4q + 3 of the key at position
+//    8g + k, and lane r gets that key's column 16t + r for four keys at once;
+//    two such reads give its 8 keys.  V rows are padded by 32 bytes, so the
+//    eight rows of a half-wave's read cover the banks once.
 //
 // Softmax in base 2 with lazy rescaling: a row's reference max moves only when
 // a tile's max exceeds it by more than 8, so the accumulators are rarely
@@ -57,31 +60,14 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(const u32x4& a, const u32x4& b, c
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Column data of one key row as a lane holds it: 8 bf16 (D = 128) or 4 (D = 64).
-template <int D>
-struct VRow;
-template <>
-struct VRow<128> {
-  typedef u32x4 type;
-};
-template <>
-struct VRow<64> {
-  typedef u32x2 type;
-};
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-// bf16 element T of lo_src and hi_src packed as (hi << 16) | lo.
-template <int T, typename V>
-__device__ __forceinline__ uint32_t pick_pair(const V& lo_src, const V& hi_src) {
-  const uint32_t sel = (T & 1) ? 0x07060302u : 0x05040100u;
-  const uint32_t lo = lo_src[T / 2];
-  const uint32_t hi = hi_src[T / 2];
-  return __builtin_amdgcn_perm(hi, lo, sel);
-}
-
-template <int D, int T>
-__device__ __forceinline__ u32x4 v_operand(const typename VRow<D>::type (&vr)[8]) {
-  return u32x4{pick_pair<T>(vr[0], vr[1]), pick_pair<T>(vr[2], vr[3]),
-               pick_pair<T>(vr[4], vr[5]), pick_pair<T>(vr[6], vr[7])};
+// LDS transpose read of 8 bytes (four bf16) at byte offset `off` of `base`.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* base, int off) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)((__attribute__((address_space(3))) const uint8_t*)base + off));
+  return __builtin_bit_cast(u32x2, v);
 }
 
 }  // namespace
@@ -92,13 +78,13 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
   constexpr int DT = D / 16;            // d-tiles of the output (= columns per lane per key)
   constexpr int QB = RW / 16;           // 16-row query blocks per wave
   constexpr int QT = 4 * RW;            // query rows per workgroup
-  constexpr int ROW = D * 2 + 16;       // padded LDS row, bytes
+  constexpr int ROW = D * 2 + 16;       // padded LDS row of K, bytes
+  constexpr int ROWV = D * 2 + 32;      // padded LDS row of V, bytes
   constexpr int CH = D / 8;             // 16-byte chunks per row
   constexpr int KPP = 256 / CH;         // key rows staged per pass of the workgroup
   constexpr int NPASS = kKeys / KPP;    // staging passes per tile
-  constexpr int TILE = kKeys * ROW;
-  typedef typename VRow<D>::type vrow_t;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2][2][TILE];   // [buffer][K, V]
+  constexpr int TILE = kKeys * (ROW + ROWV);   // K rows, then V rows
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2][TILE];   // [buffer]
   __shared__ int sh_bad;
 
   const int qtile = gridDim.x - 1 - blockIdx.x;   // later (longer) tiles first
@@ -203,9 +189,9 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
   const auto stage_store = [&](int buf) {
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
-      const int off = (kr0 + KPP * p) * ROW + cc * 16;
-      *reinterpret_cast<u32x4*>(&smem[buf][0][off]) = kst[p];
-      *reinterpret_cast<u32x4*>(&smem[buf][1][off]) = vst[p];
+      const int kr = kr0 + KPP * p;
+      *reinterpret_cast<u32x4*>(&smem[buf][kr * ROW + cc * 16]) = kst[p];
+      *reinterpret_cast<u32x4*>(&smem[buf][kKeys * ROW + kr * ROWV + cc * 16]) = vst[p];
     }
   };
 
@@ -233,8 +219,8 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
 
     const int tile_first = kt * kKeys;
     if (wave_rows > 0 && tile_first <= wave_last_pos) {
-      const uint8_t* kb = smem[kt & 1][0];
-      const uint8_t* vb = smem[kt & 1][1];
+      const uint8_t* kb = smem[kt & 1];
+      const uint8_t* vb = smem[kt & 1] + kKeys * ROW;
       const bool need_mask = tile_first + kKeys - 1 > wave_first_pos;
 
       // ---- S^T = K Q^T: four 16-key groups ----
@@ -305,24 +291,16 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
       // ---- O^T += V^T P^T, 32 keys per step ----
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        vrow_t vr[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int key = 32 * kk + (j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4));
-          vr[j] = *reinterpret_cast<const vrow_t*>(vb + key * ROW + 2 * DT * r);
-        }
-        // all d-tile operands first, then the MFMAs back to back: building each
-        // operand right before its MFMA serialises on the operand registers
+        // positions 8g + k (k < 4) hold key 4g + k of the step, 8g + 4 + k key
+        // 16 + 4g + k, as in the weights' operand
+        const int vrow = 32 * kk + 4 * g + ((lane & 15) >> 2);
+        const int vcol = 2 * 4 * (lane & 3);
         u32x4 va[DT];
-        va[0] = v_operand<D, 0>(vr);
-        va[1] = v_operand<D, 1>(vr);
-        va[2] = v_operand<D, 2>(vr);
-        va[3] = v_operand<D, 3>(vr);
-        if constexpr (DT > 4) {
-          va[4] = v_operand<D, 4>(vr);
-          va[5] = v_operand<D, 5>(vr);
-          va[6] = v_operand<D, 6>(vr);
-          va[7] = v_operand<D, 7>(vr);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+          const u32x2 lo = lds_read_tr16(vb, vrow * ROWV + 32 * t + vcol);
+          const u32x2 hi = lds_read_tr16(vb, (vrow + 16) * ROWV + 32 * t + vcol);
+          va[t] = u32x4{lo[0], lo[1], hi[0], hi[1]};
         }
 #pragma unroll
         for (int t = 0; t < DT; ++t)
@@ -333,7 +311,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
     stage_store((kt + 1) & 1);
   }
 
-  // ---- normalise and store: lane holds O[row 16qb + r][DT*(4g+i) + t] ----
+  // ---- normalise and store: lane holds O[row 16qb + r][16t + 4g + i] ----
   lds_barrier();
   const bool poisoned = sh_bad != 0;
 #pragma unroll
@@ -344,16 +322,10 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
     const float inv = 1.f / l;
     bf16_t* dst = out + ((int64_t)(q0 + qi) * hq + h) * D;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t wv[DT / 2];
-#pragma unroll
-      for (int x = 0; x < DT / 2; ++x)
-        wv[x] = poisoned ? 0x7FC07FC0u
-                         : pack_bf16x2(o[qb][2 * x][i] * inv, o[qb][2 * x + 1][i] * inv);
-      if constexpr (DT == 8)
-        *reinterpret_cast<u32x4*>(dst + DT * (4 * g + i)) = u32x4{wv[0], wv[1], wv[2], wv[3]};
-      else
-        *reinterpret_cast<u32x2*>(dst + DT * (4 * g + i)) = u32x2{wv[0], wv[1]};
+    for (int t = 0; t < DT; ++t) {
+      const uint32_t lo = poisoned ? 0x7FC07FC0u : pack_bf16x2(o[qb][t][0] * inv, o[qb][t][1] * inv);
+      const uint32_t hi = poisoned ? 0x7FC07FC0u : pack_bf16x2(o[qb][t][2] * inv, o[qb][t][3] * inv);
+      *reinterpret_cast<u32x2*>(dst + 16 * t + 4 * g) = u32x2{lo, hi};
     }
   }
 }
