@@ -57,7 +57,8 @@ typedef enum {
   PA_ERR_NULL = -1,        /* a required pointer is NULL */
   PA_ERR_SHAPE = -2,       /* a size is negative, zero where it must not be, or inconsistent */
   PA_ERR_UNSUPPORTED = -3, /* block_size, head_dim, dtype or group size outside the supported set */
-  PA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than pa_decode_workspace_bytes() */
+  PA_ERR_WORKSPACE = -4,   /* workspace missing, smaller than pa_decode_workspace_bytes(), or
+                              not 16-byte aligned */
   PA_ERR_LAUNCH = -5,      /* the HIP runtime refused a kernel launch or a copy */
   PA_ERR_NO_BLOCKS = -6,   /* block manager: a pool has too few free blocks; nothing changed */
   PA_ERR_SEQ = -7,         /* block manager: unknown or duplicate sequence id, or the sequence
@@ -133,8 +134,8 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int 
  *  max_context_len an upper bound on context_lens (sizes the grid and the
  *                 workspace when partition_size > 0).  A sequence whose length
  *                 exceeds it, or exceeds max_blocks_per_seq * block_size, gets NaN.
- *  workspace      device buffer of at least pa_decode_workspace_bytes(); may be
- *                 NULL when partition_size == 0.
+ *  workspace      device buffer of at least pa_decode_workspace_bytes(), 16-byte
+ *                 aligned; may be NULL when partition_size == 0.
  */
 int pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
               const int32_t* block_tables, const int32_t* context_lens,
@@ -148,8 +149,9 @@ int pa_decode(void* out, const void* query, const void* key_cache, const void* v
  * pa_decode_splitk_reduce -- merge the partition results pa_decode left in the
  * workspace: with M = max_p lse_p and w_p = exp(lse_p - M),
  * out = sum_p w_p o_p / sum_p w_p.  Sequences with at most one partition are
- * left untouched (pa_decode wrote them).  Arguments must match the pa_decode
- * call that filled the workspace.
+ * left untouched (pa_decode wrote them); when max_context_len <= partition_size
+ * nothing is launched.  Arguments must match the pa_decode call that filled the
+ * workspace (16-byte aligned).
  */
 int pa_decode_splitk_reduce(void* out, const void* workspace, size_t workspace_bytes,
                             const int32_t* context_lens, int num_seqs, int num_heads,

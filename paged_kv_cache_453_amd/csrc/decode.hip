@@ -13,16 +13,17 @@ namespace pa {
 // Split-K merge: out = sum_p exp(lse_p - M) o_p / sum_p exp(lse_p - M).
 //
 // One wave per (sequence, head), four per workgroup.  A first pass takes the
-// max of the log-sum-exps with one partition per lane; then each lane owns
-// D/64 adjacent columns and walks the partitions, the weight of partition p
-// broadcast from the lane that computed it.  The partials of successive
-// partitions are independent loads, unrolled so that many are in flight --
-// the merge is a short stream over the workspace, not a chain of waits.
+// max of the log-sum-exps with one partition per lane.  Then the wave reads
+// four partitions per step: the lanes of quarter q take partition p0 + q and
+// 16-byte pieces of its row (D/16 columns a lane), so every step has 2 KB in
+// flight per wave (four steps unrolled), and the quarters' sums are added
+// across lanes at the end.
 constexpr int kReduceWaves = 4;
+constexpr int kReduceUnroll = 4;
 
 template <typename T, int D>
 __global__ __launch_bounds__(64 * kReduceWaves) void splitk_reduce_kernel(ReduceArgs a) {
-  constexpr int E = D / kWave;          // columns per lane
+  constexpr int E = D / 16;             // columns per lane
   const int row_sh = blockIdx.x * kReduceWaves + wave_uniform(threadIdx.x >> 6);
   if (row_sh >= a.num_seqs * a.num_heads) return;
   const int s = row_sh / a.num_heads;
@@ -45,32 +46,39 @@ __global__ __launch_bounds__(64 * kReduceWaves) void splitk_reduce_kernel(Reduce
   mm = xor_max_above<1>(mm);
   nan = __ballot(nan) != 0;
 
+  const int q = lane >> 4;              // this lane's partition within a step of four
+  const int col = (lane & 15) * E;
   float acc[E], wsum = 0.f;
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  const float* po = a.part_o + row * D + lane * E;
-  for (int p0 = 0; p0 < n; p0 += kWave) {
-    const float wl = p0 + lane < n ? expf(lse[p0 + lane] - mm) : 0.f;
-    wsum += wl;
-    const int cnt = min(kWave, n - p0);
-#pragma unroll 8
-    for (int t = 0; t < cnt; ++t) {
-      const float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), t));
-      const float* src = po + (int64_t)(p0 + t) * D;
-      if constexpr (E == 2) {
-        const float2 v = *reinterpret_cast<const float2*>(src);
-        acc[0] = fmaf(wt, v.x, acc[0]);
-        acc[1] = fmaf(wt, v.y, acc[1]);
-      } else {
-        acc[0] = fmaf(wt, src[0], acc[0]);
+  const float* po = a.part_o + row * D + col;
+  for (int p0 = 0; p0 < n; p0 += 4 * kReduceUnroll) {
+#pragma unroll
+    for (int u = 0; u < kReduceUnroll; ++u) {
+      const int p = p0 + 4 * u + q;
+      if (p < n) {
+        const float wt = expf(lse[p] - mm);
+        wsum += wt;
+        const f32x4* src = reinterpret_cast<const f32x4*>(po + (int64_t)p * D);
+#pragma unroll
+        for (int e4 = 0; e4 < E / 4; ++e4) {
+          const f32x4 v = src[e4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[4 * e4 + i] = fmaf(wt, v[i], acc[4 * e4 + i]);
+        }
       }
     }
   }
-  wsum = xor_sum_above<1>(wsum);
-  T* dst = static_cast<T*>(a.out) + (int64_t)row_sh * D + lane * E;
+  // add the four quarters (lanes l, l ^ 16, l ^ 32, l ^ 48)
 #pragma unroll
-  for (int e = 0; e < E; ++e)
-    dst[e] = ElemTraits<T>::from_f32(nan ? __builtin_nanf("") : acc[e] / wsum);
+  for (int e = 0; e < E; ++e) acc[e] = xor_sum_above<16>(acc[e]);
+  wsum = xor_sum_above<16>(wsum);
+  if (q == 0) {
+    T* dst = static_cast<T*>(a.out) + (int64_t)row_sh * D + col;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      dst[e] = ElemTraits<T>::from_f32(nan ? __builtin_nanf("") : acc[e] / wsum);
+  }
 }
 
 // Grouped-query decode with at least this many query heads per kv head runs on

@@ -31,6 +31,10 @@ int max_partitions(int max_context_len, int partition_size) {
 int status_of(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
 
 bool scale_ok(float s) { return s > 0.f && s < INFINITY; }
+// The split-K merge reads the partials in 16-byte pieces.
+bool workspace_ok(const void* ws, size_t bytes, size_t need) {
+  return ws && bytes >= need && (reinterpret_cast<uintptr_t>(ws) & 15) == 0;
+}
 
 // Shared by pa_decode and pa_decode_fp8: checks, then the kernel choice.
 int decode_impl(void* out, const void* query, const void* key_cache, const void* value_cache,
@@ -60,7 +64,7 @@ int decode_impl(void* out, const void* query, const void* key_cache, const void*
   if (partition_size > 0) {
     const size_t need = pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len,
                                                   partition_size);
-    if (num_seqs > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+    if (num_seqs > 0 && !workspace_ok(workspace, workspace_bytes, need)) return PA_ERR_WORKSPACE;
   }
   if (num_seqs == 0) return PA_OK;
   pa::DecodeArgs a = {};
@@ -102,7 +106,7 @@ const char* pa_status_string(int status) {
     case PA_ERR_NULL: return "null pointer argument";
     case PA_ERR_SHAPE: return "invalid or inconsistent size argument";
     case PA_ERR_UNSUPPORTED: return "unsupported block_size, head_dim, dtype or group size";
-    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_WORKSPACE: return "workspace missing, too small or not 16-byte aligned";
     case PA_ERR_LAUNCH: return "kernel launch or copy failed";
     case PA_ERR_NO_BLOCKS: return "not enough free blocks";
     case PA_ERR_SEQ: return "unknown or duplicate sequence, or wrong side of a swap";
@@ -229,9 +233,10 @@ int pa_decode_splitk_reduce(void* out, const void* workspace, size_t workspace_b
     return PA_ERR_SHAPE;
   const size_t need =
       pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, partition_size);
-  if (num_seqs > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+  if (num_seqs > 0 && !workspace_ok(workspace, workspace_bytes, need)) return PA_ERR_WORKSPACE;
   if (num_seqs == 0) return PA_OK;
   const int nparts = max_partitions(max_context_len, partition_size);
+  if (nparts <= 1) return PA_OK;   // every sequence has one partition: pa_decode wrote it
   const size_t rows = (size_t)num_seqs * num_heads * nparts;
   pa::ReduceArgs a;
   a.out = out;

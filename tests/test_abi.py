@@ -76,6 +76,7 @@ def test_decode_validation(lib):
     assert decode(lib, ps=16) == PA_ERR_WORKSPACE
     need = lib.pa_decode_workspace_bytes(4, 8, 128, 64, 16)
     assert decode(lib, ps=16, ws=P, wsb=need - 1) == PA_ERR_WORKSPACE
+    assert decode(lib, ps=16, ws=P + 4, wsb=need) == PA_ERR_WORKSPACE   # not 16-byte aligned
     assert decode(lib, S=0, out=None, query=None) == PA_OK      # nothing to do, nothing launched
 
 
@@ -100,6 +101,7 @@ def test_reduce_validation(lib):
     f = lib.pa_decode_splitk_reduce
     assert f(P, None, 0, P, 4, 8, 128, 64, 16, BF16, None) == PA_ERR_WORKSPACE
     assert f(P, P, 10, P, 4, 8, 128, 64, 16, BF16, None) == PA_ERR_WORKSPACE
+    assert f(P, P + 8, 1 << 30, P, 4, 8, 128, 64, 16, BF16, None) == PA_ERR_WORKSPACE
     assert f(P, P, 1 << 30, P, 4, 8, 128, 64, 0, BF16, None) == PA_ERR_SHAPE
     assert f(None, P, 1 << 30, P, 4, 8, 128, 64, 16, BF16, None) == PA_ERR_NULL
 
