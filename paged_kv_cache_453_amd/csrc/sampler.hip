@@ -26,14 +26,18 @@
 //    atomic instruction's lanes never meet on an address; then the tokens of
 //    the chosen bucket are gathered into LDS (a slice per wave, positions
 //    from the wave's ballot) and the remaining digits (8, 8, 4 bits) are
-//    resolved over them alone, in one small histogram (over the row again if
-//    a slice overflows).  Tokens tied with the K-th stay.  The select stops
-//    at the first digit whose bucket closes the count exactly.
+//    resolved over them alone, in one small histogram per level (over the row
+//    again if a slice overflows).  Tokens tied with the K-th stay.  The select
+//    stops at the first digit whose bucket closes the count exactly.
 //  - Top-p: the largest rank t whose mass {rank >= t} reaches P times the
 //    top-k mass, by the same select with 64-bit mass histograms; the top-k
 //    mass is the total of its first histogram.  Every token at or above it is
-//    one whose strictly-more-probable mass is below P.
-//  - Draw: a scan of the wave masses locates floor(u * total) in a wave; that
+//    one whose strictly-more-probable mass is below P.  When a top-p follows
+//    a top-k whose bucket and everything above it are at most kGatherAll
+//    tokens, the top-k gather takes all of them, and the top-p select then
+//    runs over the list alone.
+//  - Draw: a scan of the wave masses (from the list when it holds every kept
+//    token, else from the registers) locates floor(u * total) in a wave; that
 //    wave scans its rows (DPP lane moves) to the lane whose group holds it,
 //    and the lane walks the group to the token: the inverse of the
 //    distribution function.
