@@ -68,6 +68,22 @@ def test_draws_match_the_oracle(gpu, dtype, vocab):
     assert exact >= len(got) - 1
 
 
+def test_the_benchmark_batch(gpu):
+    """The sampler bench's first logits batch: 256 rows x 32000, every row."""
+    say("sampler: 256 x 32000 benchmark batch")
+    logits, t, k, p, u = sampler_inputs(256, 32000, 453)
+    got = run(gpu, logits, t, k, p, u)
+    x = logits.astype(np.float64)
+    exact = 0
+    for r in range(len(got)):
+        want = sampler.sample(x[r], float(t[r]), int(k[r]), float(p[r]), float(u[r]))
+        if got[r] == want:
+            exact += 1
+        else:
+            assert got[r] in admissible(x[r], float(t[r]), int(k[r]), float(p[r]), float(u[r])), r
+    assert exact >= len(got) - 2
+
+
 def test_uniform_grid_reproduces_the_distribution(gpu):
     """The pages' parameters (0.7, 50, 0.9) on one row, u on a grid of 8192 points."""
     say("sampler: uniform grid")
