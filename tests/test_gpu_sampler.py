@@ -53,12 +53,17 @@ def admissible(x, t, k, p, u):
     return out
 
 
-@pytest.mark.parametrize("dtype,vocab", [("f32", 32000), ("bf16", 32000), ("f32", 1000),
-                                         ("f32", 32768), ("bf16", 7)])
-def test_draws_match_the_oracle(gpu, dtype, vocab):
-    say(f"sampler {dtype} vocab={vocab}")
+@pytest.mark.parametrize("dtype,vocab,stride", [
+    ("f32", 32000, None), ("bf16", 32000, None), ("f32", 1000, None), ("f32", 32768, None),
+    ("bf16", 7, None),
+    ("f32", 31999, None),      # the last 16-byte group of a row is partial
+    ("bf16", 16387, None),     # 16 tokens a thread, a partial last group
+    ("f32", 4093, 4093),       # rows 4 bytes apart from 16-byte alignment: no vector loads
+    ("bf16", 30001, 30005)])
+def test_draws_match_the_oracle(gpu, dtype, vocab, stride):
+    say(f"sampler {dtype} vocab={vocab} stride={stride}")
     logits, t, k, p, u = sampler_inputs(48, vocab, 91)
-    got = run(gpu, logits, t, k, p, u, dtype)
+    got = run(gpu, logits, t, k, p, u, dtype, stride=stride)
     x = storage_values(logits, dtype)
     exact = 0
     for r in range(len(got)):
