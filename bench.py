@@ -30,6 +30,9 @@ shuffled pool) with split-K partitions and their merge.
             the metric of that line is its read + write GB/s), swaps to and
             from pinned host memory (pa_swap_blocks), and the native block
             manager's host time for one decode step of 256 sequences
+  stream_read  the part's achievable HBM read rate: plain 16-byte loads over a
+            4 GiB buffer (pa_stream_read), the ceiling the HBM-bound kernels
+            are compared with; the default line reports it too
 
 Inputs are seeded synthetic data already resident in GPU memory before timing
 starts.  Prints one JSON line: KV GB/s over the whole step (the metric), % of
@@ -286,8 +289,10 @@ class StepTimer:
                 for k, (name, _) in enumerate(launches)}
 
 
+STREAM_BYTES = 4 << 30
+STREAM_METRIC = "achievable HBM read GB/s (plain 16-byte loads over a 4 GiB buffer)"
 WORKLOADS = ("llama13b", "llama7b", "gqa", "mixed", "llama13b_fp8", "gqa_fp8", "prefix_cache",
-             "sampler", "block_moves")
+             "sampler", "block_moves", "stream_read")
 SAMPLER_BUFFERS = 9
 SAMPLER_METRIC = "next-token sampling rows/s (temperature + top-k + top-p + draw), 32000-token vocabulary"
 PREFIX_METRIC = ("prefill us for 32 prompts sharing a 2048-token system prompt, with prefix-cache "
@@ -314,6 +319,42 @@ def build_workload(name: str, ps: int):
         "prefill": "4 x 512-token causal chunks over paged prefixes U{0..3584}",
         "decode": "64 prompts x 3 samples sharing 2048-token prefixes + U{0..512} private",
         "seed": 457}
+
+
+def stream_read_gbs(torch, dev, lib, timer, launches: int = 20) -> float:
+    """The part's achievable read rate: pa_stream_read over a 4 GiB buffer
+    (GB/s, 1e9), the ceiling the HBM-bound kernels are compared with."""
+    buf = torch.ones(STREAM_BYTES // 4, dtype=torch.int32, device=dev)
+    sink = torch.empty(lib.pa_stream_read_sink_words(), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    run = lambda: lib.pa_stream_read(buf, sink, stream=stream)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    ms = timer.per_launch([("read", run)], launches, stream)["read"]
+    del buf
+    return STREAM_BYTES / (ms * 1e-3) / 1e9
+
+
+def bench_stream_read(args, torch, dev, lib, timer) -> int:
+    """The stream-read calibration as its own line."""
+    log(f"bench: timing {args.steps} stream-read launches over {STREAM_BYTES >> 30} GiB")
+    gbs = stream_read_gbs(torch, dev, lib, timer, args.steps)
+    ms = STREAM_BYTES / gbs / 1e6
+    result = {
+        "metric": STREAM_METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": 3, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u32", "data": "synthetic",
+        "config": {"workload": "read of a 4 GiB device buffer, nontemporal 16-byte loads, "
+                               "grid-stride, a 32-bit fold per workgroup"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "stream_read_kernel", "algorithmic_bytes_per_launch": STREAM_BYTES},
+        "cpu_baseline": None,
+        "cpu_baseline_note": "a calibration of the GPU's memory, with no CPU counterpart",
+    }
+    print(json.dumps(result), flush=True)
+    return 0
 
 
 def bench_block_moves(args, torch, dev, lib, timer) -> int:
@@ -656,6 +697,8 @@ def main(argv=None):
         return bench_prefix_cache(args, torch, dev, lib, StepTimer(torch))
     if args.workload == "sampler":
         return bench_sampler(args, torch, dev, lib, StepTimer(torch))
+    if args.workload == "stream_read":
+        return bench_stream_read(args, torch, dev, lib, StepTimer(torch))
     fp8 = args.workload.endswith("_fp8")
     base = args.workload[:-len("_fp8")] if fp8 else args.workload
     if ps is None:
@@ -846,6 +889,11 @@ def main(argv=None):
         "cpu_baseline": cpu,
     }
     result.update(extra)
+    if args.workload == "llama13b":
+        # the part's achievable read rate, beside the 8 TB/s peak the roofline uses
+        read = stream_read_gbs(torch, dev, lib, timer)
+        result["achievable_read_gbs"] = round(read, 2)
+        result["decode_pct_of_achievable_read"] = round(100.0 * decode_gbs / read, 2)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -443,6 +443,23 @@ int pa_sample(int32_t* tokens, const void* logits, int64_t row_stride, int num_r
               int vocab_size, const float* temperature, const int32_t* top_k,
               const float* top_p, const float* uniform, pa_dtype dtype, hipStream_t stream);
 
+/*
+ * Measurement aid (not an operation of the method): the HBM read rate this
+ * part reaches with plain, fully coalesced 16-byte loads, the ceiling the
+ * decode kernels -- bound by HBM reads (xdnf.cn article, section 六.5) -- are
+ * compared with.
+ *
+ * pa_stream_read reads every byte of `buffer` once (nontemporal 16-byte
+ * loads, grid-stride) and writes pa_stream_read_sink_words() 32-bit words to
+ * `sink`, one per workgroup; their XOR equals the XOR of the buffer's 32-bit
+ * words.
+ *  buffer  device memory, 16-byte aligned; bytes a multiple of 16 (else
+ *          PA_ERR_SHAPE).  0 bytes writes zeros to the sink.
+ *  sink    device uint32 [pa_stream_read_sink_words()].
+ */
+int pa_stream_read_sink_words(void);
+int pa_stream_read(const void* buffer, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
 /* Human-readable name of a pa_status value (static storage). */
 const char* pa_status_string(int status);
 

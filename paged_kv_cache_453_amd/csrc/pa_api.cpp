@@ -420,4 +420,13 @@ int pa_sample(int32_t* tokens, const void* logits, int64_t row_stride, int num_r
   return status_of(pa::launch_sample(a, dtype == PA_BF16, stream));
 }
 
+int pa_stream_read_sink_words(void) { return pa::kStreamBlocks; }
+
+int pa_stream_read(const void* buffer, int64_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (bytes < 0 || bytes % 16 != 0) return PA_ERR_SHAPE;
+  if (!sink || (bytes > 0 && !buffer)) return PA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(buffer) & 15) != 0) return PA_ERR_SHAPE;
+  return status_of(pa::launch_stream_read(buffer, bytes, sink, stream));
+}
+
 }  // extern "C"

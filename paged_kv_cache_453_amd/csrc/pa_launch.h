@@ -110,6 +110,11 @@ hipError_t launch_copy_blocks(const BlockPools& pools, const int32_t* block_mapp
 hipError_t launch_swap_blocks(const BlockPools& pools, const int32_t* host_pairs,
                               hipStream_t stream);
 hipError_t launch_sample(const SampleArgs& a, bool bf16, hipStream_t stream);
+
+// Stream-read calibration: kStreamBlocks workgroups, one 32-bit fold each (the grid
+// and unroll that read fastest in a sweep of 1024..65536 workgroups x unroll 4..16).
+constexpr int kStreamBlocks = 32768;
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
 hipError_t launch_prefill_mfma(const DecodeArgs& a, int head_dim, hipStream_t stream);
 
 }  // namespace pa

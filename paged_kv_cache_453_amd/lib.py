@@ -88,6 +88,10 @@ def load() -> ctypes.CDLL:
     lib.pa_copy_blocks.restype = i32
     lib.pa_swap_blocks.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, vp]
     lib.pa_swap_blocks.restype = i32
+    lib.pa_stream_read_sink_words.argtypes = []
+    lib.pa_stream_read_sink_words.restype = i32
+    lib.pa_stream_read.argtypes = [vp, i64, vp, vp]
+    lib.pa_stream_read.restype = i32
     pp = ctypes.POINTER(ctypes.c_void_p)
     for name, args, res in (
             ("pa_bm_create", [i64, i64, i32, pp], i32),
@@ -121,7 +125,8 @@ def load() -> ctypes.CDLL:
 
 EXPORTED = ("pa_reshape_and_cache", "pa_decode_workspace_bytes", "pa_decode",
             "pa_decode_splitk_reduce", "pa_prefill_chunk", "pa_reshape_and_cache_fp8",
-            "pa_decode_fp8", "pa_sample", "pa_copy_blocks", "pa_swap_blocks", "pa_status_string")
+            "pa_decode_fp8", "pa_sample", "pa_copy_blocks", "pa_swap_blocks",
+            "pa_stream_read_sink_words", "pa_stream_read", "pa_status_string")
 
 
 # --------------------------------------------------------------------------
@@ -342,6 +347,25 @@ def pa_sample(tokens, logits, temperature, top_k, top_p, uniform, stream=None) -
     _check("pa_sample", lib.pa_sample(
         _ptr(tokens), _ptr(logits), logits.stride(0), s, v, _ptr(temperature), _ptr(top_k),
         _ptr(top_p), _ptr(uniform), _dtype_code(logits), _stream(stream)))
+
+
+def pa_stream_read_sink_words() -> int:
+    """Words of the sink pa_stream_read writes (one per workgroup)."""
+    return int(load().pa_stream_read_sink_words())
+
+
+def pa_stream_read(buffer, sink, stream=None) -> None:
+    """Read every byte of `buffer` (a contiguous GPU tensor, 16-byte aligned,
+    a multiple of 16 bytes) with plain 16-byte loads; `sink` is a GPU int32 or
+    uint32 tensor of pa_stream_read_sink_words() elements, which receives the
+    per-workgroup XOR folds.  A measurement aid, not an operation of the method."""
+    lib = load()
+    _on_gpu(buffer, sink)
+    _need(buffer.is_contiguous(), "buffer must be contiguous")
+    _need(sink.is_contiguous() and sink.element_size() == 4 and
+          sink.numel() >= lib.pa_stream_read_sink_words(), "sink too small")
+    nbytes = buffer.numel() * buffer.element_size()
+    _check("pa_stream_read", lib.pa_stream_read(_ptr(buffer), nbytes, _ptr(sink), _stream(stream)))
 
 
 # --------------------------------------------------------------------------

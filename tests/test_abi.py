@@ -238,3 +238,13 @@ def test_sample_validation(lib):
     assert call(V=40000, stride=40000) == PA_ERR_UNSUPPORTED  # beyond the LDS row
     assert call(dtype=2) == PA_ERR_UNSUPPORTED
     assert call(S=0, tok=None) == PA_OK
+
+
+def test_stream_read_validation(lib):
+    f = lib.pa_stream_read
+    assert lib.pa_stream_read_sink_words() > 0
+    assert f(P, 24, P, None) == PA_ERR_SHAPE          # not a multiple of 16 bytes
+    assert f(P, -16, P, None) == PA_ERR_SHAPE
+    assert f(P + 8, 16, P, None) == PA_ERR_SHAPE      # not 16-byte aligned
+    assert f(P, 16, None, None) == PA_ERR_NULL
+    assert f(None, 16, P, None) == PA_ERR_NULL
