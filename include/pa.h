@@ -229,6 +229,24 @@ int pa_decode_fp8(void* out, const void* query, const uint8_t* key_cache,
                   size_t workspace_bytes, pa_dtype dtype, hipStream_t stream);
 
 /*
+ * pa_prefill_chunk_fp8 -- pa_prefill_chunk over FP8 caches: causal attention
+ * of each sequence's chunk of new queries over its paged prefix and itself
+ * (xdnf.cn article, section 六.4), with K and V the values the codes stand for
+ * (code value times k_scale / v_scale), so that a step that mixes prefill
+ * chunks with decode runs on one FP8 cache.  query and out are bf16 (the
+ * matrix-core path; PA_ERR_UNSUPPORTED otherwise); accumulation is fp32.  The
+ * scales must be positive and finite (else PA_ERR_SHAPE).  Every other
+ * argument, and the NaN reporting of contract violations, as pa_prefill_chunk.
+ */
+int pa_prefill_chunk_fp8(void* out, const void* query, const uint8_t* key_cache,
+                         const uint8_t* value_cache, const int32_t* block_tables,
+                         const int32_t* query_start_loc, const int32_t* context_lens, int num_seqs,
+                         int num_query_tokens, int num_heads, int num_kv_heads, int head_dim,
+                         int block_size, int max_blocks_per_seq, int64_t num_blocks,
+                         int max_query_len, float scale, float k_scale, float v_scale,
+                         pa_dtype dtype, hipStream_t stream);
+
+/*
  * pa_copy_blocks -- copy whole physical blocks inside the K and V pools.
  *
  * For each pair (src, dst) = (block_mapping[2i], block_mapping[2i+1]) copies

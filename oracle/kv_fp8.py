@@ -111,3 +111,31 @@ def decode(query, k_pool, v_pool, block_tables, context_lens, scale, k_scale, v_
             kh = h // g
             out[s, h] = pa.attend(q64[s, h][None, :], ks[:, kh, :], vs[:, kh, :], scale)[0]
     return out
+
+
+def prefill(query, k_pool, v_pool, block_tables, query_start_loc, context_lens, scale, k_scale,
+            v_scale, query_dtype: str, block_size: int = 16) -> np.ndarray:
+    """Causal chunked prefill over an FP8 cache (xdnf.cn article, section 六.4):
+    sequence s's chunk of C new queries sits at the last C of its L cached
+    positions, and query i sees keys 0 .. L - C + i -- the plain definition on
+    the values the codes stand for.  Returns float64 [Tq, Hq, D]."""
+    tq, hq, d = query.shape
+    hkv = k_pool.shape[1]
+    g = hq // hkv
+    q64 = pa.to_f64(query, query_dtype)
+    out = np.zeros((tq, hq, d), dtype=np.float64)
+    for s in range(len(context_lens)):
+        a, b = int(query_start_loc[s]), int(query_start_loc[s + 1])
+        C, L = b - a, int(context_lens[s])
+        if C == 0:
+            continue
+        if C > L:
+            raise ValueError("chunk longer than the cached context")
+        ks = values(pa.gather(k_pool, block_tables[s], L, block_size), k_scale)
+        vs = values(pa.gather(v_pool, block_tables[s], L, block_size), v_scale)
+        pos = (L - C) + np.arange(C)
+        visible = np.arange(L)[None, :] <= pos[:, None]
+        for h in range(hq):
+            kh = h // g
+            out[a:b, h] = pa.attend(q64[a:b, h, :], ks[:, kh, :], vs[:, kh, :], scale, visible)
+    return out

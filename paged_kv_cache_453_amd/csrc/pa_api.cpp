@@ -251,18 +251,22 @@ int pa_decode_splitk_reduce(void* out, const void* workspace, size_t workspace_b
   return status_of(pa::launch_splitk_reduce(a, head_dim, out_dtype == PA_BF16, stream));
 }
 
-int pa_prefill_chunk(void* out, const void* query, const void* key_cache, const void* value_cache,
-                     const int32_t* block_tables, const int32_t* query_start_loc,
-                     const int32_t* context_lens, int num_seqs, int num_query_tokens,
-                     int num_heads, int num_kv_heads, int head_dim, int block_size,
-                     int max_blocks_per_seq, int64_t num_blocks, int max_query_len, float scale,
-                     pa_dtype dtype, hipStream_t stream) {
+namespace {
+
+int prefill_impl(void* out, const void* query, const void* key_cache, const void* value_cache,
+                 const int32_t* block_tables, const int32_t* query_start_loc,
+                 const int32_t* context_lens, int num_seqs, int num_query_tokens, int num_heads,
+                 int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                 int64_t num_blocks, int max_query_len, float scale, bool fp8, float k_scale,
+                 float v_scale, pa_dtype dtype, hipStream_t stream) {
   if (num_seqs < 0 || num_query_tokens < 0 || max_query_len < 0) return PA_ERR_SHAPE;
   if (num_seqs > 0 && (!out || !query || !key_cache || !value_cache || !block_tables ||
                        !query_start_loc || !context_lens))
     return PA_ERR_NULL;
   if (!dtype_ok(dtype) || block_size != kBlockSize || !head_dim_ok(head_dim))
     return PA_ERR_UNSUPPORTED;
+  if (fp8 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;   // the matrix-core path only
+  if (fp8 && (!scale_ok(k_scale) || !scale_ok(v_scale))) return PA_ERR_SHAPE;
   if (num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads != 0 ||
       num_heads > kMaxGridY || num_kv_heads > kMaxGridY || max_blocks_per_seq < 1 ||
       num_blocks < 1 || num_seqs > kMaxGridY)
@@ -290,10 +294,38 @@ int pa_prefill_chunk(void* out, const void* query, const void* key_cache, const 
   a.partition_blocks = 0;
   a.max_partitions = 1;
   a.max_query_len = max_query_len;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  a.v_scale = 1.f;
+  a.scale_log2 = scale * (fp8 ? k_scale : 1.f) * 1.4426950408889634f;
+  a.v_scale = fp8 ? v_scale : 1.f;
+  if (fp8) return status_of(pa::launch_prefill_mfma_fp8(a, head_dim, stream));
   if (dtype == PA_BF16) return status_of(pa::launch_prefill_mfma(a, head_dim, stream));
   return status_of(pa::launch_decode(a, head_dim, false, stream));
+}
+
+}  // namespace
+
+int pa_prefill_chunk(void* out, const void* query, const void* key_cache, const void* value_cache,
+                     const int32_t* block_tables, const int32_t* query_start_loc,
+                     const int32_t* context_lens, int num_seqs, int num_query_tokens,
+                     int num_heads, int num_kv_heads, int head_dim, int block_size,
+                     int max_blocks_per_seq, int64_t num_blocks, int max_query_len, float scale,
+                     pa_dtype dtype, hipStream_t stream) {
+  return prefill_impl(out, query, key_cache, value_cache, block_tables, query_start_loc,
+                      context_lens, num_seqs, num_query_tokens, num_heads, num_kv_heads, head_dim,
+                      block_size, max_blocks_per_seq, num_blocks, max_query_len, scale, false, 1.f,
+                      1.f, dtype, stream);
+}
+
+int pa_prefill_chunk_fp8(void* out, const void* query, const uint8_t* key_cache,
+                         const uint8_t* value_cache, const int32_t* block_tables,
+                         const int32_t* query_start_loc, const int32_t* context_lens, int num_seqs,
+                         int num_query_tokens, int num_heads, int num_kv_heads, int head_dim,
+                         int block_size, int max_blocks_per_seq, int64_t num_blocks,
+                         int max_query_len, float scale, float k_scale, float v_scale,
+                         pa_dtype dtype, hipStream_t stream) {
+  return prefill_impl(out, query, key_cache, value_cache, block_tables, query_start_loc,
+                      context_lens, num_seqs, num_query_tokens, num_heads, num_kv_heads, head_dim,
+                      block_size, max_blocks_per_seq, num_blocks, max_query_len, scale, true,
+                      k_scale, v_scale, dtype, stream);
 }
 
 int pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* block_mapping,

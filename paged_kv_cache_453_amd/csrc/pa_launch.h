@@ -116,5 +116,7 @@ hipError_t launch_sample(const SampleArgs& a, bool bf16, hipStream_t stream);
 constexpr int kStreamBlocks = 32768;
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
 hipError_t launch_prefill_mfma(const DecodeArgs& a, int head_dim, hipStream_t stream);
+// The same over FP8 (E4M3) pools; a.scale_log2 includes the K scale, a.v_scale is V's.
+hipError_t launch_prefill_mfma_fp8(const DecodeArgs& a, int head_dim, hipStream_t stream);
 
 }  // namespace pa

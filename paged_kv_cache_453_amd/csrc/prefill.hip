@@ -33,6 +33,12 @@
 //    two such reads give its 8 keys.  V rows are padded by 32 bytes, so the
 //    eight rows of a half-wave's read cover the banks once.
 //
+// FP8 (E4M3) caches: the staging loads read 8 codes (8 bytes) where they would
+// read 8 bf16 (16 bytes), and widen them to bf16 as they store the tile to LDS
+// (exact: an E4M3 value has at most 4 significant bits); from there the
+// kernel is the bf16 one.  The per-tensor K scale is folded into the score
+// scale by the caller, the V scale into the final normalisation.
+//
 // Softmax in base 2 with lazy rescaling: a row's reference max moves only when
 // a tile's max exceeds it by more than 8, so the accumulators are rarely
 // touched by the vector ALUs.  Probabilities are rounded to bf16 for the p.V
@@ -41,6 +47,8 @@
 // numerator and denominator use the same weights.  exp2 is the raw hardware
 // instruction: weights below 2^-126 flush to zero, which a softmax ignores.
 #include <math.h>
+
+#include <type_traits>
 
 #include "pa_device.h"
 #include "pa_launch.h"
@@ -72,8 +80,9 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* base, int off) {
 
 }  // namespace
 
-template <int D, int RW>
+template <typename KV, int D, int RW>
 __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
+  constexpr bool kFp8 = sizeof(KV) == 1;
   constexpr int KS = D / 32;            // k-steps of the score MFMA
   constexpr int DT = D / 16;            // d-tiles of the output (= columns per lane per key)
   constexpr int QB = RW / 16;           // 16-row query blocks per wave
@@ -145,8 +154,8 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
   const int nblk = (kend + kBlock - 1) / kBlock;
   const float sl2 = a.scale_log2;
   const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-  const bf16_t* kpool = static_cast<const bf16_t*>(a.k_cache);
-  const bf16_t* vpool = static_cast<const bf16_t*>(a.v_cache);
+  const KV* kpool = static_cast<const KV*>(a.k_cache);
+  const KV* vpool = static_cast<const KV*>(a.v_cache);
 
   // Staging: thread (key row kr0 + KPP*p, chunk cc) for p < NPASS.  Block ids
   // of a tile sit in lanes 0..3 of ids (fetched two tiles ahead from an
@@ -158,12 +167,14 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
   // exact: the waits before the LDS stores cover only what they store.
   const int cc = tid % CH;
   const int kr0 = tid / CH;
-  const int row_bytes = D * 2;
+  const int row_bytes = D * (int)sizeof(KV);
+  // what one thread loads per key row: 8 elements (16 bytes of bf16, 8 of fp8)
+  typedef typename std::conditional<kFp8, u32x2, u32x4>::type piece_t;
   const auto fetch_ids = [&](int kt) {
     const int j = kt * 4 + (lane & 3);
     return table[min(j, a.max_blocks_per_seq - 1)];
   };
-  u32x4 kst[NPASS], vst[NPASS];
+  piece_t kst[NPASS], vst[NPASS];
   const auto stage_load = [&](int kt, int ids) {
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
@@ -177,21 +188,34 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
       const bool live = rows > 0 && in_pool;
       const int64_t off = live ? ((int64_t)bid * a.num_kv_heads + kvh) * kBlock * D : 0;
       const int nbytes = live ? rows * row_bytes : 0;
-      const int lane_off = (key % kBlock) * row_bytes + cc * 16;
-      kst[p] = __builtin_amdgcn_raw_buffer_load_b128(
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(kpool + off), 0, nbytes, kBufferWord3),
-          lane_off, 0, 0);
-      vst[p] = __builtin_amdgcn_raw_buffer_load_b128(
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(vpool + off), 0, nbytes, kBufferWord3),
-          lane_off, 0, 0);
+      const int lane_off = (key % kBlock) * row_bytes + cc * 8 * (int)sizeof(KV);
+      const auto krs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<KV*>(kpool + off), 0, nbytes, kBufferWord3);
+      const auto vrs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<KV*>(vpool + off), 0, nbytes, kBufferWord3);
+      if constexpr (kFp8) {
+        kst[p] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(krs, lane_off, 0, 0));
+        vst[p] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(vrs, lane_off, 0, 0));
+      } else {
+        kst[p] = __builtin_amdgcn_raw_buffer_load_b128(krs, lane_off, 0, 0);
+        vst[p] = __builtin_amdgcn_raw_buffer_load_b128(vrs, lane_off, 0, 0);
+      }
+    }
+  };
+  const auto widen = [](const piece_t& x) -> u32x4 {
+    if constexpr (kFp8) {
+      const u32x2 lo = fp8x4_to_bf16x4(x[0]), hi = fp8x4_to_bf16x4(x[1]);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    } else {
+      return x;
     }
   };
   const auto stage_store = [&](int buf) {
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
       const int kr = kr0 + KPP * p;
-      *reinterpret_cast<u32x4*>(&smem[buf][kr * ROW + cc * 16]) = kst[p];
-      *reinterpret_cast<u32x4*>(&smem[buf][kKeys * ROW + kr * ROWV + cc * 16]) = vst[p];
+      *reinterpret_cast<u32x4*>(&smem[buf][kr * ROW + cc * 16]) = widen(kst[p]);
+      *reinterpret_cast<u32x4*>(&smem[buf][kKeys * ROW + kr * ROWV + cc * 16]) = widen(vst[p]);
     }
   };
 
@@ -319,7 +343,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
     const float l = lacc[qb][0];
     const int qi = qw0 + 16 * qb + r;
     if (qi >= chunk) continue;
-    const float inv = 1.f / l;
+    const float inv = (kFp8 ? a.v_scale : 1.f) / l;
     bf16_t* dst = out + ((int64_t)(q0 + qi) * hq + h) * D;
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
@@ -334,15 +358,24 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
 // blocks (16 rows per wave measured 15% slower on the mixed workload's chunks).
 constexpr int kPrefillRowsPerWave = 32;
 
-hipError_t launch_prefill_mfma(const DecodeArgs& a, int head_dim, hipStream_t stream) {
+template <typename KV>
+hipError_t launch_prefill(const DecodeArgs& a, int head_dim, hipStream_t stream) {
   constexpr int RW = kPrefillRowsPerWave;
   if (a.num_seqs == 0 || a.max_query_len == 0) return hipSuccess;
   dim3 grid((a.max_query_len + 4 * RW - 1) / (4 * RW), a.num_heads, a.num_seqs);
   if (head_dim == 64)
-    hipLaunchKernelGGL((prefill_mfma_kernel<64, RW>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((prefill_mfma_kernel<KV, 64, RW>), grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((prefill_mfma_kernel<128, RW>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((prefill_mfma_kernel<KV, 128, RW>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_prefill_mfma(const DecodeArgs& a, int head_dim, hipStream_t stream) {
+  return launch_prefill<bf16_t>(a, head_dim, stream);
+}
+
+hipError_t launch_prefill_mfma_fp8(const DecodeArgs& a, int head_dim, hipStream_t stream) {
+  return launch_prefill<fp8_t>(a, head_dim, stream);
 }
 
 }  // namespace pa

@@ -88,6 +88,9 @@ def load() -> ctypes.CDLL:
     lib.pa_copy_blocks.restype = i32
     lib.pa_swap_blocks.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, vp]
     lib.pa_swap_blocks.restype = i32
+    lib.pa_prefill_chunk_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                         i32, i32, i64, i32, f32, f32, f32, i32, vp]
+    lib.pa_prefill_chunk_fp8.restype = i32
     lib.pa_stream_read_sink_words.argtypes = []
     lib.pa_stream_read_sink_words.restype = i32
     lib.pa_stream_read.argtypes = [vp, i64, vp, vp]
@@ -125,8 +128,8 @@ def load() -> ctypes.CDLL:
 
 EXPORTED = ("pa_reshape_and_cache", "pa_decode_workspace_bytes", "pa_decode",
             "pa_decode_splitk_reduce", "pa_prefill_chunk", "pa_reshape_and_cache_fp8",
-            "pa_decode_fp8", "pa_sample", "pa_copy_blocks", "pa_swap_blocks",
-            "pa_stream_read_sink_words", "pa_stream_read", "pa_status_string")
+            "pa_decode_fp8", "pa_prefill_chunk_fp8", "pa_sample", "pa_copy_blocks",
+            "pa_swap_blocks", "pa_stream_read_sink_words", "pa_stream_read", "pa_status_string")
 
 
 # --------------------------------------------------------------------------
@@ -326,6 +329,32 @@ def pa_decode_fp8(out, query, key_cache, value_cache, block_tables, context_lens
         _ptr(context_lens), _ptr(shared_prefix_blocks), s, hq, hkv, d, bs, block_tables.shape[1],
         nb, int(max_context_len), float(scale), float(k_scale), float(v_scale),
         int(partition_size), ws_ptr, ws_bytes, _dtype_code(query), _stream(stream)))
+
+
+def pa_prefill_chunk_fp8(out, query, key_cache, value_cache, block_tables, query_start_loc,
+                         context_lens, scale: float, k_scale: float, v_scale: float,
+                         max_query_len: int, stream=None) -> None:
+    """pa_prefill_chunk over uint8 E4M3 caches whose codes stand for value * k_scale /
+    v_scale; out/query bf16 [Tq, Hq, D]."""
+    torch = _torch()
+    lib = load()
+    _on_gpu(out, query, key_cache, value_cache, block_tables, query_start_loc, context_lens)
+    _need(block_tables.dtype == torch.int32 and query_start_loc.dtype == torch.int32 and
+          context_lens.dtype == torch.int32, "index arrays must be int32")
+    _need(key_cache.dtype == torch.uint8 and value_cache.dtype == torch.uint8,
+          "FP8 caches are uint8 tensors of E4M3 codes")
+    tq, hq, d = query.shape
+    nb, hkv, bs, d2 = key_cache.shape
+    s = context_lens.numel()
+    _need(d2 == d and tuple(out.shape) == (tq, hq, d) and value_cache.shape == key_cache.shape,
+          "shape mismatch")
+    _need(query_start_loc.numel() == s + 1 and block_tables.shape[0] == s, "sequence count mismatch")
+    _need(out.dtype == query.dtype, "query and output dtypes differ")
+    _check("pa_prefill_chunk_fp8", lib.pa_prefill_chunk_fp8(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(query_start_loc), _ptr(context_lens), s, tq, hq, hkv, d, bs, block_tables.shape[1],
+        nb, int(max_query_len), float(scale), float(k_scale), float(v_scale),
+        _dtype_code(query), _stream(stream)))
 
 
 # --------------------------------------------------------------------------

@@ -248,3 +248,22 @@ def test_stream_read_validation(lib):
     assert f(P + 8, 16, P, None) == PA_ERR_SHAPE      # not 16-byte aligned
     assert f(P, 16, None, None) == PA_ERR_NULL
     assert f(None, 16, P, None) == PA_ERR_NULL
+
+
+def test_fp8_prefill_validation(lib):
+    f = lib.pa_prefill_chunk_fp8
+    # a valid argument set (never called as is: it would launch), then one fault at a time,
+    # each rejected before any HIP call
+    args = [P, P, P, P, P, P, P, 2, 8, 8, 8, 128, 16, 4, 64, 4, 0.125, 0.07, 0.11, BF16, None]
+    bad = list(args)
+    bad[19] = 0                                         # fp32 query: only bf16 runs on this path
+    assert f(*bad) == PA_ERR_UNSUPPORTED
+    bad = list(args)
+    bad[17] = 0.0                                       # k_scale must be positive
+    assert f(*bad) == PA_ERR_SHAPE
+    bad = list(args)
+    bad[18] = float("inf")
+    assert f(*bad) == PA_ERR_SHAPE
+    bad = list(args)
+    bad[2] = None
+    assert f(*bad) == PA_ERR_NULL

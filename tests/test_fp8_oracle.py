@@ -104,6 +104,45 @@ def test_decode_reduces_to_plain_attention_on_the_values():
     np.testing.assert_allclose(got, want, rtol=1e-14, atol=1e-14)
 
 
+def _prefill_case(seed):
+    rng = np.random.default_rng(seed)
+    hq, hkv, d, nb = 4, 2, 64, 16
+    k_codes = rng.integers(0, 256, (nb, hkv, 16, d), dtype=np.uint8)
+    v_codes = rng.integers(0, 256, (nb, hkv, 16, d), dtype=np.uint8)
+    for c in (k_codes, v_codes):                          # no NaN codes
+        c[(c & 0x7F) == 0x7F] = 0x3C
+    tables = np.array([[3, 7, 1, 9], [0, 2, -1, -1], [11, 12, 13, -1]], dtype=np.int32)
+    lens = np.array([50, 17, 40], dtype=np.int32)        # chunks of 7, 17 and 1 new tokens
+    qsl = np.array([0, 7, 24, 25], dtype=np.int32)
+    q = rng.standard_normal((25, hq, d)).astype(np.float32)
+    return q, k_codes, v_codes, tables, qsl, lens
+
+
+def test_prefill_reduces_to_plain_prefill_on_the_values():
+    """Power-of-two scales keep the dequantised values exact in fp32, so the FP8
+    prefill must equal the plain prefill oracle on those values."""
+    q, kc, vc, tables, qsl, lens = _prefill_case(5)
+    ks, vs, scale = 0.03125, 0.5, np.float32(0.125)
+    got = kv_fp8.prefill(q, kc, vc, tables, qsl, lens, scale, ks, vs, "f32")
+    kp = (kv_fp8.decode_codes(kc) * ks).astype(np.float32)
+    vp = (kv_fp8.decode_codes(vc) * vs).astype(np.float32)
+    want = oracle.prefill(q, kp, vp, tables, qsl, lens, scale, "f32")
+    np.testing.assert_allclose(got, want, rtol=1e-14, atol=1e-14)
+    # a planted swap of the two scales is a different result
+    swapped = kv_fp8.prefill(q, kc, vc, tables, qsl, lens, scale, vs, ks, "f32")
+    assert not np.allclose(swapped, want, rtol=1e-6, atol=1e-6)
+
+
+def test_prefill_one_token_chunk_is_decode():
+    """The last query of a chunk sees the whole context: a one-token chunk is
+    the FP8 decode of that token (xdnf.cn article, section 六.4)."""
+    q, kc, vc, tables, qsl, lens = _prefill_case(6)
+    got = kv_fp8.prefill(q, kc, vc, tables, qsl, lens, np.float32(0.125), 0.07, 0.11, "f32")
+    last = np.array([qsl[1] - 1, qsl[2] - 1, qsl[3] - 1])
+    want = kv_fp8.decode(q[last], kc, vc, tables, lens, np.float32(0.125), 0.07, 0.11, "f32")
+    np.testing.assert_allclose(got[last], want, rtol=1e-13, atol=1e-13)
+
+
 def test_fp8_scatter_quantises_into_slots():
     rng = np.random.default_rng(4)
     nb, hkv, d = 6, 2, 64

@@ -14,7 +14,7 @@ import pytest
 
 from oracle import kv_fp8
 from pa_harness import TOL, as_f64, assert_close, say
-from workloads import config2, fp8_codes, fp8_pools, make_decode
+from workloads import config2, config4, fp8_codes, fp8_pools, make_decode, make_prefill
 from workloads.device import host_to_torch, to_device, torch_to_storage, upload_fp8_pools
 from workloads.generate import f32_to_bf16_bits
 
@@ -209,3 +209,51 @@ def test_fp8_llama13b_scatter_then_decode(gpu):
     want = kv_fp8.decode(gg.query[pick], kq2, vq2, w.host_tables(gg.block_tables[pick]),
                          gg.context_lens[pick], w.scale, K_SCALE, V_SCALE, "bf16")
     assert_close(as_f64(g.out)[pick], want, "bf16", "fp8 13B decode (sampled)")
+
+
+def run_fp8_prefill(gpu, w, k_codes, v_codes):
+    import torch
+    dw = to_device(w)
+    kc, vc = upload_fp8_pools(w, k_codes, v_codes)
+    g = dw.prefill
+    gpu.pa_prefill_chunk_fp8(g.out, g.query, kc, vc, g.block_tables, g.query_start_loc,
+                             g.context_lens, float(w.scale), K_SCALE, V_SCALE, g.max_query_len)
+    torch.cuda.synchronize()
+    return dw, kc, vc
+
+
+def oracle_fp8_prefill(w, k_codes, v_codes):
+    g = w.prefill
+    return kv_fp8.prefill(g.query, k_codes, v_codes, w.host_tables(g.block_tables),
+                          g.query_start_loc, g.context_lens, w.scale, K_SCALE, V_SCALE, "bf16")
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(4, 4, 128), (8, 2, 128), (6, 3, 64), (32, 8, 128)])
+def test_fp8_prefill_matches_oracle(gpu, hq, hkv, d):
+    """Ragged chunks over ragged paged prefixes (not multiples of 16 or 64)."""
+    say(f"fp8 prefill hq={hq} hkv={hkv} d={d}")
+    w = make_prefill(f"fp8-prefill-{hq}-{hkv}-{d}", 81 + hq, "bf16", [0, 5, 16, 100, 777],
+                     [1, 70, 64, 130, 33], hq, hkv, d, 256)
+    kq, vq = fp8_pools(w, 82)
+    dw, _, _ = run_fp8_prefill(gpu, w, kq, vq)
+    assert_close(as_f64(dw.prefill.out), oracle_fp8_prefill(w, kq, vq), "bf16",
+                 f"fp8 prefill {hq}/{hkv} d={d}")
+
+
+def test_fp8_mixed_step_on_one_cache(gpu):
+    """A step that prefills chunks and decodes other sequences over the same FP8
+    pools: both parts against the oracle."""
+    import torch
+    say("fp8 mixed step: prefill chunks + shared-prefix decoders on one FP8 cache")
+    w = config4(num_prompts=8, samples=3, num_prefill=2, num_blocks=4096)
+    kq, vq = fp8_pools(w, 83)
+    dw, kc, vc = run_fp8_prefill(gpu, w, kq, vq)
+    g = dw.decode
+    gpu.pa_decode_fp8(g.out, g.query, kc, vc, g.block_tables, g.context_lens, float(w.scale),
+                      K_SCALE, V_SCALE, g.max_context_len, 0)
+    torch.cuda.synchronize()
+    assert_close(as_f64(dw.prefill.out), oracle_fp8_prefill(w, kq, vq), "bf16", "fp8 mixed prefill")
+    d = w.decode
+    want = kv_fp8.decode(d.query, kq, vq, w.host_tables(d.block_tables), d.context_lens, w.scale,
+                         K_SCALE, V_SCALE, w.dtype)
+    assert_close(as_f64(g.out), want, w.dtype, "fp8 mixed decode")
