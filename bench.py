@@ -13,10 +13,10 @@ shuffled pool) with split-K partitions and their merge.
   mixed     chunked prefill of 4 x 512-token chunks over paged prefixes, then
             decode of 192 sequences sharing 2048-token prefixes in groups of 3
             (also timed with prefill and decode on two streams)
-  llama13b_fp8, gqa_fp8
-            the llama13b and gqa steps over an FP8 (OCP E4M3) cache with one
-            scale per pool: quantising scatter (llama13b), decode, merge; KV
-            bytes count one byte per element
+  llama13b_fp8, gqa_fp8, mixed_fp8
+            the llama13b, gqa and mixed steps over an FP8 (OCP E4M3) cache with
+            one scale per pool: quantising scatter (llama13b), chunked prefill
+            (mixed), decode, merge; KV bytes count one byte per element
   prefix_cache  32 prompts at Llama-2-13B shape sharing a 2048-token system
             prompt, each with 256 tokens of its own: the chunked prefill of
             all 32 with prefix-cache hits (256 query tokens each over the
@@ -140,8 +140,13 @@ def cpu_baseline(w, budget_s: float = 10.0, fp8_pools=None):
             p = w.prefill
             qsl = p.query_start_loc
             t0 = time.perf_counter()
-            oracle.prefill(p.query[qsl[0]:qsl[1]], k, v, w.host_tables(p.block_tables[:1]),
-                           qsl[:2] - qsl[0], p.context_lens[:1], w.scale, w.dtype)
+            if fp8:
+                kv_fp8.prefill(p.query[qsl[0]:qsl[1]], k, v, w.host_tables(p.block_tables[:1]),
+                               qsl[:2] - qsl[0], p.context_lens[:1], w.scale, FP8_K_SCALE,
+                               FP8_V_SCALE, w.dtype)
+            else:
+                oracle.prefill(p.query[qsl[0]:qsl[1]], k, v, w.host_tables(p.block_tables[:1]),
+                               qsl[:2] - qsl[0], p.context_lens[:1], w.scale, w.dtype)
             dt = time.perf_counter() - t0
             t_total += dt
             notes.append(f"prefill of the first {int(qsl[1] - qsl[0])}-token chunk "
@@ -291,7 +296,8 @@ class StepTimer:
 
 STREAM_BYTES = 4 << 30
 STREAM_METRIC = "achievable HBM read GB/s (plain 16-byte loads over a 4 GiB buffer)"
-WORKLOADS = ("llama13b", "llama7b", "gqa", "mixed", "llama13b_fp8", "gqa_fp8", "prefix_cache",
+WORKLOADS = ("llama13b", "llama7b", "gqa", "mixed", "llama13b_fp8", "gqa_fp8", "mixed_fp8",
+             "prefix_cache",
              "sampler", "block_moves", "stream_read")
 SAMPLER_BUFFERS = 9
 SAMPLER_METRIC = "next-token sampling rows/s (temperature + top-k + top-p + draw), 32000-token vocabulary"
@@ -715,6 +721,8 @@ def main(argv=None):
         codes = fp8_pools(w, 453)
         cfg["workload"] = cfg["workload"].replace("paged decode", "paged decode over an FP8 "
                                                   "(E4M3) cache")
+        if base == "mixed":
+            cfg["workload"] = cfg["workload"].replace("chunked prefill", "FP8 chunked prefill")
         cfg["kv_cache"] = (f"fp8 e4m3 codes, random sign / exponent field 0..9 / mantissa; "
                            f"k_scale {FP8_K_SCALE}, v_scale {FP8_V_SCALE}")
     log(f"bench: generated in {time.time() - t0:.1f} s; uploading")
@@ -755,9 +763,14 @@ def main(argv=None):
 
     def prefill(s=stream):
         p = dw.prefill
-        lib.pa_prefill_chunk(p.out, p.query, dw.k_cache, dw.v_cache, p.block_tables,
-                             p.query_start_loc, p.context_lens, w.scale, p.max_query_len,
-                             stream=s)
+        if fp8:
+            lib.pa_prefill_chunk_fp8(p.out, p.query, dw.k_cache, dw.v_cache, p.block_tables,
+                                     p.query_start_loc, p.context_lens, w.scale, FP8_K_SCALE,
+                                     FP8_V_SCALE, p.max_query_len, stream=s)
+        else:
+            lib.pa_prefill_chunk(p.out, p.query, dw.k_cache, dw.v_cache, p.block_tables,
+                                 p.query_start_loc, p.context_lens, w.scale, p.max_query_len,
+                                 stream=s)
 
     launches = []
     if w.slot_mapping is not None:
@@ -802,7 +815,7 @@ def main(argv=None):
         flops = accounting.prefill_flops(p.query_start_loc, p.context_lens, w.num_heads,
                                          w.head_dim)
         unique = accounting.unique_kv_bytes(g.block_tables, g.context_lens, w.num_kv_heads,
-                                            w.head_dim, w.elem_bytes)
+                                            w.head_dim, kv_elem)
         tokens += int(p.query_start_loc[-1])
         pf_tflops = flops / (kernel_ms["prefill"] * 1e-3) / 1e12
         unique_gbs = unique / (kernel_ms["decode"] * 1e-3) / 1e9
@@ -817,7 +830,7 @@ def main(argv=None):
         extra["roofline_prefill"] = {
             "bound": "mfma", "achieved": round(pf_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(pf_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None, "kernel": "prefill_mfma_kernel<128,32>",
+            "traffic": None, "kernel": f"prefill_mfma_kernel<{kv_name},128,32>",
             "algorithmic_flops_per_launch": int(flops)}
         extra["prefill_tokens_per_step"] = int(p.query_start_loc[-1])
         # a rate against the HBM peak must count each physical row once
