@@ -668,6 +668,9 @@ def main(argv=None):
                     help="split-K partition length in tokens (default: 2048 for the Llama "
                          "shapes, 512 for gqa as its configuration states, 2048 for mixed)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefix-groups", action="store_true",
+                    help="mixed workloads: decode with pa_decode (each sample streams the "
+                         "shared prefix itself) instead of pa_decode_shared_prefix")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -685,6 +688,7 @@ def main(argv=None):
               "device; run it with --gpus 1", file=sys.stderr)
         return 2
 
+    import numpy as np
     import torch
 
     from paged_kv_cache_453_amd import lib
@@ -745,7 +749,11 @@ def main(argv=None):
             lib.pa_reshape_and_cache(dw.new_k, dw.new_v, dw.k_cache, dw.v_cache,
                                      dw.slot_mapping, stream=stream)
 
-    def decode(s=stream):
+    # samples of one prompt: their common partitions are streamed once per group
+    grouped = dg.prefix_group is not None and ps > 0 and not args.no_prefix_groups
+    max_group = int(np.bincount(g.prefix_group).max()) if g.prefix_group is not None else 1
+
+    def plain_decode(s=stream):
         if fp8:
             lib.pa_decode_fp8(dg.out, dg.query, dw.k_cache, dw.v_cache, dg.block_tables,
                               dg.context_lens, w.scale, FP8_K_SCALE, FP8_V_SCALE,
@@ -755,6 +763,20 @@ def main(argv=None):
             lib.pa_decode(dg.out, dg.query, dw.k_cache, dw.v_cache, dg.block_tables,
                           dg.context_lens, w.scale, g.max_context_len, ps, ws if ps else None,
                           stream=s, shared_prefix_blocks=dg.shared_prefix_blocks)
+
+    def grouped_decode(s=stream):
+        if fp8:
+            lib.pa_decode_fp8_shared_prefix(
+                dg.out, dg.query, dw.k_cache, dw.v_cache, dg.block_tables, dg.context_lens,
+                w.scale, FP8_K_SCALE, FP8_V_SCALE, g.max_context_len, ps, ws,
+                dg.shared_prefix_blocks, dg.prefix_group, max_group, stream=s)
+        else:
+            lib.pa_decode_shared_prefix(
+                dg.out, dg.query, dw.k_cache, dw.v_cache, dg.block_tables, dg.context_lens,
+                w.scale, g.max_context_len, ps, ws, dg.shared_prefix_blocks, dg.prefix_group,
+                max_group, stream=s)
+
+    decode = grouped_decode if grouped else plain_decode
 
     def reduce(s=stream):
         if ps:
@@ -795,6 +817,11 @@ def main(argv=None):
     log("bench: step %.1f us (%s)" % (ms_per_step * 1e3, ", ".join(
         f"{k} {v * 1e3:.1f}" for k, v in kernel_ms.items())))
 
+    if grouped:
+        # the same decode without the grouped pass, for comparison
+        extra_ms = timer.per_launch([("decode_ungrouped", plain_decode)], args.steps, stream)
+        log("bench: decode without prefix groups %.1f us" % (extra_ms["decode_ungrouped"] * 1e3))
+
     kv_elem = 1 if fp8 else w.elem_bytes
     kv = accounting.decode_kv_bytes(g.context_lens, w.num_kv_heads, w.head_dim, kv_elem)
     gbs = kv / (ms_per_step * 1e-3) / 1e9
@@ -805,6 +832,10 @@ def main(argv=None):
     kv_name = "fp8" if fp8 else "bf16"
     dec_kernel = (f"decode_gqa_mfma_kernel<{kv_name}>" if group >= 4 else
                   f"decode_valu_kernel<bf16,{kv_name},{w.head_dim},{group}>")
+    if grouped:
+        dec_kernel = (f"decode_valu_kernel<bf16,{kv_name},{w.head_dim},3,grouped> + "
+                      f"decode_valu_kernel<bf16,{kv_name},{w.head_dim},{group}> "
+                      "(one pa_decode_shared_prefix call)")
     roofline = {"bound": "hbm", "achieved": round(decode_gbs, 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(decode_gbs / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic("decode") if args.workload == "llama13b" else None,
@@ -838,6 +869,13 @@ def main(argv=None):
         extra["kv_bytes_unique_per_step"] = int(unique)
         gbs = unique / (ms_per_step * 1e-3) / 1e9
         extra["prefixes"] = w.meta.get("prefixes")
+        extra["decode_prefix_groups"] = {
+            "entry_point": "pa_decode_shared_prefix" if grouped else "pa_decode",
+            "groups": int(np.unique(g.prefix_group).size) if g.prefix_group is not None else 0,
+            "max_group_size": max_group}
+        if grouped:
+            extra["decode_prefix_groups"]["decode_us_without_grouping"] = round(
+                extra_ms["decode_ungrouped"] * 1e3, 2)
 
         # the same step with prefill (matrix cores) and decode (HBM) on two streams
         side = torch.cuda.Stream(device=dev)

@@ -146,6 +146,49 @@ int pa_decode(void* out, const void* query, const void* key_cache, const void* v
               hipStream_t stream);
 
 /*
+ * pa_decode_shared_prefix -- pa_decode for a batch in which groups of
+ * sequences share their leading blocks, reading each shared block once per
+ * group instead of once per sequence.
+ *
+ * Samples of one prompt keep the prompt's physical blocks in common ("vLLM
+ * 基本原理", section 内存共享), and so do requests that hit one cached prefix
+ * (xdnf.cn article, section 六.3).  Decode is bound by the bytes it streams
+ * (xdnf.cn article, section 六.5), so here a split-K partition made only of
+ * such blocks is streamed once and scored against the queries of up to four
+ * sharers (query slots: members x query heads per kv head <= 4); each sharer
+ * gets the same per-partition partial its own workgroup would have produced,
+ * and pa_decode_splitk_reduce() merges them as usual.  Every argument of
+ * pa_decode keeps its meaning, with these differences:
+ *
+ *  shared_prefix_blocks  required: int32 [num_seqs], leading table entries of
+ *                 each sequence that other sequences of its group also name.
+ *  prefix_group   device int32 [num_seqs]: the first sequence (leader) of each
+ *                 sequence's group; a group's members are consecutive and its
+ *                 leader names itself.  For member s with leader L, the
+ *                 partitions that lie in the first min(shared_prefix_blocks[s],
+ *                 shared_prefix_blocks[L]) entries and in full blocks of both
+ *                 are read through L's table, so s's table must name the same
+ *                 blocks there (else s's output is NaN).  An entry that does
+ *                 not describe such a group (leader after s or negative, or
+ *                 not its own leader) leaves s ungrouped: it is computed as by
+ *                 pa_decode.
+ *  max_group_size largest group (>= 1); it sets the members per workgroup.
+ *  partition_size must be > 0 (the shared partitions are split-K partials).
+ * Query-head groups larger than 2 (num_heads / num_kv_heads > 2) leave no
+ * room for a second member: the call then computes exactly what pa_decode
+ * computes.  The result equals pa_decode's bit for bit (same partitions, same
+ * order of accumulation).
+ */
+int pa_decode_shared_prefix(void* out, const void* query, const void* key_cache,
+                            const void* value_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, const int32_t* shared_prefix_blocks,
+                            const int32_t* prefix_group, int max_group_size, int num_seqs,
+                            int num_heads, int num_kv_heads, int head_dim, int block_size,
+                            int max_blocks_per_seq, int64_t num_blocks, int max_context_len,
+                            float scale, int partition_size, void* workspace,
+                            size_t workspace_bytes, pa_dtype dtype, hipStream_t stream);
+
+/*
  * pa_decode_splitk_reduce -- merge the partition results pa_decode left in the
  * workspace: with M = max_p lse_p and w_p = exp(lse_p - M),
  * out = sum_p w_p o_p / sum_p w_p.  Sequences with at most one partition are
@@ -227,6 +270,21 @@ int pa_decode_fp8(void* out, const void* query, const uint8_t* key_cache,
                   int max_blocks_per_seq, int64_t num_blocks, int max_context_len, float scale,
                   float k_scale, float v_scale, int partition_size, void* workspace,
                   size_t workspace_bytes, pa_dtype dtype, hipStream_t stream);
+
+/*
+ * pa_decode_fp8_shared_prefix -- pa_decode_shared_prefix over FP8 caches:
+ * the arguments of pa_decode_fp8 plus prefix_group and max_group_size, with
+ * the same grouping rules; equal bit for bit to pa_decode_fp8.
+ */
+int pa_decode_fp8_shared_prefix(void* out, const void* query, const uint8_t* key_cache,
+                                const uint8_t* value_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, const int32_t* shared_prefix_blocks,
+                                const int32_t* prefix_group, int max_group_size, int num_seqs,
+                                int num_heads, int num_kv_heads, int head_dim, int block_size,
+                                int max_blocks_per_seq, int64_t num_blocks, int max_context_len,
+                                float scale, float k_scale, float v_scale, int partition_size,
+                                void* workspace, size_t workspace_bytes, pa_dtype dtype,
+                                hipStream_t stream);
 
 /*
  * pa_prefill_chunk_fp8 -- pa_prefill_chunk over FP8 caches: causal attention

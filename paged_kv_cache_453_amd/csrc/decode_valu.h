@@ -332,9 +332,47 @@ __device__ __forceinline__ bool locate_item(const DecodeArgs& a, int item, ItemI
   return true;
 }
 
+// Grouped pass over shared prefixes.  Samples of one prompt keep its blocks in
+// common ("vLLM 基本原理", section 内存共享), as do requests that hit one cached
+// prefix (xdnf.cn article, section 六.3); their block tables then name the same
+// physical blocks, and a partition made of such blocks holds the same K/V for
+// every sharer.  The grouped pass streams each such partition once and scores
+// it against the queries of up to group_members sharers at a time, writing
+// each sharer's partial (o_p, lse_p) exactly where its own split-K workgroup
+// would have; the regular pass then skips those partitions.
+//
+// grouped_parts(s): how many leading partitions of sequence s the grouped pass
+// computes -- those inside the full blocks that s and its group's leader both
+// declare shared.  Both passes evaluate it from the same data, so every
+// partition is computed exactly once.  It is 0 (the regular pass does all)
+// unless s's group is well formed: leader <= s, the leader leads itself, and
+// the first member of s's window of group_members is in the group too, and
+// both lengths are within the call's limits.
+__device__ __forceinline__ int grouped_parts(const DecodeArgs& a, int s) {
+  if (a.prefix_group == nullptr) return 0;
+  const int lead = a.prefix_group[s];
+  if (lead < 0 || lead > s) return 0;
+  const int M = a.group_members;
+  const int first = lead + (s - lead) / M * M;
+  if (a.prefix_group[lead] != lead || a.prefix_group[first] != lead) return 0;
+  const int cap = min(a.max_context_len, a.max_blocks_per_seq * kBlock);
+  const int ls = a.context_lens[s];
+  const int ll = a.context_lens[lead];
+  if (ls < 0 || ll < 0 || ls > cap || ll > cap) return 0;
+  const int nb = min(min(a.shared_prefix_blocks[s], a.shared_prefix_blocks[lead]),
+                     min(ls, ll) / kBlock);
+  return nb > 0 ? nb / a.partition_blocks : 0;
+}
+
 // HINT: the caller passed shared_prefix_blocks, so batches of shared blocks
 // take the caching load path; without it only the streaming path is compiled.
-template <typename T, typename KV, int D, int GP, bool HINT>
+// GROUPED: the grouped pass.  Workgroup (s, kv head, partition) works only if
+// s opens a window of its group (s - leader a multiple of group_members) and
+// the partition lies in the grouped prefix of some member of the window; the
+// blocks come from the leader's table, query slot g is query head
+// kvh*G + g % G of member s + g / G, and a member whose table names other
+// blocks there gets NaN (it broke the grouping contract).
+template <typename T, typename KV, int D, int GP, bool HINT, bool GROUPED>
 __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   constexpr int E = ElemTraits<KV>::kPerLoad;  // cache elements per 16-byte load
   constexpr int LPR = D / E;                   // lanes per token row
@@ -342,11 +380,13 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   constexpr int NLD = kBlock / RPL;            // loads per block slab per lane
   constexpr int NW = kWavesPerGroup;
   static_assert(LPR >= 2 && LPR <= 32 && NLD >= 1, "layout");
+  static_assert(!GROUPED || (GP <= 32 && !HINT), "grouped pass");
 
   __shared__ float sh_acc[NW][GP][D];
   __shared__ float sh_m[NW][GP];
   __shared__ float sh_l[NW][GP];
   __shared__ int sh_bad[NW];
+  __shared__ uint32_t sh_mismatch[NW];
 
   // blockIdx.x = item * num_kv_heads + kv head: workgroups launched together
   // read the adjacent head slabs of the same physical blocks, which keeps the
@@ -359,50 +399,82 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   const int r = lane / LPR;
   const int c = lane % LPR;
   const int G = a.group;
-
-  ItemInfo it;
-  if (!locate_item(a, item, it)) return;
-  const int nblk = it.bad ? 0 : (it.ctx + kBlock - 1) / kBlock;
-  const bool split = a.partition_blocks > 0;
-  const int nparts = split ? (nblk + a.partition_blocks - 1) / a.partition_blocks : 1;
-  if (part >= (nparts > 0 ? nparts : 1)) return;
-  const int jb = split ? part * a.partition_blocks : 0;
-  const int je = split ? min(nblk, jb + a.partition_blocks) : nblk;
-  const int tok_end = min(it.ctx, je * kBlock);
   const int hq = a.num_heads;
   T* out = static_cast<T*>(a.out);
 
-  // Degenerate items (only partition 0 gets here): no context gives zeros, a
-  // violated contract gives NaN.
-  if (it.bad || it.ctx == 0) {
-    const float fill = it.bad ? __builtin_nanf("") : 0.f;
-    if (split && it.bad && it.ctx > 0 && it.ctx <= a.max_context_len) {
-      // the merge step will read this item's partitions: poison all of them
-      const int ptok = a.partition_blocks * kBlock;
-      const int np_bad = (it.ctx + ptok - 1) / ptok;
-      if (np_bad > 1) {
-        for (int i = threadIdx.x; i < np_bad * G * D; i += blockDim.x) {
-          const int p = i / (G * D);
-          const int g = (i / D) % G;
-          const int64_t row = ((int64_t)it.seq * hq + kvh * G + g) * a.max_partitions + p;
-          a.part_o[row * D + i % D] = fill;
-          if (i % D == 0) a.part_lse[row] = fill;
+  // This workgroup folds blocks [jb, je) of `table` (tokens below tok_end),
+  // the first nshared of the sequence's table read with caching.
+  int jb, je, tok_end, nshared;
+  const int32_t* table;
+  uint32_t active = 0;   // grouped: bit m = member item + m takes part
+  int nparts = 1;        // regular: partitions of the item's sequence
+  int seq = item;        // regular: the item's sequence
+  if constexpr (GROUPED) {
+    const int M = a.group_members;
+    const int lead = a.prefix_group[item];
+    if (lead < 0 || lead > item || (item - lead) % M != 0) return;
+    for (int m = 0; m < M && item + m < a.num_seqs; ++m)
+      if (a.prefix_group[item + m] == lead && part < grouped_parts(a, item + m))
+        active |= 1u << m;
+    if (active == 0) return;
+    jb = part * a.partition_blocks;
+    je = jb + a.partition_blocks;
+    tok_end = je * kBlock;   // grouped partitions are whole blocks of every member
+    nshared = 0;             // read once here: streamed
+    table = a.block_tables + (int64_t)lead * a.max_blocks_per_seq;
+  } else {
+    ItemInfo it;
+    if (!locate_item(a, item, it)) return;
+    seq = it.seq;
+    const int nblk = it.bad ? 0 : (it.ctx + kBlock - 1) / kBlock;
+    const bool split = a.partition_blocks > 0;
+    nparts = split ? (nblk + a.partition_blocks - 1) / a.partition_blocks : 1;
+    if (part >= (nparts > 0 ? nparts : 1)) return;
+    if (part < grouped_parts(a, it.seq)) return;   // the grouped pass wrote it
+    jb = split ? part * a.partition_blocks : 0;
+    je = split ? min(nblk, jb + a.partition_blocks) : nblk;
+    tok_end = min(it.ctx, je * kBlock);
+
+    // Degenerate items (only partition 0 gets here): no context gives zeros, a
+    // violated contract gives NaN.
+    if (it.bad || it.ctx == 0) {
+      const float fill = it.bad ? __builtin_nanf("") : 0.f;
+      if (split && it.bad && it.ctx > 0 && it.ctx <= a.max_context_len) {
+        // the merge step will read this item's partitions: poison all of them
+        const int ptok = a.partition_blocks * kBlock;
+        const int np_bad = (it.ctx + ptok - 1) / ptok;
+        if (np_bad > 1) {
+          for (int i = threadIdx.x; i < np_bad * G * D; i += blockDim.x) {
+            const int p = i / (G * D);
+            const int g = (i / D) % G;
+            const int64_t row = ((int64_t)it.seq * hq + kvh * G + g) * a.max_partitions + p;
+            a.part_o[row * D + i % D] = fill;
+            if (i % D == 0) a.part_lse[row] = fill;
+          }
+          return;
         }
-        return;
       }
+      for (int i = threadIdx.x; i < G * D; i += blockDim.x)
+        out[((int64_t)item * hq + kvh * G) * D + i] = ElemTraits<T>::from_f32(fill);
+      return;
     }
-    for (int i = threadIdx.x; i < G * D; i += blockDim.x)
-      out[((int64_t)item * hq + kvh * G) * D + i] = ElemTraits<T>::from_f32(fill);
-    return;
+    nshared = HINT ? a.shared_prefix_blocks[it.seq] : 0;
+    table = a.block_tables + (int64_t)it.seq * a.max_blocks_per_seq;
   }
 
-  // Query fragments of the group's heads: this lane's E elements of each.
+  // Query fragments of the slots: this lane's E elements of each.
   QFrag<T, KV> q[GP];
 #pragma unroll
   for (int g = 0; g < GP; ++g) {
-    if (g < G)
-      q[g].load(static_cast<const T*>(a.query) + ((int64_t)item * hq + kvh * G + g) * D + c * E,
-                a.scale_log2);
+    int64_t row = -1;
+    if constexpr (GROUPED) {
+      const int m = g / G;
+      if ((active >> m) & 1u) row = (int64_t)(item + m) * hq + kvh * G + (g - m * G);
+    } else {
+      if (g < G) row = (int64_t)item * hq + kvh * G + g;
+    }
+    if (row >= 0)
+      q[g].load(static_cast<const T*>(a.query) + row * D + c * E, a.scale_log2);
     else
       q[g].zero();
   }
@@ -418,10 +490,10 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 
   const KV* kpool = static_cast<const KV*>(a.k_cache);
   const KV* vpool = static_cast<const KV*>(a.v_cache);
-  const int32_t* table = a.block_tables + (int64_t)it.seq * a.max_blocks_per_seq;
   const int64_t head_slab = (int64_t)kBlock * D;
   const int lane_off = r * D + c * E;     // elements from the slab start
   bool bad_block = false;
+  uint32_t mismatch = 0;                  // grouped: bit m = member m names other blocks
 
   // Blocks of this wave: jb + w, jb + w + NW, ...  Their ids are fetched up to
   // 64 at a time into one register (lane t holds the t-th) and broadcast per
@@ -434,13 +506,21 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   const int nb_w = (je - jb - w + NW - 1) / NW;
   const int slab_bytes = kBlock * D * (int)sizeof(KV);
   const int lane_byte_off = lane_off * (int)sizeof(KV);
-  const int nshared = HINT ? a.shared_prefix_blocks[it.seq] : 0;
   const int shared_ahead = nshared - jb - w;   // this wave's block idx is shared iff idx < idx_shared
   const int idx_shared = shared_ahead > 0 ? min(nb_w, (shared_ahead + NW - 1) / NW) : 0;
   for (int base = 0; base < nb_w;) {
     const bool shared_batch = base < idx_shared;
     const int cnt = min(kWave, (shared_batch ? idx_shared : nb_w) - base);
-    const int myb = lane < cnt ? table[jb + w + NW * (base + lane)] : 0;
+    const int jl = jb + w + NW * (base + lane);   // this lane's table entry
+    const int myb = lane < cnt ? table[jl] : 0;
+    if constexpr (GROUPED) {
+#pragma unroll
+      for (int mm = 0; mm < GP; ++mm)
+        if ((active >> mm) & 1u) {
+          const int32_t* tm = a.block_tables + (int64_t)(item + mm) * a.max_blocks_per_seq;
+          if (lane < cnt && tm[jl] != myb) mismatch |= 1u << mm;
+        }
+    }
     const auto run_batch = [&](auto policy) {
       constexpr int P = decltype(policy)::value;
       const auto load_step = [&](Slab<NLD>& sl, int t) {
@@ -492,8 +572,15 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     for (int e = 0; e < E; ++e) acc[g][e] = xor_sum_above<LPR>(acc[g][e] * f);
     m[g] = mw;
   }
+  if constexpr (GROUPED) {
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) mismatch |= (uint32_t)__shfl_xor((int)mismatch, o, 64);
+  }
   __syncthreads();
-  if (lane == 0) sh_bad[w] = __builtin_amdgcn_readfirstlane((int)bad_block);
+  if (lane == 0) {
+    sh_bad[w] = __builtin_amdgcn_readfirstlane((int)bad_block);
+    sh_mismatch[w] = mismatch;
+  }
   if (r == 0) {
 #pragma unroll
     for (int g = 0; g < GP; ++g)
@@ -509,32 +596,47 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // Merge the waves and write this workgroup's result.
+  // Merge the waves and write this workgroup's results.
   bool poisoned = false;
+  uint32_t mism = 0;
 #pragma unroll
-  for (int x = 0; x < NW; ++x) poisoned |= sh_bad[x] != 0;
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
+  for (int x = 0; x < NW; ++x) {
+    poisoned |= sh_bad[x] != 0;
+    mism |= sh_mismatch[x];
+  }
+  const int nslots = GROUPED ? a.group_members * G : G;
+  for (int i = threadIdx.x; i < nslots * D; i += blockDim.x) {
     const int g = i / D;
     const int d = i - g * D;
-    float mm = -INFINITY;
+    int oseq = seq, orow = item, h = kvh * G + g, np = nparts;
+    bool bad = poisoned;
+    if constexpr (GROUPED) {
+      const int mm = g / G;
+      if (!((active >> mm) & 1u)) continue;
+      oseq = orow = item + mm;
+      h = kvh * G + (g - mm * G);
+      bad |= ((mism >> mm) & 1u) != 0;
+      const int nblk = (a.context_lens[oseq] + kBlock - 1) / kBlock;
+      np = (nblk + a.partition_blocks - 1) / a.partition_blocks;
+    }
+    float mx = -INFINITY;
 #pragma unroll
-    for (int x = 0; x < NW; ++x) mm = fmaxf(mm, sh_m[x][g]);
+    for (int x = 0; x < NW; ++x) mx = fmaxf(mx, sh_m[x][g]);
     float lsum = 0.f, o = 0.f;
 #pragma unroll
     for (int x = 0; x < NW; ++x) {
-      const float f = (sh_m[x][g] == -INFINITY) ? 0.f : exp2f(sh_m[x][g] - mm);
+      const float f = (sh_m[x][g] == -INFINITY) ? 0.f : exp2f(sh_m[x][g] - mx);
       lsum = fmaf(sh_l[x][g], f, lsum);
       o = fmaf(sh_acc[x][g][d], f, o);
     }
-    o = poisoned ? __builtin_nanf("") : o / lsum;
+    o = bad ? __builtin_nanf("") : o / lsum;
     if constexpr (std::is_same<KV, fp8_t>::value) o *= a.v_scale;
-    const int h = kvh * G + g;
-    if (nparts <= 1) {
-      out[((int64_t)item * hq + h) * D + d] = ElemTraits<T>::from_f32(o);
+    if (np <= 1) {
+      out[((int64_t)orow * hq + h) * D + d] = ElemTraits<T>::from_f32(o);
     } else {
-      const int64_t row = ((int64_t)it.seq * hq + h) * a.max_partitions + part;
+      const int64_t row = ((int64_t)oseq * hq + h) * a.max_partitions + part;
       a.part_o[row * D + d] = o;
-      if (d == 0) a.part_lse[row] = poisoned ? __builtin_nanf("") : (mm + log2f(lsum)) * kLn2;
+      if (d == 0) a.part_lse[row] = bad ? __builtin_nanf("") : (mx + log2f(lsum)) * kLn2;
     }
   }
 }
@@ -548,17 +650,32 @@ inline void launch_decode_group(const DecodeArgs& a, dim3 grid, hipStream_t stre
   const dim3 block(256);
   const int G = a.group;
   if (G <= 1)
-    hipLaunchKernelGGL((decode_valu_kernel<T, KV, D, 1, HINT>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_valu_kernel<T, KV, D, 1, HINT, false>), grid, block, 0, stream, a);
   else if (G <= 2)
-    hipLaunchKernelGGL((decode_valu_kernel<T, KV, D, 2, HINT>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_valu_kernel<T, KV, D, 2, HINT, false>), grid, block, 0, stream, a);
   else if (G <= 4)
-    hipLaunchKernelGGL((decode_valu_kernel<T, KV, D, 4, HINT>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_valu_kernel<T, KV, D, 4, HINT, false>), grid, block, 0, stream, a);
   else if constexpr (!std::is_same<KV, fp8_t>::value) {
     if (G <= 8)
-      hipLaunchKernelGGL((decode_valu_kernel<T, KV, D, 8, HINT>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((decode_valu_kernel<T, KV, D, 8, HINT, false>), grid, block, 0, stream,
+                         a);
     else
-      hipLaunchKernelGGL((decode_valu_kernel<T, KV, D, 16, HINT>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((decode_valu_kernel<T, KV, D, 16, HINT, false>), grid, block, 0, stream,
+                         a);
   }
+}
+
+// The grouped pass, with the fewest slots that hold a window's queries.
+template <typename T, typename KV, int D>
+inline void launch_decode_grouped(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
+  const dim3 block(256);
+  const int slots = a.group_members * a.group;
+  if (slots <= 2)
+    hipLaunchKernelGGL((decode_valu_kernel<T, KV, D, 2, false, true>), grid, block, 0, stream, a);
+  else if (slots <= 3)
+    hipLaunchKernelGGL((decode_valu_kernel<T, KV, D, 3, false, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_valu_kernel<T, KV, D, 4, false, true>), grid, block, 0, stream, a);
 }
 
 template <typename T, typename KV, int D>
@@ -566,6 +683,14 @@ inline hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   if (std::is_same<KV, fp8_t>::value && a.group > kFp8ValuMaxGroup) return hipErrorInvalidValue;
   dim3 grid((unsigned)((int64_t)a.num_items * a.num_kv_heads),
             a.partition_blocks > 0 ? a.max_partitions : 1);
+  if (a.prefix_group != nullptr) {
+    if (a.partition_blocks <= 0 || a.group_members < 2 || a.shared_prefix_blocks == nullptr ||
+        a.query_start_loc != nullptr || a.group_members * a.group > kGroupedMaxSlots)
+      return hipErrorInvalidValue;
+    launch_decode_grouped<T, KV, D>(a, grid, stream);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (a.shared_prefix_blocks != nullptr)
     launch_decode_group<T, KV, D, true>(a, grid, stream);
   else

@@ -39,12 +39,18 @@ bool workspace_ok(const void* ws, size_t bytes, size_t need) {
 // Shared by pa_decode and pa_decode_fp8: checks, then the kernel choice.
 int decode_impl(void* out, const void* query, const void* key_cache, const void* value_cache,
                 const int32_t* block_tables, const int32_t* context_lens,
-                const int32_t* shared_prefix_blocks, int num_seqs, int num_heads,
+                const int32_t* shared_prefix_blocks, const int32_t* prefix_group,
+                int max_group_size, int num_seqs, int num_heads,
                 int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
                 int64_t num_blocks, int max_context_len, float scale, int partition_size,
                 void* workspace, size_t workspace_bytes, pa_dtype dtype, bool fp8,
                 float k_scale, float v_scale, hipStream_t stream) {
   if (num_seqs < 0) return PA_ERR_SHAPE;
+  if (prefix_group != nullptr) {
+    // the grouped pass writes split-K partials and needs the shared counts
+    if (num_seqs > 0 && !shared_prefix_blocks) return PA_ERR_NULL;
+    if (partition_size <= 0 || max_group_size < 1) return PA_ERR_SHAPE;
+  }
   if (num_seqs > 0 && (!out || !query || !key_cache || !value_cache || !block_tables ||
                        !context_lens))
     return PA_ERR_NULL;
@@ -76,6 +82,15 @@ int decode_impl(void* out, const void* query, const void* key_cache, const void*
   a.context_lens = context_lens;
   a.query_start_loc = nullptr;
   a.shared_prefix_blocks = shared_prefix_blocks;
+  // Windows of up to group_members sharers per grouped workgroup; with fewer
+  // than two (groups of one, or query-head groups that fill the slots alone)
+  // there is nothing to share and the call is a plain decode.
+  const int members =
+      prefix_group ? (max_group_size < pa::kGroupedMaxSlots / group ? max_group_size
+                                                                     : pa::kGroupedMaxSlots / group)
+                   : 0;
+  a.prefix_group = members >= 2 ? prefix_group : nullptr;
+  a.group_members = members >= 2 ? members : 0;
   const size_t rows = (size_t)num_seqs * num_heads * nparts;
   a.part_o = partition_size > 0 ? static_cast<float*>(workspace) : nullptr;
   a.part_lse = partition_size > 0 ? static_cast<float*>(workspace) + rows * head_dim : nullptr;
@@ -202,9 +217,25 @@ int pa_decode(void* out, const void* query, const void* key_cache, const void* v
               int partition_size, void* workspace, size_t workspace_bytes, pa_dtype dtype,
               hipStream_t stream) {
   return decode_impl(out, query, key_cache, value_cache, block_tables, context_lens,
-                     shared_prefix_blocks, num_seqs, num_heads, num_kv_heads, head_dim,
-                     block_size, max_blocks_per_seq, num_blocks, max_context_len, scale,
+                     shared_prefix_blocks, nullptr, 0, num_seqs, num_heads, num_kv_heads,
+                     head_dim, block_size, max_blocks_per_seq, num_blocks, max_context_len, scale,
                      partition_size, workspace, workspace_bytes, dtype, false, 1.f, 1.f, stream);
+}
+
+int pa_decode_shared_prefix(void* out, const void* query, const void* key_cache,
+                            const void* value_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, const int32_t* shared_prefix_blocks,
+                            const int32_t* prefix_group, int max_group_size, int num_seqs,
+                            int num_heads, int num_kv_heads, int head_dim, int block_size,
+                            int max_blocks_per_seq, int64_t num_blocks, int max_context_len,
+                            float scale, int partition_size, void* workspace,
+                            size_t workspace_bytes, pa_dtype dtype, hipStream_t stream) {
+  if (num_seqs > 0 && !prefix_group) return PA_ERR_NULL;
+  return decode_impl(out, query, key_cache, value_cache, block_tables, context_lens,
+                     shared_prefix_blocks, prefix_group, max_group_size, num_seqs, num_heads,
+                     num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                     max_context_len, scale, partition_size, workspace, workspace_bytes, dtype,
+                     false, 1.f, 1.f, stream);
 }
 
 int pa_decode_fp8(void* out, const void* query, const uint8_t* key_cache,
@@ -215,10 +246,27 @@ int pa_decode_fp8(void* out, const void* query, const uint8_t* key_cache,
                   float k_scale, float v_scale, int partition_size, void* workspace,
                   size_t workspace_bytes, pa_dtype dtype, hipStream_t stream) {
   return decode_impl(out, query, key_cache, value_cache, block_tables, context_lens,
-                     shared_prefix_blocks, num_seqs, num_heads, num_kv_heads, head_dim,
-                     block_size, max_blocks_per_seq, num_blocks, max_context_len, scale,
+                     shared_prefix_blocks, nullptr, 0, num_seqs, num_heads, num_kv_heads,
+                     head_dim, block_size, max_blocks_per_seq, num_blocks, max_context_len, scale,
                      partition_size, workspace, workspace_bytes, dtype, true, k_scale, v_scale,
                      stream);
+}
+
+int pa_decode_fp8_shared_prefix(void* out, const void* query, const uint8_t* key_cache,
+                                const uint8_t* value_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, const int32_t* shared_prefix_blocks,
+                                const int32_t* prefix_group, int max_group_size, int num_seqs,
+                                int num_heads, int num_kv_heads, int head_dim, int block_size,
+                                int max_blocks_per_seq, int64_t num_blocks, int max_context_len,
+                                float scale, float k_scale, float v_scale, int partition_size,
+                                void* workspace, size_t workspace_bytes, pa_dtype dtype,
+                                hipStream_t stream) {
+  if (num_seqs > 0 && !prefix_group) return PA_ERR_NULL;
+  return decode_impl(out, query, key_cache, value_cache, block_tables, context_lens,
+                     shared_prefix_blocks, prefix_group, max_group_size, num_seqs, num_heads,
+                     num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                     max_context_len, scale, partition_size, workspace, workspace_bytes, dtype,
+                     true, k_scale, v_scale, stream);
 }
 
 int pa_decode_splitk_reduce(void* out, const void* workspace, size_t workspace_bytes,

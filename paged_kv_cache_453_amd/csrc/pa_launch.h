@@ -34,6 +34,11 @@ struct DecodeArgs {
   const int32_t* context_lens;
   const int32_t* query_start_loc;  // non-null: one work item per prefill query token
   const int32_t* shared_prefix_blocks;  // optional per-sequence cache hint (decode only)
+  // Decode only, optional: prefix_group[s] = first sequence of s's sharing
+  // group.  Windows of group_members (>= 2) consecutive members read their
+  // common full partitions once, in the grouped pass (decode_valu.h).
+  const int32_t* prefix_group;
+  int group_members;
   float* part_o;
   float* part_lse;
   int num_seqs;
@@ -50,6 +55,11 @@ struct DecodeArgs {
   float scale_log2;       // softmax scale * log2(e) (times the K scale for FP8 caches)
   float v_scale;          // FP8 caches: the V scale, applied to the output
 };
+
+// Query slots (sharing members x query heads per kv head) of one grouped-pass
+// workgroup: its registers hold that many accumulators, and 4 keeps two waves
+// per SIMD.
+constexpr int kGroupedMaxSlots = 4;
 
 struct ReduceArgs {
   void* out;

@@ -82,6 +82,13 @@ def load() -> ctypes.CDLL:
     lib.pa_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64,
                                   i32, f32, f32, f32, i32, vp, sz, i32, vp]
     lib.pa_decode_fp8.restype = i32
+    lib.pa_decode_shared_prefix.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                            i32, i32, i32, i64, i32, f32, i32, vp, sz, i32, vp]
+    lib.pa_decode_shared_prefix.restype = i32
+    lib.pa_decode_fp8_shared_prefix.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                                i32, i32, i32, i32, i64, i32, f32, f32, f32, i32,
+                                                vp, sz, i32, vp]
+    lib.pa_decode_fp8_shared_prefix.restype = i32
     lib.pa_sample.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp, vp, i32, vp]
     lib.pa_sample.restype = i32
     lib.pa_copy_blocks.argtypes = [vp, vp, vp, i64, i32, i32, i32, i64, i32, vp]
@@ -128,7 +135,8 @@ def load() -> ctypes.CDLL:
 
 EXPORTED = ("pa_reshape_and_cache", "pa_decode_workspace_bytes", "pa_decode",
             "pa_decode_splitk_reduce", "pa_prefill_chunk", "pa_reshape_and_cache_fp8",
-            "pa_decode_fp8", "pa_prefill_chunk_fp8", "pa_sample", "pa_copy_blocks",
+            "pa_decode_fp8", "pa_prefill_chunk_fp8", "pa_decode_shared_prefix",
+            "pa_decode_fp8_shared_prefix", "pa_sample", "pa_copy_blocks",
             "pa_swap_blocks", "pa_stream_read_sink_words", "pa_stream_read", "pa_status_string")
 
 
@@ -236,6 +244,74 @@ def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, sc
         _ptr(context_lens), _ptr(shared_prefix_blocks), s, hq, hkv, d, bs, block_tables.shape[1],
         nb, int(max_context_len),
         float(scale), int(partition_size), ws_ptr, ws_bytes, _dtype_code(query), _stream(stream)))
+
+
+def _decode_marshal(out, query, key_cache, value_cache, block_tables, context_lens,
+                    workspace, shared_prefix_blocks, prefix_group=None, fp8: bool = False):
+    """Shape / dtype checks shared by the decode wrappers; returns (S, Hq, D, NB, Hkv, BS,
+    workspace pointer, workspace bytes)."""
+    torch = _torch()
+    _on_gpu(out, query, key_cache, value_cache, block_tables, context_lens)
+    _need(block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32,
+          "block_tables and context_lens must be int32")
+    if fp8:
+        _need(key_cache.dtype == torch.uint8 and value_cache.dtype == torch.uint8,
+              "FP8 caches are uint8 tensors of E4M3 codes")
+    s, hq, d = query.shape
+    nb, hkv, bs, d2 = key_cache.shape
+    _need(d2 == d and tuple(out.shape) == (s, hq, d) and value_cache.shape == key_cache.shape,
+          "shape mismatch")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == s and context_lens.numel() == s,
+          "block_tables must be [S, MB] and context_lens [S]")
+    if fp8:
+        _need(out.dtype == query.dtype, "query and output dtypes differ")
+    else:
+        _need(out.dtype == query.dtype == key_cache.dtype == value_cache.dtype, "dtype mismatch")
+    for name, t in (("shared_prefix_blocks", shared_prefix_blocks), ("prefix_group", prefix_group)):
+        if t is not None:
+            _on_gpu(t)
+            _need(t.dtype == torch.int32 and t.numel() == s, f"{name} must be int32 [S]")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _on_gpu(workspace)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    return s, hq, d, nb, hkv, bs, ws_ptr, ws_bytes
+
+
+def pa_decode_shared_prefix(out, query, key_cache, value_cache, block_tables, context_lens,
+                            scale: float, max_context_len: int, partition_size: int, workspace,
+                            shared_prefix_blocks, prefix_group, max_group_size: int,
+                            stream=None) -> None:
+    """pa_decode for groups of sequences sharing leading blocks: prefix_group int32 [S] names
+    each sequence's group leader, shared_prefix_blocks int32 [S] the shared table entries
+    (see include/pa.h).  Follow with pa_decode_splitk_reduce."""
+    lib = load()
+    s, hq, d, nb, hkv, bs, ws_ptr, ws_bytes = _decode_marshal(
+        out, query, key_cache, value_cache, block_tables, context_lens, workspace,
+        shared_prefix_blocks, prefix_group)
+    _check("pa_decode_shared_prefix", lib.pa_decode_shared_prefix(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), _ptr(shared_prefix_blocks), _ptr(prefix_group), int(max_group_size),
+        s, hq, hkv, d, bs, block_tables.shape[1], nb, int(max_context_len), float(scale),
+        int(partition_size), ws_ptr, ws_bytes, _dtype_code(query), _stream(stream)))
+
+
+def pa_decode_fp8_shared_prefix(out, query, key_cache, value_cache, block_tables, context_lens,
+                                scale: float, k_scale: float, v_scale: float,
+                                max_context_len: int, partition_size: int, workspace,
+                                shared_prefix_blocks, prefix_group, max_group_size: int,
+                                stream=None) -> None:
+    """pa_decode_shared_prefix over uint8 E4M3 caches (codes stand for value * k/v scale)."""
+    lib = load()
+    s, hq, d, nb, hkv, bs, ws_ptr, ws_bytes = _decode_marshal(
+        out, query, key_cache, value_cache, block_tables, context_lens, workspace,
+        shared_prefix_blocks, prefix_group, fp8=True)
+    _check("pa_decode_fp8_shared_prefix", lib.pa_decode_fp8_shared_prefix(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), _ptr(shared_prefix_blocks), _ptr(prefix_group), int(max_group_size),
+        s, hq, hkv, d, bs, block_tables.shape[1], nb, int(max_context_len), float(scale),
+        float(k_scale), float(v_scale), int(partition_size), ws_ptr, ws_bytes,
+        _dtype_code(query), _stream(stream)))
 
 
 def pa_decode_splitk_reduce(out, workspace, context_lens, max_context_len: int,

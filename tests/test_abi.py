@@ -267,3 +267,31 @@ def test_fp8_prefill_validation(lib):
     bad = list(args)
     bad[2] = None
     assert f(*bad) == PA_ERR_NULL
+
+
+def shared_decode(lib, fp8=False, **kw):
+    args = dict(out=P, query=P, k=P, v=P, bt=P, cl=P, shared=P, group=P, maxg=3, S=4, hq=8, hkv=8,
+                d=128, bs=16, mb=4, nb=64, maxc=64, scale=0.1, ps=16, ws=None, wsb=0, dtype=BF16,
+                stream=None)
+    args.update(kw)
+    a = args
+    head = (a["out"], a["query"], a["k"], a["v"], a["bt"], a["cl"], a["shared"], a["group"],
+            a["maxg"], a["S"], a["hq"], a["hkv"], a["d"], a["bs"], a["mb"], a["nb"], a["maxc"],
+            a["scale"])
+    tail = (a["ps"], a["ws"], a["wsb"], a["dtype"], a["stream"])
+    if fp8:
+        return lib.pa_decode_fp8_shared_prefix(*head, 0.5, 0.5, *tail)
+    return lib.pa_decode_shared_prefix(*head, *tail)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_shared_prefix_decode_validation(lib, fp8):
+    need = lib.pa_decode_workspace_bytes(4, 8, 128, 64, 16)
+    assert shared_decode(lib, fp8, group=None) == PA_ERR_NULL
+    assert shared_decode(lib, fp8, shared=None, ws=P, wsb=need) == PA_ERR_NULL
+    assert shared_decode(lib, fp8, ps=0) == PA_ERR_SHAPE          # grouped partials need split-K
+    assert shared_decode(lib, fp8, maxg=0) == PA_ERR_SHAPE
+    assert shared_decode(lib, fp8, d=96, ws=P, wsb=need) == PA_ERR_UNSUPPORTED
+    assert shared_decode(lib, fp8, ws=None) == PA_ERR_WORKSPACE
+    assert shared_decode(lib, fp8, ws=P, wsb=need - 1) == PA_ERR_WORKSPACE
+    assert shared_decode(lib, fp8, S=0, out=None, query=None, group=None) == PA_OK

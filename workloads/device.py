@@ -55,6 +55,7 @@ class DeviceGroup:
     max_context_len: int = 0
     max_query_len: int = 0
     shared_prefix_blocks: Optional[object] = None
+    prefix_group: Optional[object] = None
 
 
 @dataclass
@@ -115,8 +116,11 @@ def _group(g, dtype, hq, d, device):
     shared = None
     if g.shared_prefix_blocks is not None:
         shared = torch.from_numpy(g.shared_prefix_blocks.astype(np.int32)).to(device)
+    group = None
+    if g.prefix_group is not None:
+        group = torch.from_numpy(g.prefix_group.astype(np.int32)).to(device)
     return DeviceGroup(
-        shared_prefix_blocks=shared,
+        shared_prefix_blocks=shared, prefix_group=group,
         context_lens=torch.from_numpy(g.context_lens.astype(np.int32)).to(device),
         block_tables=torch.from_numpy(g.block_tables.astype(np.int32)).to(device),
         query=q, out=out, query_start_loc=qsl, max_context_len=g.max_context_len,

@@ -207,6 +207,9 @@ class SeqGroup:
     # int32 [S] (decode only): leading table entries whose physical blocks other
     # sequences of the batch also hold -- a cache hint the kernels may use
     shared_prefix_blocks: Optional[np.ndarray] = None
+    # int32 [S] (decode only): first sequence of each sequence's sharing group
+    # (itself when it shares with no earlier sequence of the batch)
+    prefix_group: Optional[np.ndarray] = None
 
     @property
     def num_seqs(self) -> int:
@@ -482,7 +485,9 @@ def config4(seed: Optional[int] = None, dtype: str = "bf16", num_prompts: int = 
                  num_kv_heads=heads, head_dim=head_dim, num_blocks=num_blocks,
                  scale=_scale(head_dim), host_ids=ids, k_host=k, v_host=v,
                  decode=SeqGroup(context_lens=dec_lens, block_tables=dec_tables, query=dec_q,
-                                 shared_prefix_blocks=np.full(n_dec, nsh, dtype=np.int32)),
+                                 shared_prefix_blocks=np.full(n_dec, nsh, dtype=np.int32),
+                                 prefix_group=(np.arange(n_dec) // samples * samples
+                                               ).astype(np.int32)),
                  prefill=SeqGroup(context_lens=pre_lens, block_tables=pre_tables, query=pre_q,
                                   query_start_loc=qsl),
                  partition_size=partition_size)
@@ -541,7 +546,8 @@ def permute_block_ids(w: Workload, seed: int) -> Workload:
         g = getattr(w, name)
         if g is not None:
             setattr(w2, name, SeqGroup(g.context_lens, relabel(g.block_tables), g.query,
-                                       g.query_start_loc, g.shared_prefix_blocks))
+                                       g.query_start_loc, g.shared_prefix_blocks,
+                                       g.prefix_group))
     if w.slot_mapping is not None:
         s = w.slot_mapping
         w2.slot_mapping = np.where(s >= 0, pi[np.maximum(s, 0) // BLOCK_SIZE] * BLOCK_SIZE
