@@ -447,6 +447,17 @@ int64_t pa_bm_num_free(const pa_block_manager* bm, int host);
 int pa_bm_build_batch(const pa_block_manager* bm, const int64_t* seqs, int32_t num_seqs,
                       int32_t max_blocks_per_seq, int32_t* block_tables, int32_t* context_lens,
                       int32_t* shared_prefix_blocks);
+/* Sharing groups of a decode batch for pa_decode_shared_prefix, over resident sequences
+ * seqs[0..num_seqs-1] in batch order (host arrays of num_seqs entries).  A group is a run of
+ * consecutive entries whose tables start with the same physical block as the run's first entry
+ * -- samples forked from one prompt ("vLLM 基本原理", section 内存共享), or requests on one cached
+ * prefix (xdnf.cn article, section 六.3) -- so the caller places sharers next to each other.
+ * prefix_group[i] = index of the run's first entry; group_blocks[i] = for a member, its leading
+ * table entries equal to the first entry's, for the first entry the largest of its members'
+ * counts (0 in a group of one).  Pass group_blocks as pa_decode_shared_prefix's
+ * shared_prefix_blocks; *max_group_size (optional) receives the largest run. */
+int pa_bm_prefix_groups(const pa_block_manager* bm, const int64_t* seqs, int32_t num_seqs,
+                        int32_t* prefix_group, int32_t* group_blocks, int32_t* max_group_size);
 /* Checks the invariants (reference counts = table occurrences, free + held-back blocks =
  * unreferenced ones, table lengths = ceil(tokens / block_size), cache entries consistent):
  * PA_OK or PA_ERR_STATE. */

@@ -496,6 +496,37 @@ class BlockManager:
             n += 1
         return n
 
+    def prefix_groups(self, seqs):
+        """Sharing groups of a decode batch in batch order: each run of consecutive
+        entries whose tables start with the same physical block as the run's first
+        entry ("vLLM 基本原理", 内存共享: samples of one prompt name its blocks) is a
+        group led by that entry.  Returns (leader index per entry, count per entry,
+        largest run): a member's count is its leading table entries equal to the
+        leader's, the leader's the largest of its members' counts (0 alone)."""
+        for s in seqs:
+            self._resident(s)
+        n = len(seqs)
+        group, count = [0] * n, [0] * n
+        largest = 1 if n else 0
+        i = 0
+        while i < n:
+            lead = self.tables[seqs[i]]
+            end = i + 1
+            while end < n and lead and self.tables[seqs[end]] and \
+                    self.tables[seqs[end]][0] == lead[0]:
+                end += 1
+            group[i] = i
+            for m in range(i + 1, end):
+                t = self.tables[seqs[m]]
+                k = 0
+                while k < len(t) and k < len(lead) and t[k] == lead[k]:
+                    k += 1
+                group[m], count[m] = i, k
+            count[i] = max(count[i + 1:end], default=0)
+            largest = max(largest, end - i)
+            i = end
+        return group, count, largest
+
     def check_invariants(self) -> None:
         """Reference counts equal table occurrences; free plus held-back blocks
         are exactly the unreferenced ones; only last blocks may be partly

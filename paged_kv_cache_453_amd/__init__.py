@@ -14,7 +14,7 @@ from .lib import (pa_decode, pa_decode_splitk_reduce, pa_decode_workspace_bytes,
                   pa_bm_free_sequence, pa_bm_append_slots, pa_bm_append_batch, pa_bm_swap_out,
                   pa_bm_swap_in, pa_bm_pending_moves, pa_bm_take_moves, pa_bm_num_tokens,
                   pa_bm_is_swapped, pa_bm_block_table, pa_bm_num_free, pa_bm_build_batch,
-                  pa_bm_check, pa_bm_prefix_keys, pa_bm_add_prompt, pa_bm_append_tokens,
+                  pa_bm_check, pa_bm_prefix_groups, pa_bm_prefix_keys, pa_bm_add_prompt, pa_bm_append_tokens,
                   pa_bm_num_cached_blocks, BlockManager, Busy, OutOfBlocks, PagedAttentionError,
                   SequenceError, ShapeError)
 
@@ -27,6 +27,6 @@ __all__ = ["lib", "pa_decode", "pa_decode_splitk_reduce", "pa_decode_workspace_b
            "pa_bm_free_sequence", "pa_bm_append_slots", "pa_bm_append_batch", "pa_bm_swap_out",
            "pa_bm_swap_in", "pa_bm_pending_moves", "pa_bm_take_moves", "pa_bm_num_tokens",
            "pa_bm_is_swapped", "pa_bm_block_table", "pa_bm_num_free", "pa_bm_build_batch",
-           "pa_bm_check", "pa_bm_prefix_keys", "pa_bm_add_prompt", "pa_bm_append_tokens",
+           "pa_bm_check", "pa_bm_prefix_groups", "pa_bm_prefix_keys", "pa_bm_add_prompt", "pa_bm_append_tokens",
            "pa_bm_num_cached_blocks", "BlockManager", "Busy", "OutOfBlocks", "PagedAttentionError",
            "SequenceError", "ShapeError"]

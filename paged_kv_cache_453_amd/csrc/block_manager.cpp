@@ -698,6 +698,43 @@ int pa_bm_build_batch(const pa_block_manager* bm, const int64_t* seqs, int32_t n
   return PA_OK;
 }
 
+int pa_bm_prefix_groups(const pa_block_manager* bm, const int64_t* seqs, int32_t num_seqs,
+                        int32_t* prefix_group, int32_t* group_blocks, int32_t* max_group_size) {
+  if (!bm) return PA_ERR_NULL;
+  if (num_seqs < 0) return PA_ERR_SHAPE;
+  if (num_seqs > 0 && (!seqs || !prefix_group || !group_blocks)) return PA_ERR_NULL;
+  std::vector<const Sequence*> ss((size_t)num_seqs);
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    ss[(size_t)i] = bm->find(seqs[i]);
+    if (!ss[(size_t)i] || ss[(size_t)i]->on_host) return PA_ERR_SEQ;
+  }
+  int32_t largest = num_seqs > 0 ? 1 : 0;
+  for (int32_t i = 0; i < num_seqs;) {
+    // a run of consecutive entries whose tables start with entry i's first block
+    const std::vector<int32_t>& lead = ss[(size_t)i]->table;
+    int32_t end = i + 1;
+    while (end < num_seqs && !lead.empty() && !ss[(size_t)end]->table.empty() &&
+           ss[(size_t)end]->table[0] == lead[0])
+      ++end;
+    int32_t most = 0;
+    for (int32_t m = i + 1; m < end; ++m) {
+      const std::vector<int32_t>& t = ss[(size_t)m]->table;
+      int32_t n = 0;
+      while (n < (int32_t)t.size() && n < (int32_t)lead.size() && t[(size_t)n] == lead[(size_t)n])
+        ++n;
+      prefix_group[m] = i;
+      group_blocks[m] = n;
+      most = std::max(most, n);
+    }
+    prefix_group[i] = i;
+    group_blocks[i] = most;
+    largest = std::max(largest, end - i);
+    i = end;
+  }
+  if (max_group_size) *max_group_size = largest;
+  return PA_OK;
+}
+
 int pa_bm_check(const pa_block_manager* bm) {
   if (!bm) return PA_ERR_NULL;
   for (int side = 0; side < 2; ++side) {

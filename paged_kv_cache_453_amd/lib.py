@@ -122,6 +122,7 @@ def load() -> ctypes.CDLL:
             ("pa_bm_num_free", [vp, i32], i64),
             ("pa_bm_build_batch", [vp, vp, i32, i32, vp, vp, vp], i32),
             ("pa_bm_check", [vp], i32),
+            ("pa_bm_prefix_groups", [vp, vp, i32, vp, vp, vp], i32),
             ("pa_bm_prefix_keys", [vp, i64, ctypes.c_uint64, vp], i32),
             ("pa_bm_add_prompt", [vp, i64, vp, i64, ctypes.c_uint64, vp], i32),
             ("pa_bm_append_tokens", [vp, i64, vp, i32, vp], i32),
@@ -645,6 +646,20 @@ def pa_bm_build_batch(h, seqs, max_blocks_per_seq: int):
     return tables, lens, shared
 
 
+def pa_bm_prefix_groups(h, seqs):
+    """(prefix_group int32 [S], group_blocks int32 [S], max_group_size) of a decode batch, for
+    pa_decode_shared_prefix (group_blocks goes in as its shared_prefix_blocks)."""
+    np = _np()
+    s, sp = _i64s(seqs)
+    group = np.empty(s.size, dtype=np.int32)
+    blocks = np.empty(s.size, dtype=np.int32)
+    largest = ctypes.c_int32()
+    _check("pa_bm_prefix_groups", load().pa_bm_prefix_groups(
+        h, sp, s.size, group.ctypes.data if s.size else None,
+        blocks.ctypes.data if s.size else None, ctypes.byref(largest)))
+    return group, blocks, int(largest.value)
+
+
 def pa_bm_check(h) -> None:
     _check("pa_bm_check", load().pa_bm_check(h))
 
@@ -724,6 +739,9 @@ class BlockManager:
 
     def build_batch(self, seqs, max_blocks_per_seq):
         return pa_bm_build_batch(self._h, seqs, max_blocks_per_seq)
+
+    def prefix_groups(self, seqs):
+        return pa_bm_prefix_groups(self._h, seqs)
 
     def shared_prefix_blocks(self, seq):
         n = max(1, len(self.block_table(seq)))

@@ -295,3 +295,21 @@ def test_shared_prefix_decode_validation(lib, fp8):
     assert shared_decode(lib, fp8, ws=None) == PA_ERR_WORKSPACE
     assert shared_decode(lib, fp8, ws=P, wsb=need - 1) == PA_ERR_WORKSPACE
     assert shared_decode(lib, fp8, S=0, out=None, query=None, group=None) == PA_OK
+
+
+def test_prefix_groups_validation(lib):
+    import ctypes
+    h = ctypes.c_void_p()
+    assert lib.pa_bm_create(64, 0, 16, ctypes.byref(h)) == PA_OK
+    try:
+        assert lib.pa_bm_prefix_groups(None, P, 1, P, P, None) == PA_ERR_NULL
+        assert lib.pa_bm_prefix_groups(h, P, -1, P, P, None) == PA_ERR_SHAPE
+        assert lib.pa_bm_prefix_groups(h, P, 1, None, P, None) == PA_ERR_NULL
+        seq = (ctypes.c_int64 * 1)(7)
+        g, b = (ctypes.c_int32 * 1)(), (ctypes.c_int32 * 1)()
+        assert lib.pa_bm_prefix_groups(h, seq, 1, g, b, None) == -7        # PA_ERR_SEQ
+        n = ctypes.c_int32(-1)
+        assert lib.pa_bm_prefix_groups(h, None, 0, None, None, ctypes.byref(n)) == PA_OK
+        assert n.value == 0
+    finally:
+        lib.pa_bm_destroy(h)

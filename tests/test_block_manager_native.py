@@ -34,6 +34,13 @@ def compare(o, n, live):
         assert o.is_swapped(s) == n.is_swapped(s)
         if not o.is_swapped(s):
             assert o.shared_prefix_blocks(s) == n.shared_prefix_blocks(s)
+    # sharing groups of the resident sequences, in live order and sorted by first block
+    res = [s for s in live if not o.is_swapped(s)]
+    by_first = sorted(res, key=lambda s: (o.block_table(s)[:1], s))
+    for batch in (res, by_first):
+        og, oc, om = o.prefix_groups(batch)
+        ng, nc, nm = n.prefix_groups(batch)
+        assert og == ng.tolist() and oc == nc.tolist() and om == nm
 
 
 def moves_equal(mo, mn):

@@ -371,3 +371,35 @@ def test_copy_and_swap_are_plain_block_copies():
     h2 = swap_blocks(pool, host, [(9, 0), (3, 2)])
     assert np.array_equal(h2[0], pool[9]) and np.array_equal(h2[2], pool[3])
     assert not h2[[1, 3]].any()
+
+
+def test_prefix_groups_of_forked_samples_and_shared_prefixes():
+    """Sharing groups for the grouped decode, worked by hand: seq 0 has three
+    full blocks and two forked samples (one of which has moved on to a fourth,
+    private block), seq 4 shares seq 3's first block, seq 5 shares nothing."""
+    bm = BlockManager(32, 16)
+    bm.add_sequence(0)
+    bm.append_slots(0, 48)
+    bm.take_moves()
+    bm.fork(0, 1)
+    bm.fork(0, 2)
+    bm.take_moves()
+    bm.append_slots(1, 1)                    # a fourth block, private to seq 1
+    bm.add_sequence(3)
+    bm.append_slots(3, 20)
+    bm.take_moves()
+    bm.share(3, 4, [0])
+    bm.add_sequence(5)
+    bm.append_slots(5, 5)
+    bm.add_sequence(6)                       # no blocks yet
+    bm.take_moves()
+    t = {s: bm.block_table(s) for s in range(7) if s != 6}
+    assert t[1][:3] == t[0] == t[2] and len(t[1]) == 4 and t[4] == t[3][:1]
+    assert bm.prefix_groups([0, 1, 2, 3, 4, 5]) == ([0, 0, 0, 3, 3, 5], [3, 3, 3, 1, 1, 0], 3)
+    # a group is a run of neighbours: seq 2 after seq 5 starts a run of its own
+    assert bm.prefix_groups([1, 0, 5, 2]) == ([0, 0, 2, 3], [3, 3, 0, 0], 2)
+    # an empty table leads nobody and joins nobody
+    assert bm.prefix_groups([6, 0, 6]) == ([0, 1, 2], [0, 0, 0], 1)
+    assert bm.prefix_groups([]) == ([], [], 0)
+    with pytest.raises(KeyError):
+        bm.prefix_groups([0, 99])

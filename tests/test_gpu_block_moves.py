@@ -279,6 +279,43 @@ class Steps:
         assert_close(as_f64(out), want, self.dtype, f"decode after moves {seqs}")
 
 
+    def decode_grouped(self, seqs, partition_size):
+        """The manager's sharing groups drive pa_decode_shared_prefix: the output
+        must be pa_decode's bit for bit, and the oracle's within tolerance."""
+        torch = self.torch
+        mb = max(len(self.o.block_table(s)) for s in seqs) + 1
+        tables, lens, shared = self.n.build_batch(seqs, mb)
+        og, oc, om = self.o.prefix_groups(seqs)
+        ng, nc, nm = self.n.prefix_groups(seqs)
+        assert og == ng.tolist() and oc == nc.tolist() and om == nm
+        q = normal_storage(self.rng, (len(seqs), self.hq, self.d), self.dtype)
+        qt = host_to_torch(q, self.dtype, "cuda")
+        maxc = int(lens.max())
+        nbytes = self.L.pa_decode_workspace_bytes(len(seqs), self.hq, self.d, maxc,
+                                                  partition_size)
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+        bt, cl, sh, grp, gb = (torch.from_numpy(x).cuda() for x in (tables, lens, shared, ng, nc))
+        outs = []
+        for grouped in (False, True):
+            out = torch.empty_like(qt)
+            ws.fill_(0xFF)
+            if grouped:
+                self.L.pa_decode_shared_prefix(out, qt, self.kc, self.vc, bt, cl,
+                                               float(self.scale), maxc, partition_size, ws, gb,
+                                               grp, nm)
+            else:
+                self.L.pa_decode(out, qt, self.kc, self.vc, bt, cl, float(self.scale), maxc,
+                                 partition_size, ws, shared_prefix_blocks=sh)
+            self.L.pa_decode_splitk_reduce(out, ws, cl, maxc, partition_size)
+            torch.cuda.synchronize()
+            outs.append(out)
+        view = torch.int16 if self.dtype == "bf16" else torch.int32
+        assert torch.equal(outs[0].view(view), outs[1].view(view))
+        want = oracle.decode(q, self.ok, self.ov, tables, lens, self.scale, self.dtype)
+        assert_close(as_f64(outs[1]), want, self.dtype, f"grouped decode {seqs}")
+        return nm
+
+
 @pytest.mark.parametrize("dtype,hq,hkv,d", [("bf16", 32, 8, 128), ("f32", 4, 4, 64),
                                             ("bf16", 8, 8, 128)])
 def test_manager_driven_steps(gpu, dtype, hq, hkv, d):
@@ -310,6 +347,11 @@ def test_manager_driven_steps(gpu, dtype, hq, hkv, d):
     st.check_pools()
     st.decode(live)
     st.decode(live, partition_size=32)
+    # sharers next to each other: samples after their prompt, seq 30 (seq 2's
+    # first three blocks) with seq 2's samples
+    order = [0, 10, 11, 1, 12, 13, 2, 30, 14, 15, 3, 16, 17, 31]
+    assert sorted(order) == sorted(live)
+    assert st.decode_grouped(order, 32) == 4
     for s in (0, 12, 30, 2):
         st.both("append_slots", s, 7)
     st.run_moves()
