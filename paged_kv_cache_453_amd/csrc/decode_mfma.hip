@@ -12,11 +12,14 @@
 // only take the arithmetic off the vector ALUs so that the loads are never
 // starved.
 //
-// Work decomposition.  One wave per (sequence, kv head, partition); a
-// workgroup holds the 4 waves of 4 consecutive kv heads of the same sequence
-// and partition, so they walk the same block ids and read neighbouring 4 KiB
+// Work decomposition.  One wave per (sequence, kv head, partition), and one
+// wave per workgroup, kv heads fastest in launch order: the waves of one
+// (sequence, partition) walk the same block ids and read neighbouring 4 KiB
 // head slabs.  Waves never exchange data: each owns its heads' whole softmax
-// state, and partitions meet in the split-K merge.
+// state, and partitions meet in the split-K merge.  Single-wave workgroups
+// measured faster than workgroups of 2, 4 or 8 kv heads (476 / 495 / 503 /
+// 534 us on the Llama-3-8B-shaped batch, 254 / 274 / 284 / 295 us over an FP8
+// cache).
 //
 // Operand layouts (v_mfma_f32_16x16x32_bf16 for scores, v_mfma_f32_16x16x16_bf16
 // for p.V).  In both, lane l = 16 g + r supplies row/column r and reduction
@@ -63,7 +66,7 @@ namespace pa {
 namespace {
 
 constexpr int kD = 128;          // head_dim handled here
-constexpr int kHeadsPerWG = 4;   // kv heads (= waves) per workgroup
+constexpr int kHeadsPerWG = 1;   // kv heads (= waves) per workgroup
 constexpr float kRescaleSlack = 8.f;   // base-2 headroom of the lazy softmax rescale
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -250,7 +253,7 @@ __device__ __forceinline__ void consume_mfma_slab(MfmaSlab& sl, const u32x4 (&qb
 // shared_prefix_blocks, so batches of shared blocks take the caching load path;
 // without it only the streaming path is compiled.
 template <typename KV, bool HINT>
-__global__ __launch_bounds__(256) void decode_gqa_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kHeadsPerWG) void decode_gqa_mfma_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t sh_k[kHeadsPerWG][kKTileBytes];
   const int hgroups = (a.num_kv_heads + kHeadsPerWG - 1) / kHeadsPerWG;
   const int seq = blockIdx.x / hgroups;
