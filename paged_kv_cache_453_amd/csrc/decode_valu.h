@@ -373,7 +373,7 @@ __device__ __forceinline__ int grouped_parts(const DecodeArgs& a, int s) {
 // kvh*G + g % G of member s + g / G, and a member whose table names other
 // blocks there gets NaN (it broke the grouping contract).
 template <typename T, typename KV, int D, int GP, bool HINT, bool GROUPED>
-__global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kWavesPerGroup) void decode_valu_kernel(DecodeArgs a) {
   constexpr int E = ElemTraits<KV>::kPerLoad;  // cache elements per 16-byte load
   constexpr int LPR = D / E;                   // lanes per token row
   constexpr int RPL = kWave / LPR;             // token rows per wave-wide load
@@ -647,7 +647,7 @@ constexpr int kFp8ValuMaxGroup = 4;
 
 template <typename T, typename KV, int D, bool HINT>
 inline void launch_decode_group(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
-  const dim3 block(256);
+  const dim3 block(64 * kWavesPerGroup);
   const int G = a.group;
   if (G <= 1)
     hipLaunchKernelGGL((decode_valu_kernel<T, KV, D, 1, HINT, false>), grid, block, 0, stream, a);
@@ -668,7 +668,7 @@ inline void launch_decode_group(const DecodeArgs& a, dim3 grid, hipStream_t stre
 // The grouped pass, with the fewest slots that hold a window's queries.
 template <typename T, typename KV, int D>
 inline void launch_decode_grouped(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
-  const dim3 block(256);
+  const dim3 block(64 * kWavesPerGroup);
   const int slots = a.group_members * a.group;
   if (slots <= 2)
     hipLaunchKernelGGL((decode_valu_kernel<T, KV, D, 2, false, true>), grid, block, 0, stream, a);
