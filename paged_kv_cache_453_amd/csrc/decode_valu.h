@@ -393,7 +393,12 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_valu_kernel(Decode
   // HBM accesses of concurrently running waves close together.
   const int item = blockIdx.x / a.num_kv_heads;
   const int kvh = blockIdx.x - item * a.num_kv_heads;
-  const int part = blockIdx.y;
+  // The regular pass of a grouped call takes the partitions last first: its
+  // leading partitions are mostly the grouped ones it skips, and dispatched
+  // last their empty workgroups fill the launch's tail instead of holding
+  // slots the live ones need.  Otherwise the first (longest) partitions go first.
+  const int part = (!GROUPED && a.prefix_group != nullptr) ? gridDim.y - 1 - blockIdx.y
+                                                           : blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = wave_uniform(threadIdx.x >> 6);
   const int r = lane / LPR;
