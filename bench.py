@@ -69,6 +69,25 @@ COUNTED = {
                     for f in ("decode_valu.h", "decode_valu_bf16.hip", "pa_device.h")],
         "bench": "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
         "dir": "pmc", "out": "bench"},
+    # one pa_decode_shared_prefix call on the mixed workload's decoders: the grouped
+    # pass and the regular pass, summed per call
+    "mixed_decode": {
+        "json": os.path.join(ROOT, "profiles", "decode_mixed_counters.json"),
+        "kernel": ["void pa::decode_valu_kernel<unsigned short, unsigned short, 128, 3, false, true>",
+                   "void pa::decode_valu_kernel<unsigned short, unsigned short, 128, 1, true, false>"],
+        "sources": [os.path.join(_CSRC, f)
+                    for f in ("decode_valu.h", "decode_valu_bf16.hip", "pa_device.h")],
+        "bench": "python3 bench.py --workload mixed --decode-only --steps 3 --warmup 1",
+        "dir": "pmc_mixed", "out": "mixed"},
+    # the same decoders through pa_decode (each sample reads the shared prefix itself)
+    "mixed_decode_plain": {
+        "json": os.path.join(ROOT, "profiles", "decode_mixed_plain_counters.json"),
+        "kernel": ["void pa::decode_valu_kernel<unsigned short, unsigned short, 128, 1, true, false>"],
+        "sources": [os.path.join(_CSRC, f)
+                    for f in ("decode_valu.h", "decode_valu_bf16.hip", "pa_device.h")],
+        "bench": "python3 bench.py --workload mixed --decode-only --no-prefix-groups --steps 3 "
+                 "--warmup 1",
+        "dir": "pmc_mixed_plain", "out": "mixed"},
     "copy": {
         "json": os.path.join(ROOT, "profiles", "copy_blocks_13b_counters.json"),
         "kernel": "void pa::move_blocks_kernel<unsigned int __vector(4), pa::DeviceMapping>",
@@ -196,8 +215,10 @@ def digest_counters(kind: str, fetch_csv: str, write_csv: str, copy_fetch_csv: s
     spec = COUNTED[kind]
     k = spec["kernel"]
     copy = "__amd_rocclr_copyBuffer"
-    f_k = statistics.mean(_counter_rows(fetch_csv, k))
-    w_k = statistics.mean(_counter_rows(write_csv, k))
+    # several kernels: one launch of each per call, the call's traffic is their sum
+    ks = k if isinstance(k, list) else [k]
+    f_k = sum(statistics.mean(_counter_rows(fetch_csv, x)) for x in ks)
+    w_k = sum(statistics.mean(_counter_rows(write_csv, x)) for x in ks)
     f_copy = statistics.mean(_counter_rows(copy_fetch_csv, copy))
     w_copy = statistics.mean(_counter_rows(copy_write_csv, copy))
     f_scale = copy_bytes / (f_copy * 1024)
@@ -668,6 +689,9 @@ def main(argv=None):
                     help="split-K partition length in tokens (default: 2048 for the Llama "
                          "shapes, 512 for gqa as its configuration states, 2048 for mixed)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only the decode call and its merge (for counter runs); prints "
+                         "a short JSON line")
     ap.add_argument("--no-prefix-groups", action="store_true",
                     help="mixed workloads: decode with pa_decode (each sample streams the "
                          "shared prefix itself) instead of pa_decode_shared_prefix")
@@ -803,6 +827,9 @@ def main(argv=None):
     if ps:
         launches.append(("splitk_reduce", reduce))
 
+    if args.decode_only:
+        launches = [(n, f) for n, f in launches if n in ("decode", "splitk_reduce")]
+
     def step():
         for _, fn in launches:
             fn()
@@ -816,6 +843,18 @@ def main(argv=None):
     kernel_ms = timer.per_launch(launches, args.steps, stream)
     log("bench: step %.1f us (%s)" % (ms_per_step * 1e3, ", ".join(
         f"{k} {v * 1e3:.1f}" for k, v in kernel_ms.items())))
+
+    if args.decode_only:
+        kv = accounting.decode_kv_bytes(g.context_lens, w.num_kv_heads, w.head_dim,
+                                        1 if fp8 else w.elem_bytes)
+        unique = accounting.unique_kv_bytes(g.block_tables, g.context_lens, w.num_kv_heads,
+                                            w.head_dim, 1 if fp8 else w.elem_bytes)
+        print(json.dumps({
+            "mode": "decode_only", "workload": args.workload, "partition_size": ps,
+            "entry_point": ("pa_decode_shared_prefix" if grouped else "pa_decode"),
+            "decode_us": round(kernel_ms["decode"] * 1e3, 2),
+            "kv_bytes_logical": int(kv), "kv_bytes_unique": int(unique)}), flush=True)
+        return 0
 
     if grouped:
         # the same decode without the grouped pass, for comparison
@@ -851,6 +890,9 @@ def main(argv=None):
         pf_tflops = flops / (kernel_ms["prefill"] * 1e-3) / 1e12
         unique_gbs = unique / (kernel_ms["decode"] * 1e-3) / 1e9
         # the decode of shared prefixes must read each physical row once at least
+        if args.workload == "mixed":
+            roofline["traffic"] = measured_traffic("mixed_decode" if grouped
+                                                   else "mixed_decode_plain")
         roofline.update({"achieved": round(unique_gbs, 2),
                          "frac": round(unique_gbs / HBM_PEAK_GBS, 4),
                          "algorithmic_bytes_per_launch": int(unique),
