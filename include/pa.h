@@ -154,8 +154,8 @@ int pa_decode(void* out, const void* query, const void* key_cache, const void* v
  * 基本原理", section 内存共享), and so do requests that hit one cached prefix
  * (xdnf.cn article, section 六.3).  Decode is bound by the bytes it streams
  * (xdnf.cn article, section 六.5), so here a split-K partition made only of
- * such blocks is streamed once and scored against the queries of up to four
- * sharers (query slots: members x query heads per kv head <= 4); each sharer
+ * such blocks is streamed once and scored against the queries of a window of
+ * sharers (see below for its size); each sharer
  * gets the same per-partition partial its own workgroup would have produced,
  * and pa_decode_splitk_reduce() merges them as usual.  Every argument of
  * pa_decode keeps its meaning, with these differences:
@@ -174,10 +174,13 @@ int pa_decode(void* out, const void* query, const void* key_cache, const void* v
  *                 pa_decode.
  *  max_group_size largest group (>= 1); it sets the members per workgroup.
  *  partition_size must be > 0 (the shared partitions are split-K partials).
- * Query-head groups larger than 2 (num_heads / num_kv_heads > 2) leave no
- * room for a second member: the call then computes exactly what pa_decode
- * computes.  The result equals pa_decode's bit for bit (same partitions, same
- * order of accumulation).
+ * A workgroup holds up to 4 query slots (members x query heads per kv head)
+ * on the vector-ALU path and 16 on the matrix-core path (bf16 query,
+ * head_dim 128, 4 or more query heads per kv head), so windows of up to
+ * 4 / G or 16 / G members share a read (G = num_heads / num_kv_heads); where
+ * fewer than two fit, the call computes exactly what pa_decode computes.  The
+ * result equals pa_decode's bit for bit (same partitions, same order of
+ * accumulation).
  */
 int pa_decode_shared_prefix(void* out, const void* query, const void* key_cache,
                             const void* value_cache, const int32_t* block_tables,

@@ -58,6 +58,7 @@
 
 #include <type_traits>
 
+#include "decode_groups.h"
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -252,13 +253,16 @@ __device__ __forceinline__ void consume_mfma_slab(MfmaSlab& sl, const u32x4 (&qb
 // KV: the cache element type (bf16, or fp8 codes).  HINT: the caller passed
 // shared_prefix_blocks, so batches of shared blocks take the caching load path;
 // without it only the streaming path is compiled.
-template <typename KV, bool HINT>
+template <typename KV, bool HINT, bool GROUPED>
 __global__ __launch_bounds__(64 * kHeadsPerWG) void decode_gqa_mfma_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t sh_k[kHeadsPerWG][kKTileBytes];
   const int hgroups = (a.num_kv_heads + kHeadsPerWG - 1) / kHeadsPerWG;
-  const int seq = blockIdx.x / hgroups;
-  const int kvh = (blockIdx.x - seq * hgroups) * kHeadsPerWG + wave_uniform(threadIdx.x >> 6);
-  const int part = blockIdx.y;
+  const int item = blockIdx.x / hgroups;
+  const int kvh = (blockIdx.x - item * hgroups) * kHeadsPerWG + wave_uniform(threadIdx.x >> 6);
+  // the regular pass of a grouped call takes the partitions last first (its
+  // leading ones are mostly grouped: their empty workgroups then fill the tail)
+  const int part = (!GROUPED && a.prefix_group != nullptr) ? gridDim.y - 1 - blockIdx.y
+                                                           : blockIdx.y;
   if (kvh >= a.num_kv_heads) return;
   const int lane = threadIdx.x & (kWave - 1);
   const int r = lane & 15;
@@ -267,48 +271,87 @@ __global__ __launch_bounds__(64 * kHeadsPerWG) void decode_gqa_mfma_kernel(Decod
   const int hq = a.num_heads;
   bf16_t* out = static_cast<bf16_t*>(a.out);
 
-  const int ctx = a.context_lens[seq];
-  const bool bad = ctx < 0 || ctx > a.max_blocks_per_seq * kBlock ||
-                   (a.partition_blocks > 0 && ctx > a.max_context_len);
-  const int nblk = bad ? 0 : (ctx + kBlock - 1) / kBlock;
-  const bool split = a.partition_blocks > 0;
-  const int nparts = split ? (nblk + a.partition_blocks - 1) / a.partition_blocks : 1;
-  if (part >= (nparts > 0 ? nparts : 1)) return;
+  // This wave folds blocks [jb, je) of `table` (tokens below tok_end).  Column
+  // r of the products is query head kvh*G + r of sequence item (regular), or
+  // query head kvh*G + r % G of member item + r / G of a sharing window
+  // (grouped: the blocks come from the leader's table, and a member whose
+  // table names other blocks there gets NaN).
+  int jb, je, tok_end, nparts = 1, nshared = 0;
+  const int32_t* table;
+  uint32_t active = 0;
+  if constexpr (GROUPED) {
+    const int M = a.group_members;
+    const int lead = a.prefix_group[item];
+    if (lead < 0 || lead > item || (item - lead) % M != 0) return;
+    for (int m = 0; m < M && item + m < a.num_seqs; ++m)
+      if (a.prefix_group[item + m] == lead && part < grouped_parts(a, item + m))
+        active |= 1u << m;
+    if (active == 0) return;
+    jb = part * a.partition_blocks;
+    je = jb + a.partition_blocks;
+    tok_end = je * kBlock;
+    table = a.block_tables + (int64_t)lead * a.max_blocks_per_seq;
+  } else {
+    const int ctx = a.context_lens[item];
+    const bool bad = ctx < 0 || ctx > a.max_blocks_per_seq * kBlock ||
+                     (a.partition_blocks > 0 && ctx > a.max_context_len);
+    const int nblk = bad ? 0 : (ctx + kBlock - 1) / kBlock;
+    const bool split = a.partition_blocks > 0;
+    nparts = split ? (nblk + a.partition_blocks - 1) / a.partition_blocks : 1;
+    if (part >= (nparts > 0 ? nparts : 1)) return;
+    if (part < grouped_parts(a, item)) return;   // the grouped pass wrote it
 
-  // Degenerate sequences (only partition 0 gets here): no context gives zeros,
-  // a violated contract gives NaN, in the partials too if the merge will read
-  // them.
-  if (bad || ctx == 0) {
-    const float fill = bad ? __builtin_nanf("") : 0.f;
-    if (split && bad && ctx > 0 && ctx <= a.max_context_len) {
-      const int ptok = a.partition_blocks * kBlock;
-      const int np_bad = (ctx + ptok - 1) / ptok;
-      if (np_bad > 1) {
-        for (int i = lane; i < np_bad * G * kD; i += kWave) {
-          const int p = i / (G * kD);
-          const int h = (i / kD) % G;
-          const int64_t row = ((int64_t)seq * hq + kvh * G + h) * a.max_partitions + p;
-          a.part_o[row * kD + i % kD] = fill;
-          if (i % kD == 0) a.part_lse[row] = fill;
+    // Degenerate sequences (only partition 0 gets here): no context gives zeros,
+    // a violated contract gives NaN, in the partials too if the merge will read
+    // them.
+    if (bad || ctx == 0) {
+      const float fill = bad ? __builtin_nanf("") : 0.f;
+      if (split && bad && ctx > 0 && ctx <= a.max_context_len) {
+        const int ptok = a.partition_blocks * kBlock;
+        const int np_bad = (ctx + ptok - 1) / ptok;
+        if (np_bad > 1) {
+          for (int i = lane; i < np_bad * G * kD; i += kWave) {
+            const int p = i / (G * kD);
+            const int h = (i / kD) % G;
+            const int64_t row = ((int64_t)item * hq + kvh * G + h) * a.max_partitions + p;
+            a.part_o[row * kD + i % kD] = fill;
+            if (i % kD == 0) a.part_lse[row] = fill;
+          }
+          return;
         }
-        return;
       }
+      for (int i = lane; i < G * kD; i += kWave)
+        out[((int64_t)item * hq + kvh * G) * kD + i] = f32_to_bf16(fill);
+      return;
     }
-    for (int i = lane; i < G * kD; i += kWave)
-      out[((int64_t)seq * hq + kvh * G) * kD + i] = f32_to_bf16(fill);
-    return;
+    jb = split ? part * a.partition_blocks : 0;
+    je = split ? min(nblk, jb + a.partition_blocks) : nblk;
+    tok_end = min(ctx, je * kBlock);
+    nshared = HINT ? a.shared_prefix_blocks[item] : 0;
+    table = a.block_tables + (int64_t)item * a.max_blocks_per_seq;
+  }
+  // this lane's column: sequence colseq, query head colh (colseq < 0: no head)
+  int colseq = -1, colh = 0;
+  if constexpr (GROUPED) {
+    const int m = r / G;
+    if (m < 32 && ((active >> m) & 1u)) {
+      colseq = item + m;
+      colh = kvh * G + (r - m * G);
+    }
+  } else {
+    if (r < G) {
+      colseq = item;
+      colh = kvh * G + r;
+    }
   }
 
-  const int jb = split ? part * a.partition_blocks : 0;
-  const int je = split ? min(nblk, jb + a.partition_blocks) : nblk;
-  const int tok_end = min(ctx, je * kBlock);
-
   u32x4 qb[4];
-  const bf16_t* qrow = static_cast<const bf16_t*>(a.query) + ((int64_t)seq * hq + kvh * G + r) * kD;
+  const bf16_t* qrow =
+      static_cast<const bf16_t*>(a.query) + ((int64_t)max(colseq, 0) * hq + colh) * kD;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
-    qb[ks] = r < G ? *reinterpret_cast<const u32x4*>(qrow + (4 * ks + g) * 8)
-                   : u32x4{0u, 0u, 0u, 0u};
+    qb[ks] = colseq >= 0 ? *reinterpret_cast<const u32x4*>(qrow + (4 * ks + g) * 8)
+                         : u32x4{0u, 0u, 0u, 0u};
 
   HeadState st;
   st.m = -INFINITY;
@@ -319,10 +362,10 @@ __global__ __launch_bounds__(64 * kHeadsPerWG) void decode_gqa_mfma_kernel(Decod
   const KV* kpool = static_cast<const KV*>(a.k_cache);
   const KV* vpool = static_cast<const KV*>(a.v_cache);
   constexpr int kSlabBytes = kBlock * kD * (int)sizeof(KV);
-  const int32_t* table = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
   const int64_t head_slab = (int64_t)kBlock * kD;
   uint8_t* ktile = sh_k[kvh % kHeadsPerWG];
   bool bad_block = false;
+  uint32_t mismatch = 0;   // grouped: bit m = member m names other blocks
 
   // Blocks jb .. je-1, their ids fetched 64 at a time (lane t holds the t-th)
   // and broadcast per step.  Two slabs are in flight: the next block's loads
@@ -332,12 +375,18 @@ __global__ __launch_bounds__(64 * kHeadsPerWG) void decode_gqa_mfma_kernel(Decod
   // outside the pool reads as zeros and poisons the result.
   // Batches never mix blocks the caller marks as shared with private ones, so
   // each batch runs with one cache policy.
-  const int nshared = HINT ? a.shared_prefix_blocks[seq] : 0;
   const int shared_end = max(jb, min(je, nshared));
   for (int base = jb; base < je;) {
     const bool shared_batch = base < shared_end;
     const int cnt = min(kWave, (shared_batch ? shared_end : je) - base);
     const int myb = lane < cnt ? table[base + lane] : 0;
+    if constexpr (GROUPED) {
+      for (int m = 0; m < a.group_members; ++m)
+        if ((active >> m) & 1u) {
+          const int32_t* tm = a.block_tables + (int64_t)(item + m) * a.max_blocks_per_seq;
+          if (lane < cnt && tm[base + lane] != myb) mismatch |= 1u << m;
+        }
+    }
     const auto run_batch = [&](auto policy) {
       constexpr int P = decltype(policy)::value;
       const auto load_step = [&](SlabOf<KV>& sl, int t) {
@@ -381,13 +430,23 @@ __global__ __launch_bounds__(64 * kHeadsPerWG) void decode_gqa_mfma_kernel(Decod
   float lsum = st.lsum;
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
-  const bool poisoned = __builtin_amdgcn_readfirstlane((int)bad_block) != 0;
-  if (r >= G) return;
+  bool poisoned = __builtin_amdgcn_readfirstlane((int)bad_block) != 0;
+  int np = nparts;
+  if constexpr (GROUPED) {
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) mismatch |= (uint32_t)__shfl_xor((int)mismatch, o, 64);
+    if (colseq >= 0) {
+      poisoned |= ((mismatch >> (r / G)) & 1u) != 0;
+      const int nb = (a.context_lens[colseq] + kBlock - 1) / kBlock;
+      np = (nb + a.partition_blocks - 1) / a.partition_blocks;
+    }
+  }
+  if (colseq < 0) return;
   float inv = 1.f / lsum;
   if constexpr (std::is_same<KV, fp8_t>::value) inv = a.v_scale / lsum;
-  const int h = kvh * G + r;
-  if (nparts <= 1) {
-    bf16_t* dst = out + ((int64_t)seq * hq + h) * kD;
+  const int h = colh;
+  if (np <= 1) {
+    bf16_t* dst = out + ((int64_t)colseq * hq + h) * kD;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       u32x4 w;
@@ -398,7 +457,7 @@ __global__ __launch_bounds__(64 * kHeadsPerWG) void decode_gqa_mfma_kernel(Decod
       *reinterpret_cast<u32x4*>(dst + 8 * (4 * g + i)) = w;
     }
   } else {
-    const int64_t row = ((int64_t)seq * hq + h) * a.max_partitions + part;
+    const int64_t row = ((int64_t)colseq * hq + h) * a.max_partitions + part;
     float* dst = a.part_o + row * kD;
     const float nan = __builtin_nanf("");
 #pragma unroll
@@ -416,18 +475,30 @@ __global__ __launch_bounds__(64 * kHeadsPerWG) void decode_gqa_mfma_kernel(Decod
   }
 }
 
+// Query columns of the products: a grouped-pass wave stacks the query heads
+// of up to 16 / G sharers.
+constexpr int kMfmaColumns = 16;
+
 template <typename KV>
 hipError_t launch_gqa_mfma(const DecodeArgs& a, hipStream_t stream) {
   if (a.num_items == 0) return hipSuccess;
   const int hgroups = (a.num_kv_heads + kHeadsPerWG - 1) / kHeadsPerWG;
   dim3 grid((unsigned)((int64_t)a.num_items * hgroups),
             a.partition_blocks > 0 ? a.max_partitions : 1);
-  if (a.shared_prefix_blocks != nullptr)
-    hipLaunchKernelGGL((decode_gqa_mfma_kernel<KV, true>), grid, dim3(64 * kHeadsPerWG), 0,
-                       stream, a);
+  const dim3 block(64 * kHeadsPerWG);
+  DecodeArgs b = a;   // both passes see the same window size
+  b.group_members = group_window(a, kMfmaColumns);
+  if (b.group_members == 0) b.prefix_group = nullptr;
+  if (b.prefix_group != nullptr) {
+    if (b.partition_blocks <= 0 || b.shared_prefix_blocks == nullptr) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((decode_gqa_mfma_kernel<KV, false, true>), grid, block, 0, stream, b);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (b.shared_prefix_blocks != nullptr)
+    hipLaunchKernelGGL((decode_gqa_mfma_kernel<KV, true, false>), grid, block, 0, stream, b);
   else
-    hipLaunchKernelGGL((decode_gqa_mfma_kernel<KV, false>), grid, dim3(64 * kHeadsPerWG), 0,
-                       stream, a);
+    hipLaunchKernelGGL((decode_gqa_mfma_kernel<KV, false, false>), grid, block, 0, stream, b);
   return hipGetLastError();
 }
 

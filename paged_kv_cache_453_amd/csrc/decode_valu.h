@@ -46,6 +46,7 @@
 
 #include <type_traits>
 
+#include "decode_groups.h"
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -330,38 +331,6 @@ __device__ __forceinline__ bool locate_item(const DecodeArgs& a, int item, ItemI
   it.bad = item >= qsl[lo + 1] || chunk > len || chunk > a.max_query_len ||
            len > a.max_blocks_per_seq * kBlock || it.ctx < 1 || it.ctx > len;
   return true;
-}
-
-// Grouped pass over shared prefixes.  Samples of one prompt keep its blocks in
-// common ("vLLM 基本原理", section 内存共享), as do requests that hit one cached
-// prefix (xdnf.cn article, section 六.3); their block tables then name the same
-// physical blocks, and a partition made of such blocks holds the same K/V for
-// every sharer.  The grouped pass streams each such partition once and scores
-// it against the queries of up to group_members sharers at a time, writing
-// each sharer's partial (o_p, lse_p) exactly where its own split-K workgroup
-// would have; the regular pass then skips those partitions.
-//
-// grouped_parts(s): how many leading partitions of sequence s the grouped pass
-// computes -- those inside the full blocks that s and its group's leader both
-// declare shared.  Both passes evaluate it from the same data, so every
-// partition is computed exactly once.  It is 0 (the regular pass does all)
-// unless s's group is well formed: leader <= s, the leader leads itself, and
-// the first member of s's window of group_members is in the group too, and
-// both lengths are within the call's limits.
-__device__ __forceinline__ int grouped_parts(const DecodeArgs& a, int s) {
-  if (a.prefix_group == nullptr) return 0;
-  const int lead = a.prefix_group[s];
-  if (lead < 0 || lead > s) return 0;
-  const int M = a.group_members;
-  const int first = lead + (s - lead) / M * M;
-  if (a.prefix_group[lead] != lead || a.prefix_group[first] != lead) return 0;
-  const int cap = min(a.max_context_len, a.max_blocks_per_seq * kBlock);
-  const int ls = a.context_lens[s];
-  const int ll = a.context_lens[lead];
-  if (ls < 0 || ll < 0 || ls > cap || ll > cap) return 0;
-  const int nb = min(min(a.shared_prefix_blocks[s], a.shared_prefix_blocks[lead]),
-                     min(ls, ll) / kBlock);
-  return nb > 0 ? nb / a.partition_blocks : 0;
 }
 
 // HINT: the caller passed shared_prefix_blocks, so batches of shared blocks
@@ -688,18 +657,21 @@ inline hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   if (std::is_same<KV, fp8_t>::value && a.group > kFp8ValuMaxGroup) return hipErrorInvalidValue;
   dim3 grid((unsigned)((int64_t)a.num_items * a.num_kv_heads),
             a.partition_blocks > 0 ? a.max_partitions : 1);
-  if (a.prefix_group != nullptr) {
-    if (a.partition_blocks <= 0 || a.group_members < 2 || a.shared_prefix_blocks == nullptr ||
-        a.query_start_loc != nullptr || a.group_members * a.group > kGroupedMaxSlots)
+  DecodeArgs b = a;   // both passes see the same window size
+  b.group_members = group_window(a, kGroupedMaxSlots);
+  if (b.group_members == 0) b.prefix_group = nullptr;
+  if (b.prefix_group != nullptr) {
+    if (b.partition_blocks <= 0 || b.shared_prefix_blocks == nullptr ||
+        b.query_start_loc != nullptr)
       return hipErrorInvalidValue;
-    launch_decode_grouped<T, KV, D>(a, grid, stream);
+    launch_decode_grouped<T, KV, D>(b, grid, stream);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (a.shared_prefix_blocks != nullptr)
-    launch_decode_group<T, KV, D, true>(a, grid, stream);
+  if (b.shared_prefix_blocks != nullptr)
+    launch_decode_group<T, KV, D, true>(b, grid, stream);
   else
-    launch_decode_group<T, KV, D, false>(a, grid, stream);
+    launch_decode_group<T, KV, D, false>(b, grid, stream);
   return hipGetLastError();
 }
 

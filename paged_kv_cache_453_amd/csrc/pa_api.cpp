@@ -82,15 +82,11 @@ int decode_impl(void* out, const void* query, const void* key_cache, const void*
   a.context_lens = context_lens;
   a.query_start_loc = nullptr;
   a.shared_prefix_blocks = shared_prefix_blocks;
-  // Windows of up to group_members sharers per grouped workgroup; with fewer
-  // than two (groups of one, or query-head groups that fill the slots alone)
-  // there is nothing to share and the call is a plain decode.
-  const int members =
-      prefix_group ? (max_group_size < pa::kGroupedMaxSlots / group ? max_group_size
-                                                                     : pa::kGroupedMaxSlots / group)
-                   : 0;
-  a.prefix_group = members >= 2 ? prefix_group : nullptr;
-  a.group_members = members >= 2 ? members : 0;
+  // The launchers size the windows of sharers per grouped workgroup from
+  // max_group_size and the query slots their kernel holds; with fewer than two
+  // members per window the call is a plain decode.
+  a.prefix_group = prefix_group;
+  a.group_members = prefix_group ? max_group_size : 0;
   const size_t rows = (size_t)num_seqs * num_heads * nparts;
   a.part_o = partition_size > 0 ? static_cast<float*>(workspace) : nullptr;
   a.part_lse = partition_size > 0 ? static_cast<float*>(workspace) + rows * head_dim : nullptr;

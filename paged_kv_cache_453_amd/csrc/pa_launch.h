@@ -36,7 +36,9 @@ struct DecodeArgs {
   const int32_t* shared_prefix_blocks;  // optional per-sequence cache hint (decode only)
   // Decode only, optional: prefix_group[s] = first sequence of s's sharing
   // group.  Windows of group_members (>= 2) consecutive members read their
-  // common full partitions once, in the grouped pass (decode_valu.h).
+  // common full partitions once, in the grouped pass (decode_groups.h); the
+  // entry point passes the caller's largest group size, each launcher the
+  // window size its kernel holds.
   const int32_t* prefix_group;
   int group_members;
   float* part_o;

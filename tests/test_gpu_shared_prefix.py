@@ -198,20 +198,59 @@ def test_prefix_ends_inside_partition_and_short_members(gpu):
     assert (grouped[8].float() == 0).all()
 
 
-@pytest.mark.parametrize("hq,hkv", [(16, 8), (32, 4)])
-def test_grouped_query_heads(gpu, hq, hkv):
-    """Two query heads per kv head leave room for windows of two; eight fill
-    the slots alone (a plain decode on the matrix cores)."""
-    say(f"shared-prefix decode: {hq} query heads over {hkv} kv heads")
-    w = mixed_decoders(heads=hkv, partition_size=512)
+def gqa_decoders(hq, hkv, dtype="bf16", **kw):
+    """The mixed workload's decoders with hq query heads over hkv kv heads."""
+    w = mixed_decoders(heads=hkv, dtype=dtype, **kw)
     rng = np.random.default_rng(99)
     q = rng.standard_normal((w.decode.num_seqs, hq, w.head_dim)).astype(np.float32)
-    w.decode.query = f32_to_bf16_bits(q)
+    w.decode.query = q if dtype == "f32" else f32_to_bf16_bits(q)
     w.num_heads = hq
+    return w
+
+
+@pytest.mark.parametrize("hq,hkv,groups", [(16, 8, 3), (32, 8, 3), (32, 4, 3), (32, 4, 7)])
+def test_grouped_query_heads(gpu, hq, hkv, groups):
+    """Grouped-query heads: two per kv head on the vector ALUs (windows of two
+    sharers in four slots); four or eight on the matrix cores, whose 16 query
+    columns take windows of four or two sharers."""
+    say(f"shared-prefix decode: {hq} query heads over {hkv} kv heads, groups of {groups}")
+    w = gqa_decoders(hq, hkv, samples=groups, num_prompts=24 // groups, partition_size=512)
     dw = to_device(w)
-    plain, grouped = decode_pair(dw, 512, dw.decode.prefix_group, 3)
+    plain, grouped = decode_pair(dw, 512, dw.decode.prefix_group, groups)
     assert same_bits(plain, grouped)
-    assert_close(as_f64(grouped), oracle_decode(w, scattered=False), "bf16", f"{hq}/{hkv}")
+    assert_close(as_f64(grouped), oracle_decode(w, scattered=False), "bf16",
+                 f"{hq}/{hkv} groups of {groups}")
+
+
+def test_grouped_query_heads_member_with_other_blocks(gpu):
+    """On the matrix cores too, a member that breaks the grouping gets NaN and
+    nobody else changes."""
+    import torch
+    w = gqa_decoders(32, 8, partition_size=512)
+    dw = to_device(w)
+    g = dw.decode
+    bt = g.block_tables.clone()
+    bt[5, 3] = g.block_tables[0, 3]
+    g.block_tables = bt
+    plain, grouped = decode_pair(dw, 512, g.prefix_group, 3)
+    others = [s for s in range(w.decode.num_seqs) if s != 5]
+    assert same_bits(plain[others], grouped[others])
+    assert torch.isnan(grouped[5].float()).all()
+
+
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (32, 4)])
+def test_fp8_grouped_query_heads(gpu, hq, hkv):
+    say(f"shared-prefix decode over an FP8 cache, {hq}/{hkv} heads")
+    w = gqa_decoders(hq, hkv, partition_size=512)
+    kq, vq = fp8_pools(w, 93)
+    dw = to_device(w, pools=False)
+    pools = upload_fp8_pools(w, kq, vq)
+    plain, grouped = decode_pair(dw, 512, dw.decode.prefix_group, 3, pools=pools)
+    assert same_bits(plain, grouped)
+    d = w.decode
+    want = kv_fp8.decode(d.query, kq, vq, w.host_tables(d.block_tables), d.context_lens, w.scale,
+                         K_SCALE, V_SCALE, "bf16")
+    assert_close(as_f64(grouped), want, "bf16", f"fp8 grouped decode {hq}/{hkv}")
 
 
 @pytest.mark.parametrize("qdtype", ["bf16", "f32"])
