@@ -13,6 +13,8 @@ shuffled pool) with split-K partitions and their merge.
   mixed     chunked prefill of 4 x 512-token chunks over paged prefixes, then
             decode of 192 sequences sharing 2048-token prefixes in groups of 3
             (also timed with prefill and decode on two streams)
+  mixed_gqa, mixed_gqa_fp8
+            the mixed step with 32 query heads over 8 kv heads (Llama-3-8B shape)
   llama13b_fp8, gqa_fp8, mixed_fp8
             the llama13b, gqa and mixed steps over an FP8 (OCP E4M3) cache with
             one scale per pool: quantising scatter (llama13b), chunked prefill
@@ -318,7 +320,7 @@ class StepTimer:
 STREAM_BYTES = 4 << 30
 STREAM_METRIC = "achievable HBM read GB/s (plain 16-byte loads over a 4 GiB buffer)"
 WORKLOADS = ("llama13b", "llama7b", "gqa", "mixed", "llama13b_fp8", "gqa_fp8", "mixed_fp8",
-             "prefix_cache",
+             "mixed_gqa", "mixed_gqa_fp8", "prefix_cache",
              "sampler", "block_moves", "stream_read")
 SAMPLER_BUFFERS = 9
 SAMPLER_METRIC = "next-token sampling rows/s (temperature + top-k + top-p + draw), 32000-token vocabulary"
@@ -341,6 +343,13 @@ def build_workload(name: str, ps: int):
         return config3(partition_size=ps), {
             "workload": "llama3-8b-shaped GQA long-context paged decode (decode + split-K merge)",
             "context_lens": "uniform [8192,32768]", "seed": 456}
+    if name == "mixed_gqa":
+        return config4(partition_size=ps, heads=32, kv_heads=8), {
+            "workload": "mixed chunked prefill + shared-prefix paged decode, grouped-query "
+                        "heads (Llama-3-8B shape: 32 query heads over 8 kv heads)",
+            "prefill": "4 x 512-token causal chunks over paged prefixes U{0..3584}",
+            "decode": "64 prompts x 3 samples sharing 2048-token prefixes + U{0..512} private",
+            "seed": 457}
     return config4(partition_size=ps), {
         "workload": "mixed chunked prefill + shared-prefix paged decode",
         "prefill": "4 x 512-token causal chunks over paged prefixes U{0..3584}",
@@ -749,7 +758,7 @@ def main(argv=None):
         codes = fp8_pools(w, 453)
         cfg["workload"] = cfg["workload"].replace("paged decode", "paged decode over an FP8 "
                                                   "(E4M3) cache")
-        if base == "mixed":
+        if base.startswith("mixed"):
             cfg["workload"] = cfg["workload"].replace("chunked prefill", "FP8 chunked prefill")
         cfg["kv_cache"] = (f"fp8 e4m3 codes, random sign / exponent field 0..9 / mantissa; "
                            f"k_scale {FP8_K_SCALE}, v_scale {FP8_V_SCALE}")
@@ -871,7 +880,10 @@ def main(argv=None):
     kv_name = "fp8" if fp8 else "bf16"
     dec_kernel = (f"decode_gqa_mfma_kernel<{kv_name}>" if group >= 4 else
                   f"decode_valu_kernel<bf16,{kv_name},{w.head_dim},{group}>")
-    if grouped:
+    if grouped and group >= 4:
+        dec_kernel = (f"decode_gqa_mfma_kernel<{kv_name},grouped> + "
+                      f"decode_gqa_mfma_kernel<{kv_name}> (one pa_decode_shared_prefix call)")
+    elif grouped:
         dec_kernel = (f"decode_valu_kernel<bf16,{kv_name},{w.head_dim},3,grouped> + "
                       f"decode_valu_kernel<bf16,{kv_name},{w.head_dim},{group}> "
                       "(one pa_decode_shared_prefix call)")

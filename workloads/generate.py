@@ -437,8 +437,9 @@ def config4(seed: Optional[int] = None, dtype: str = "bf16", num_prompts: int = 
             samples: int = 3, shared_prefix: int = 2048, max_private: int = 512,
             num_prefill: int = 4, chunk: int = 512, max_prefix: int = 3584,
             num_blocks: int = 16384, heads: int = 40, head_dim: int = 128,
-            partition_size: int = 512) -> Workload:
-    """Chunked-prefill sequences plus decoders that share whole prefix blocks.
+            partition_size: int = 512, kv_heads: Optional[int] = None) -> Workload:
+    """Chunked-prefill sequences plus decoders that share whole prefix blocks
+    (heads query heads over kv_heads kv heads, by default as many).
 
     Sharing follows "vLLM 基本原理" (section "内存共享": samples of one prompt
     point at the same physical prompt blocks, private blocks only past the fork)
@@ -476,13 +477,16 @@ def config4(seed: Optional[int] = None, dtype: str = "bf16", num_prompts: int = 
         raise ValueError("pool too small")
     live = _live_rows(dec_tables, dec_lens)
     live.update(_live_rows(pre_tables, pre_lens))
-    ids, k, v = _materialise(live, dtype, heads, head_dim, kids[1], kids[2])
+    hkv = heads if kv_heads is None else kv_heads
+    if heads % hkv:
+        raise ValueError("query heads must be a multiple of kv heads")
+    ids, k, v = _materialise(live, dtype, hkv, head_dim, kids[1], kids[2])
     dec_q = _normal((n_dec, heads, head_dim), dtype, kids[3])
     qsl = np.zeros(num_prefill + 1, dtype=np.int32)
     qsl[1:] = np.cumsum(np.full(num_prefill, chunk, dtype=np.int32))
     pre_q = _normal((int(qsl[-1]), heads, head_dim), dtype, kids[4])
     w = Workload(name=f"mixed-prefill-decode-{dtype}", dtype=dtype, num_heads=heads,
-                 num_kv_heads=heads, head_dim=head_dim, num_blocks=num_blocks,
+                 num_kv_heads=hkv, head_dim=head_dim, num_blocks=num_blocks,
                  scale=_scale(head_dim), host_ids=ids, k_host=k, v_host=v,
                  decode=SeqGroup(context_lens=dec_lens, block_tables=dec_tables, query=dec_q,
                                  shared_prefix_blocks=np.full(n_dec, nsh, dtype=np.int32),
