@@ -63,12 +63,13 @@ _CSRC = os.path.join(ROOT, "paged_kv_cache_453_amd", "csrc")
 # kernels whose HBM traffic comes from committed counter runs: the summary file,
 # the kernel name prefix in the rocprofv3 CSVs, the sources the kernel is built
 # from, and the bench command the counter runs profiled
+_DECODE_SOURCES = [os.path.join(_CSRC, f) for f in
+                   ("decode_valu.h", "decode_groups.h", "decode_valu_bf16.hip", "pa_device.h")]
 COUNTED = {
     "decode": {
         "json": os.path.join(ROOT, "profiles", "decode_llama13b_counters.json"),
         "kernel": "void pa::decode_valu_kernel<unsigned short, unsigned short, 128, 1, false, false>",
-        "sources": [os.path.join(_CSRC, f)
-                    for f in ("decode_valu.h", "decode_valu_bf16.hip", "pa_device.h")],
+        "sources": _DECODE_SOURCES,
         "bench": "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
         "dir": "pmc", "out": "bench"},
     # one pa_decode_shared_prefix call on the mixed workload's decoders: the grouped
@@ -77,16 +78,14 @@ COUNTED = {
         "json": os.path.join(ROOT, "profiles", "decode_mixed_counters.json"),
         "kernel": ["void pa::decode_valu_kernel<unsigned short, unsigned short, 128, 3, false, true>",
                    "void pa::decode_valu_kernel<unsigned short, unsigned short, 128, 1, true, false>"],
-        "sources": [os.path.join(_CSRC, f)
-                    for f in ("decode_valu.h", "decode_valu_bf16.hip", "pa_device.h")],
+        "sources": _DECODE_SOURCES,
         "bench": "python3 bench.py --workload mixed --decode-only --steps 3 --warmup 1",
         "dir": "pmc_mixed", "out": "mixed"},
     # the same decoders through pa_decode (each sample reads the shared prefix itself)
     "mixed_decode_plain": {
         "json": os.path.join(ROOT, "profiles", "decode_mixed_plain_counters.json"),
         "kernel": ["void pa::decode_valu_kernel<unsigned short, unsigned short, 128, 1, true, false>"],
-        "sources": [os.path.join(_CSRC, f)
-                    for f in ("decode_valu.h", "decode_valu_bf16.hip", "pa_device.h")],
+        "sources": _DECODE_SOURCES,
         "bench": "python3 bench.py --workload mixed --decode-only --no-prefix-groups --steps 3 "
                  "--warmup 1",
         "dir": "pmc_mixed_plain", "out": "mixed"},
