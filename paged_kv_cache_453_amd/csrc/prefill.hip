@@ -10,9 +10,11 @@
 // Tiling.  A workgroup (4 waves) owns 4*RW query rows of one head of one
 // sequence; each wave owns RW rows as RW/16 blocks of 16.  Keys go in tiles of
 // 64 (4 cache blocks), staged in LDS row-major (padded rows) by coalesced
-// 16-byte copies and double-buffered: the next tile's global loads are issued
-// before the current tile is computed and land in the other buffer after it.
-// A wave skips the tiles that lie entirely above its causal diagonal.
+// 16-byte copies: the next tile's global loads are issued before the current
+// tile is computed and land in registers, and are stored to the one LDS tile
+// buffer after a barrier that follows the computation (a second buffer was
+// about 2% slower, and twice the LDS).  A wave skips the tiles that lie
+// entirely above its causal diagonal.
 //
 // Orientation.  Scores are produced transposed, S^T = K Q^T, and the output as
 // O^T = V^T P^T.  In a 16x16 MFMA result lane l = 16g + r holds rows 4g..4g+3
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
   constexpr int KPP = 256 / CH;         // key rows staged per pass of the workgroup
   constexpr int NPASS = kKeys / KPP;    // staging passes per tile
   constexpr int TILE = kKeys * (ROW + ROWV);   // K rows, then V rows
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2][TILE];   // [buffer]
+  __shared__ __attribute__((aligned(16))) uint8_t smem[TILE];
   __shared__ int sh_bad;
 
   const int qtile = gridDim.x - 1 - blockIdx.x;   // later (longer) tiles first
@@ -210,12 +212,12 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
       return x;
     }
   };
-  const auto stage_store = [&](int buf) {
+  const auto stage_store = [&]() {
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
       const int kr = kr0 + KPP * p;
-      *reinterpret_cast<u32x4*>(&smem[buf][kr * ROW + cc * 16]) = widen(kst[p]);
-      *reinterpret_cast<u32x4*>(&smem[buf][kKeys * ROW + kr * ROWV + cc * 16]) = widen(vst[p]);
+      *reinterpret_cast<u32x4*>(&smem[kr * ROW + cc * 16]) = widen(kst[p]);
+      *reinterpret_cast<u32x4*>(&smem[kKeys * ROW + kr * ROWV + cc * 16]) = widen(vst[p]);
     }
   };
 
@@ -233,18 +235,18 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
   int ids_next = fetch_ids(0);
   stage_load(0, ids_next);
   ids_next = fetch_ids(1);
-  stage_store(0);
+  stage_store();
 
   for (int kt = 0; kt < ntiles; ++kt) {
     const int ids_cur = ids_next;
     stage_load(kt + 1, ids_cur);     // past the last tile: empty resources, no traffic
     ids_next = fetch_ids(kt + 2);
-    lds_barrier();   // tile kt is in buffer kt & 1; buffer (kt+1) & 1 is free
+    lds_barrier();   // tile kt is in the buffer
 
     const int tile_first = kt * kKeys;
     if (wave_rows > 0 && tile_first <= wave_last_pos) {
-      const uint8_t* kb = smem[kt & 1];
-      const uint8_t* vb = smem[kt & 1] + kKeys * ROW;
+      const uint8_t* kb = smem;
+      const uint8_t* vb = smem + kKeys * ROW;
       const bool need_mask = tile_first + kKeys - 1 > wave_first_pos;
 
       // ---- S^T = K Q^T: four 16-key groups ----
@@ -332,7 +334,8 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
           for (int qb = 0; qb < QB; ++qb) o[qb][t] = mfma_16x16x32(va[t], pk[kk][qb], o[qb][t]);
       }
     }
-    stage_store((kt + 1) & 1);
+    lds_barrier();   // every wave is done with tile kt
+    stage_store();
   }
 
   // ---- normalise and store: lane holds O[row 16qb + r][16t + 4g + i] ----
