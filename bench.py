@@ -19,6 +19,9 @@ shuffled pool) with split-K partitions and their merge.
             the llama13b, gqa and mixed steps over an FP8 (OCP E4M3) cache with
             one scale per pool: quantising scatter (llama13b), chunked prefill
             (mixed), decode, merge; KV bytes count one byte per element
+  prefill_long  4 chunks of 128 tokens over 16384-token paged prefixes (40
+            heads): the split prefill (runs of 2048 keys) against one workgroup
+            per query tile
   prefix_cache  32 prompts at Llama-2-13B shape sharing a 2048-token system
             prompt, each with 256 tokens of its own: the chunked prefill of
             all 32 with prefix-cache hits (256 query tokens each over the
@@ -319,12 +322,14 @@ class StepTimer:
 STREAM_BYTES = 4 << 30
 STREAM_METRIC = "achievable HBM read GB/s (plain 16-byte loads over a 4 GiB buffer)"
 WORKLOADS = ("llama13b", "llama7b", "gqa", "mixed", "llama13b_fp8", "gqa_fp8", "mixed_fp8",
-             "mixed_gqa", "mixed_gqa_fp8", "prefix_cache",
+             "mixed_gqa", "mixed_gqa_fp8", "prefix_cache", "prefill_long",
              "sampler", "block_moves", "stream_read")
 SAMPLER_BUFFERS = 9
 SAMPLER_METRIC = "next-token sampling rows/s (temperature + top-k + top-p + draw), 32000-token vocabulary"
 PREFIX_METRIC = ("prefill us for 32 prompts sharing a 2048-token system prompt, with prefix-cache "
                  "hits, at Llama-2-13B shape")
+LONG_PREFILL_METRIC = ("chunked prefill TFLOP/s, 4 chunks of 128 tokens over 16384-token paged "
+                       "prefixes at Llama-2-13B head shape, split over the keys")
 COPY_METRIC = "paged KV block copy GB/s (copy-on-write, read + write bytes) at Llama-2-13B pool shape"
 
 
@@ -598,6 +603,74 @@ def bench_prefix_cache(args, torch, dev, lib, timer) -> int:
     return 0
 
 
+def bench_prefill_long(args, torch, dev, lib, timer) -> int:
+    """Chunks over long paged prefixes: few query tiles with long causal key
+    ranges, where one workgroup per query tile leaves most of the part idle;
+    pa_prefill_chunk_split against pa_prefill_chunk."""
+    import numpy as np
+
+    from workloads import accounting, make_prefill
+    from workloads.device import to_device
+
+    nseq, prefix, chunk, h, d = 4, 16384, 128, 40, 128
+    split = args.prefill_split or 2048
+    w = make_prefill("prefill-long", 453, "bf16", [prefix] * nseq, [chunk] * nseq, h, h, d,
+                     nseq * ((prefix + chunk) // 16 + 1))
+    dw = to_device(w, device=dev)
+    g = dw.prefill
+    maxc = prefix + chunk
+    ws = torch.empty(lib.pa_prefill_workspace_bytes(nseq * chunk, h, d, maxc, split),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def split_run():
+        lib.pa_prefill_chunk_split(g.out, g.query, dw.k_cache, dw.v_cache, g.block_tables,
+                                   g.query_start_loc, g.context_lens, w.scale, g.max_query_len,
+                                   maxc, split, ws, stream=stream)
+
+    def plain_run():
+        lib.pa_prefill_chunk(g.out, g.query, dw.k_cache, dw.v_cache, g.block_tables,
+                             g.query_start_loc, g.context_lens, w.scale, g.max_query_len,
+                             stream=stream)
+
+    for _ in range(args.warmup):
+        split_run()
+        plain_run()
+    torch.cuda.synchronize()
+    log(f"bench: timing {args.steps} long-prefix prefills, split and whole")
+    ms = timer.per_launch([("split", split_run), ("unsplit", plain_run)], args.steps, stream)
+    flops = accounting.prefill_flops(w.prefill.query_start_loc, w.prefill.context_lens, h, d)
+    tf = flops / (ms["split"] * 1e-3) / 1e12
+    tf_plain = flops / (ms["unsplit"] * 1e-3) / 1e12
+    result = {
+        "metric": LONG_PREFILL_METRIC, "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms["split"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{nseq} chunks of {chunk} query tokens over {prefix}-token paged "
+                               f"prefixes, 40 = 40 heads, head_dim 128, bf16, block size 16",
+                   "split_tokens": split, "seed": 453},
+        "prefill_us": {"split": round(ms["split"] * 1e3, 2),
+                       "unsplit": round(ms["unsplit"] * 1e3, 2)},
+        "speedup_over_unsplit": round(ms["unsplit"] / ms["split"], 3),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": f"prefill_mfma_kernel<bf16,128,32> in runs of {split} keys + "
+                               "prefill_merge_kernel (one pa_prefill_chunk_split call)",
+                     "algorithmic_flops_per_launch": int(flops),
+                     "unsplit_achieved": round(tf_plain, 2),
+                     "unsplit_frac": round(tf_plain / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        cpu = prefix_cpu_baseline(d, h, chunk, prefix + chunk, n=nseq)
+        cpu.update(value=round(flops / (cpu["value"] * 1e-6) / 1e12, 6), unit="TFLOP/s")
+        result["cpu_baseline"] = cpu
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def prefix_cpu_baseline(d: int, hq: int, own: int, total: int, n: int = 32):
     """The fp64 prefill oracle on one prompt's chunk (own query tokens over a
     total-token context), one host thread, scaled to the 32-prompt batch."""
@@ -697,6 +770,10 @@ def main(argv=None):
                     help="split-K partition length in tokens (default: 2048 for the Llama "
                          "shapes, 512 for gqa as its configuration states, 2048 for mixed)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-split", type=int, default=None,
+                    help="keys per run of the split prefill (pa_prefill_chunk_split): mixed "
+                         "workloads default to 0 = pa_prefill_chunk, one workgroup per query "
+                         "tile; prefill_long defaults to 2048")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode call and its merge (for counter runs); prints "
                          "a short JSON line")
@@ -737,6 +814,8 @@ def main(argv=None):
         return bench_block_moves(args, torch, dev, lib, StepTimer(torch))
     if args.workload == "prefix_cache":
         return bench_prefix_cache(args, torch, dev, lib, StepTimer(torch))
+    if args.workload == "prefill_long":
+        return bench_prefill_long(args, torch, dev, lib, StepTimer(torch))
     if args.workload == "sampler":
         return bench_sampler(args, torch, dev, lib, StepTimer(torch))
     if args.workload == "stream_read":
@@ -815,7 +894,31 @@ def main(argv=None):
             lib.pa_decode_splitk_reduce(dg.out, ws, dg.context_lens, g.max_context_len, ps,
                                         stream=s)
 
-    def prefill(s=stream):
+    # long causal key ranges of the prefill chunks split over workgroups
+    pf_split = 0
+    if w.prefill is not None:
+        pf_split = 0 if args.prefill_split is None else args.prefill_split
+    pf_maxc = int(w.prefill.context_lens.max()) if w.prefill is not None else 0
+    pws = None
+    if pf_split:
+        pq = dw.prefill.query
+        pws = torch.empty(max(lib.pa_prefill_workspace_bytes(pq.shape[0], pq.shape[1], pq.shape[2],
+                                                             pf_maxc, pf_split), 16),
+                          dtype=torch.uint8, device=dev)
+
+    def split_prefill(s=stream):
+        p = dw.prefill
+        if fp8:
+            lib.pa_prefill_chunk_fp8_split(p.out, p.query, dw.k_cache, dw.v_cache, p.block_tables,
+                                           p.query_start_loc, p.context_lens, w.scale,
+                                           FP8_K_SCALE, FP8_V_SCALE, p.max_query_len, pf_maxc,
+                                           pf_split, pws, stream=s)
+        else:
+            lib.pa_prefill_chunk_split(p.out, p.query, dw.k_cache, dw.v_cache, p.block_tables,
+                                       p.query_start_loc, p.context_lens, w.scale,
+                                       p.max_query_len, pf_maxc, pf_split, pws, stream=s)
+
+    def plain_prefill(s=stream):
         p = dw.prefill
         if fp8:
             lib.pa_prefill_chunk_fp8(p.out, p.query, dw.k_cache, dw.v_cache, p.block_tables,
@@ -826,6 +929,7 @@ def main(argv=None):
                                  p.query_start_loc, p.context_lens, w.scale, p.max_query_len,
                                  stream=s)
 
+    prefill = split_prefill if pf_split else plain_prefill
     launches = []
     if w.slot_mapping is not None:
         launches.append(("reshape_and_cache", scatter))
@@ -863,6 +967,11 @@ def main(argv=None):
             "decode_us": round(kernel_ms["decode"] * 1e3, 2),
             "kv_bytes_logical": int(kv), "kv_bytes_unique": int(unique)}), flush=True)
         return 0
+
+    if pf_split:
+        # the same prefill without splitting, for comparison
+        pf_ms = timer.per_launch([("prefill_unsplit", plain_prefill)], args.steps, stream)
+        log("bench: prefill without splitting %.1f us" % (pf_ms["prefill_unsplit"] * 1e3))
 
     if grouped:
         # the same decode without the grouped pass, for comparison
@@ -914,8 +1023,13 @@ def main(argv=None):
         extra["roofline_prefill"] = {
             "bound": "mfma", "achieved": round(pf_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(pf_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None, "kernel": f"prefill_mfma_kernel<{kv_name},128,32>",
+            "traffic": None, "kernel": f"prefill_mfma_kernel<{kv_name},128,32>" + (
+                f" in runs of {pf_split} keys + prefill_merge_kernel (one "
+                "pa_prefill_chunk_split call)" if pf_split else ""),
             "algorithmic_flops_per_launch": int(flops)}
+        if pf_split:
+            extra["roofline_prefill"]["prefill_us_without_splitting"] = round(
+                pf_ms["prefill_unsplit"] * 1e3, 2)
         extra["prefill_tokens_per_step"] = int(p.query_start_loc[-1])
         # a rate against the HBM peak must count each physical row once
         extra["kv_gbs_logical"] = round(gbs, 2)

@@ -229,6 +229,44 @@ int pa_prefill_chunk(void* out, const void* query, const void* key_cache, const 
                      pa_dtype dtype, hipStream_t stream);
 
 /*
+ * pa_prefill_chunk_split -- pa_prefill_chunk with the causal key range of long
+ * query tiles split over several workgroups (split-K).
+ *
+ * A workgroup takes 128 query rows of one head; their keys (the paged prefix
+ * and the chunk up to the tile's last row) are cut into runs of split_tokens
+ * keys, each run one workgroup that leaves, per row, its normalised output
+ * and the natural-log sum of exp(scale * q.k) over its keys in the workspace;
+ * a merge launched by this call combines them by the log-sum-exp rule of
+ * pa_decode_splitk_reduce.  Tiles whose range needs one run are written
+ * directly.  The result equals pa_prefill_chunk's up to rounding; the point
+ * is balance: a chunk over a long prefix no longer keeps one workgroup busy
+ * long after the others (xdnf.cn article, section 六.4: chunks of one prompt
+ * see everything before them).
+ *
+ *  max_context_len  upper bound on context_lens (sizes the workspace); a
+ *                   longer sequence gets NaN rows.
+ *  split_tokens     keys per run, a positive multiple of 64 (else PA_ERR_SHAPE).
+ *  workspace        device buffer of at least pa_prefill_workspace_bytes(),
+ *                   16-byte aligned (else PA_ERR_WORKSPACE): fp32 outputs
+ *                   [num_query_tokens, num_heads, P, head_dim], then fp32 sums
+ *                   [num_query_tokens, num_heads, P], P = ceil(max_context_len /
+ *                   split_tokens).  The call overwrites what it needs of it.
+ *  dtype            PA_BF16 only (the matrix-core kernel; PA_ERR_UNSUPPORTED
+ *                   otherwise).
+ * Every other argument as pa_prefill_chunk.
+ */
+size_t pa_prefill_workspace_bytes(int num_query_tokens, int num_heads, int head_dim,
+                                  int max_context_len, int split_tokens);
+int pa_prefill_chunk_split(void* out, const void* query, const void* key_cache,
+                           const void* value_cache, const int32_t* block_tables,
+                           const int32_t* query_start_loc, const int32_t* context_lens,
+                           int num_seqs, int num_query_tokens, int num_heads, int num_kv_heads,
+                           int head_dim, int block_size, int max_blocks_per_seq,
+                           int64_t num_blocks, int max_query_len, int max_context_len,
+                           int split_tokens, float scale, void* workspace,
+                           size_t workspace_bytes, pa_dtype dtype, hipStream_t stream);
+
+/*
  * FP8 KV cache.  The cache may store K and V as 8-bit floats (OCP E4M3: 1 sign,
  * 4 exponent bits with bias 7, 3 mantissa bits, no infinities, largest
  * magnitude 448), one byte per element, which halves the bytes decode streams
@@ -306,6 +344,21 @@ int pa_prefill_chunk_fp8(void* out, const void* query, const uint8_t* key_cache,
                          int block_size, int max_blocks_per_seq, int64_t num_blocks,
                          int max_query_len, float scale, float k_scale, float v_scale,
                          pa_dtype dtype, hipStream_t stream);
+
+/*
+ * pa_prefill_chunk_fp8_split -- pa_prefill_chunk_split over FP8 caches (the
+ * arguments of pa_prefill_chunk_fp8 plus max_context_len, split_tokens and
+ * the workspace, with the same rules).
+ */
+int pa_prefill_chunk_fp8_split(void* out, const void* query, const uint8_t* key_cache,
+                               const uint8_t* value_cache, const int32_t* block_tables,
+                               const int32_t* query_start_loc, const int32_t* context_lens,
+                               int num_seqs, int num_query_tokens, int num_heads,
+                               int num_kv_heads, int head_dim, int block_size,
+                               int max_blocks_per_seq, int64_t num_blocks, int max_query_len,
+                               int max_context_len, int split_tokens, float scale, float k_scale,
+                               float v_scale, void* workspace, size_t workspace_bytes,
+                               pa_dtype dtype, hipStream_t stream);
 
 /*
  * pa_copy_blocks -- copy whole physical blocks inside the K and V pools.

@@ -8,7 +8,8 @@ from . import lib
 from .lib import (pa_decode, pa_decode_splitk_reduce, pa_decode_workspace_bytes,
                   pa_prefill_chunk, pa_reshape_and_cache, pa_reshape_and_cache_fp8,
                   pa_decode_fp8, pa_prefill_chunk_fp8, pa_decode_shared_prefix,
-                  pa_decode_fp8_shared_prefix, pa_sample, pa_copy_blocks, pa_swap_blocks,
+                  pa_decode_fp8_shared_prefix, pa_prefill_workspace_bytes,
+                  pa_prefill_chunk_split, pa_prefill_chunk_fp8_split, pa_sample, pa_copy_blocks, pa_swap_blocks,
                   pa_stream_read, pa_stream_read_sink_words,
                   pa_bm_create, pa_bm_destroy, pa_bm_add_sequence, pa_bm_fork, pa_bm_share,
                   pa_bm_free_sequence, pa_bm_append_slots, pa_bm_append_batch, pa_bm_swap_out,
@@ -21,7 +22,8 @@ from .lib import (pa_decode, pa_decode_splitk_reduce, pa_decode_workspace_bytes,
 __all__ = ["lib", "pa_decode", "pa_decode_splitk_reduce", "pa_decode_workspace_bytes",
            "pa_prefill_chunk", "pa_reshape_and_cache", "pa_reshape_and_cache_fp8",
            "pa_decode_fp8", "pa_prefill_chunk_fp8", "pa_decode_shared_prefix",
-           "pa_decode_fp8_shared_prefix", "pa_sample", "pa_copy_blocks", "pa_swap_blocks",
+           "pa_decode_fp8_shared_prefix", "pa_prefill_workspace_bytes",
+           "pa_prefill_chunk_split", "pa_prefill_chunk_fp8_split", "pa_sample", "pa_copy_blocks", "pa_swap_blocks",
            "pa_stream_read", "pa_stream_read_sink_words",
            "pa_bm_create", "pa_bm_destroy", "pa_bm_add_sequence", "pa_bm_fork", "pa_bm_share",
            "pa_bm_free_sequence", "pa_bm_append_slots", "pa_bm_append_batch", "pa_bm_swap_out",

@@ -14,6 +14,7 @@
 namespace {
 
 constexpr int kBlockSize = 16;
+constexpr int kPrefillKeyTile = 64;   // keys per prefill tile: split runs are whole tiles
 constexpr int kMaxGroup = 16;
 constexpr int64_t kMaxGridY = 65535;
 
@@ -302,8 +303,13 @@ int prefill_impl(void* out, const void* query, const void* key_cache, const void
                  const int32_t* context_lens, int num_seqs, int num_query_tokens, int num_heads,
                  int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
                  int64_t num_blocks, int max_query_len, float scale, bool fp8, float k_scale,
-                 float v_scale, pa_dtype dtype, hipStream_t stream) {
+                 float v_scale, pa_dtype dtype, hipStream_t stream, int split_tokens = 0,
+                 int max_context_len = 0, void* workspace = nullptr, size_t workspace_bytes = 0) {
   if (num_seqs < 0 || num_query_tokens < 0 || max_query_len < 0) return PA_ERR_SHAPE;
+  if (split_tokens < 0 || split_tokens % kPrefillKeyTile != 0 ||
+      (split_tokens > 0 && max_context_len < 0))
+    return PA_ERR_SHAPE;
+  if (split_tokens > 0 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;   // matrix-core path
   if (num_seqs > 0 && (!out || !query || !key_cache || !value_cache || !block_tables ||
                        !query_start_loc || !context_lens))
     return PA_ERR_NULL;
@@ -317,6 +323,14 @@ int prefill_impl(void* out, const void* query, const void* key_cache, const void
     return PA_ERR_SHAPE;
   if (num_heads / num_kv_heads > kMaxGroup) return PA_ERR_UNSUPPORTED;
   if ((int64_t)num_query_tokens * num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;
+  const int nsplit = split_tokens > 0 ? max_partitions(max_context_len, split_tokens) : 1;
+  if (split_tokens > 0) {
+    if (nsplit > kMaxGridY) return PA_ERR_SHAPE;
+    const size_t need = pa_prefill_workspace_bytes(num_query_tokens, num_heads, head_dim,
+                                                   max_context_len, split_tokens);
+    if (num_seqs > 0 && num_query_tokens > 0 && !workspace_ok(workspace, workspace_bytes, need))
+      return PA_ERR_WORKSPACE;
+  }
   if (num_seqs == 0 || num_query_tokens == 0) return PA_OK;
   pa::DecodeArgs a = {};
   a.out = out;
@@ -326,6 +340,11 @@ int prefill_impl(void* out, const void* query, const void* key_cache, const void
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.query_start_loc = query_start_loc;
+  if (split_tokens > 0) {
+    const size_t rows = (size_t)num_query_tokens * num_heads * nsplit;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = static_cast<float*>(workspace) + rows * head_dim;
+  }
   a.shared_prefix_blocks = nullptr;
   a.num_seqs = num_seqs;
   a.num_items = num_query_tokens;
@@ -334,9 +353,9 @@ int prefill_impl(void* out, const void* query, const void* key_cache, const void
   a.group = num_heads / num_kv_heads;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_blocks = num_blocks;
-  a.max_context_len = INT_MAX;
-  a.partition_blocks = 0;
-  a.max_partitions = 1;
+  a.max_context_len = split_tokens > 0 ? max_context_len : INT_MAX;
+  a.partition_blocks = split_tokens / kBlockSize;
+  a.max_partitions = nsplit;
   a.max_query_len = max_query_len;
   a.scale_log2 = scale * (fp8 ? k_scale : 1.f) * 1.4426950408889634f;
   a.v_scale = fp8 ? v_scale : 1.f;
@@ -370,6 +389,49 @@ int pa_prefill_chunk_fp8(void* out, const void* query, const uint8_t* key_cache,
                       context_lens, num_seqs, num_query_tokens, num_heads, num_kv_heads, head_dim,
                       block_size, max_blocks_per_seq, num_blocks, max_query_len, scale, true,
                       k_scale, v_scale, dtype, stream);
+}
+
+size_t pa_prefill_workspace_bytes(int num_query_tokens, int num_heads, int head_dim,
+                                  int max_context_len, int split_tokens) {
+  if (split_tokens <= 0 || num_query_tokens <= 0 || num_heads <= 0 || head_dim <= 0 ||
+      max_context_len < 0)
+    return 0;
+  const size_t rows = (size_t)num_query_tokens * (size_t)num_heads *
+                      (size_t)max_partitions(max_context_len, split_tokens);
+  return rows * (size_t)head_dim * sizeof(float) + rows * sizeof(float);
+}
+
+int pa_prefill_chunk_split(void* out, const void* query, const void* key_cache,
+                           const void* value_cache, const int32_t* block_tables,
+                           const int32_t* query_start_loc, const int32_t* context_lens,
+                           int num_seqs, int num_query_tokens, int num_heads, int num_kv_heads,
+                           int head_dim, int block_size, int max_blocks_per_seq,
+                           int64_t num_blocks, int max_query_len, int max_context_len,
+                           int split_tokens, float scale, void* workspace,
+                           size_t workspace_bytes, pa_dtype dtype, hipStream_t stream) {
+  if (split_tokens <= 0) return PA_ERR_SHAPE;
+  return prefill_impl(out, query, key_cache, value_cache, block_tables, query_start_loc,
+                      context_lens, num_seqs, num_query_tokens, num_heads, num_kv_heads, head_dim,
+                      block_size, max_blocks_per_seq, num_blocks, max_query_len, scale, false, 1.f,
+                      1.f, dtype, stream, split_tokens, max_context_len, workspace,
+                      workspace_bytes);
+}
+
+int pa_prefill_chunk_fp8_split(void* out, const void* query, const uint8_t* key_cache,
+                               const uint8_t* value_cache, const int32_t* block_tables,
+                               const int32_t* query_start_loc, const int32_t* context_lens,
+                               int num_seqs, int num_query_tokens, int num_heads,
+                               int num_kv_heads, int head_dim, int block_size,
+                               int max_blocks_per_seq, int64_t num_blocks, int max_query_len,
+                               int max_context_len, int split_tokens, float scale, float k_scale,
+                               float v_scale, void* workspace, size_t workspace_bytes,
+                               pa_dtype dtype, hipStream_t stream) {
+  if (split_tokens <= 0) return PA_ERR_SHAPE;
+  return prefill_impl(out, query, key_cache, value_cache, block_tables, query_start_loc,
+                      context_lens, num_seqs, num_query_tokens, num_heads, num_kv_heads, head_dim,
+                      block_size, max_blocks_per_seq, num_blocks, max_query_len, scale, true,
+                      k_scale, v_scale, dtype, stream, split_tokens, max_context_len, workspace,
+                      workspace_bytes);
 }
 
 int pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* block_mapping,

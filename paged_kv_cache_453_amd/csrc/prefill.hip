@@ -60,8 +60,14 @@ namespace pa {
 namespace {
 
 constexpr int kKeys = 64;             // keys per tile (4 blocks)
+constexpr int kXcds = 8;              // accelerator dies: workgroup ids go to them round-robin
 constexpr int kBufferWord3 = 0x00020000;   // raw 32-bit buffer resource, no format conversion
 constexpr float kSlack = 8.f;         // base-2 headroom of the lazy rescale
+// Starting reference max, below any score: a row that has seen only masked
+// keys (a split's first tile can lie above part of a wave's diagonal) keeps
+// weights exp2(-inf - kNoMax) = 0 and rescales by exp2(0) = 1, never by an
+// inf - inf.
+constexpr float kNoMax = -1e30f;
 // bf16 1.0 in every slot: A operand whose product with P^T is the row sums
 constexpr u32x4 kOnes = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 
@@ -98,9 +104,31 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[TILE];
   __shared__ int sh_bad;
 
-  const int qtile = gridDim.x - 1 - blockIdx.x;   // later (longer) tiles first
-  const int h = blockIdx.y;
-  const int s = blockIdx.z;
+  // blockIdx.x = query tile (later, longer tiles first) x key split: with
+  // split-K (a.partition_blocks > 0) the causal key range of a tile is cut
+  // into runs of a.partition_blocks blocks, one workgroup each
+  // Workgroup ids go to the accelerator dies (XCDs, each with its own L2)
+  // round-robin.  The workgroups that read one kv head's K/V -- its query tiles,
+  // splits and query heads, a group -- are numbered so that they all land on
+  // one XCD, one after another, and groups are dealt to the XCDs in turn: the
+  // K/V tiles a group stages are then read from HBM about once instead of once
+  // per query tile (prefix-cache prefill: 1.8x fewer bytes fetched by the L2s,
+  // 6% faster; whole prompts: 4.8x, 7%).
+  const int nsplit_max = a.partition_blocks > 0 ? a.max_partitions : 1;
+  const int qt_count = (a.max_query_len + QT - 1) / QT;
+  const int X = qt_count * nsplit_max;            // query tiles x splits of one head
+  const int gsize = X * a.group;                  // workgroups reading one kv head's K/V
+  const int ngroups = a.num_seqs * a.num_kv_heads;
+  const int xcd = blockIdx.x % kXcds;
+  const int k = blockIdx.x / kXcds;
+  const int grp = (k / gsize) * kXcds + xcd;
+  if (grp >= ngroups) return;
+  const int m = k - (k / gsize) * gsize;
+  const int s = grp / a.num_kv_heads;
+  const int h = (grp - s * a.num_kv_heads) * a.group + m / X;
+  const int xm = m % X;
+  const int qtile = qt_count - 1 - xm / nsplit_max;   // later (longer) tiles first
+  const int split = xm % nsplit_max;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = wave_uniform(tid >> 6);
@@ -117,12 +145,16 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
   const int len = a.context_lens[s];
   const int qr0 = qtile * QT;
   if (qr0 >= chunk) return;
-  const bool bad = chunk > len || chunk > a.max_query_len || len > a.max_blocks_per_seq * kBlock;
+  // (with split-K the workspace holds the splits of max_context_len keys)
+  const bool bad = chunk > len || chunk > a.max_query_len || len > a.max_blocks_per_seq * kBlock ||
+                   (a.partition_blocks > 0 && len > a.max_context_len);
   const int prefix = len - chunk;
   bf16_t* out = static_cast<bf16_t*>(a.out);
 
   if (bad) {
-    // the whole chunk of this sequence is reported as NaN
+    // the whole chunk of this sequence is reported as NaN (by the first split;
+    // the merge leaves such rows alone)
+    if (split != 0) return;
     for (int i = tid; i < QT * D; i += 256) {
       const int rr = qr0 + i / D;
       if (rr < chunk) out[((int64_t)(q0 + rr) * hq + h) * D + i % D] = 0x7FC0;
@@ -138,6 +170,14 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
   const int wave_first_pos = prefix + qw0;
   const int wave_last_pos = prefix + qw0 + wave_rows - 1;
 
+  const int qlast = min(chunk, qr0 + QT) - 1;
+  const int kend = prefix + qlast + 1;            // keys [0, kend) matter to this workgroup
+  const int ntiles = (kend + kKeys - 1) / kKeys;
+  const int nblk = (kend + kBlock - 1) / kBlock;
+  const int split_tiles = a.partition_blocks > 0 ? a.partition_blocks / 4 : ntiles;
+  const int nsplit = a.partition_blocks > 0 ? (ntiles + split_tiles - 1) / split_tiles : 1;
+  if (split >= nsplit) return;   // the whole workgroup: no barrier is left waiting
+
   // Q^T as the B operand: lane (r, g) holds chunk 4ks+g of query row 16qb + r.
   u32x4 qop[QB][KS];
 #pragma unroll
@@ -150,10 +190,6 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
                                : u32x4{0u, 0u, 0u, 0u};
   }
 
-  const int qlast = min(chunk, qr0 + QT) - 1;
-  const int kend = prefix + qlast + 1;            // keys [0, kend) matter to this workgroup
-  const int ntiles = (kend + kKeys - 1) / kKeys;
-  const int nblk = (kend + kBlock - 1) / kBlock;
   const float sl2 = a.scale_log2;
   const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
   const KV* kpool = static_cast<const KV*>(a.k_cache);
@@ -226,21 +262,26 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
   float mref[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    mref[qb] = -INFINITY;
+    mref[qb] = kNoMax;
     lacc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < DT; ++t) o[qb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  int ids_next = fetch_ids(0);
-  stage_load(0, ids_next);
-  ids_next = fetch_ids(1);
+  // this workgroup's key tiles [kt0, kt1); a prefetch past kt1 asks for tile
+  // ntiles, past the end, which reads nothing
+  const int kt0 = split * split_tiles;
+  const int kt1 = min(ntiles, kt0 + split_tiles);
+  const auto in_range = [&](int kt) { return kt < kt1 ? kt : ntiles; };
+  int ids_next = fetch_ids(kt0);
+  stage_load(kt0, ids_next);
+  ids_next = fetch_ids(in_range(kt0 + 1));
   stage_store();
 
-  for (int kt = 0; kt < ntiles; ++kt) {
+  for (int kt = kt0; kt < kt1; ++kt) {
     const int ids_cur = ids_next;
-    stage_load(kt + 1, ids_cur);     // past the last tile: empty resources, no traffic
-    ids_next = fetch_ids(kt + 2);
+    stage_load(in_range(kt + 1), ids_cur);   // past the last tile: empty resources, no traffic
+    ids_next = fetch_ids(in_range(kt + 2));
     lds_barrier();   // tile kt is in the buffer
 
     const int tile_first = kt * kKeys;
@@ -341,6 +382,27 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
   // ---- normalise and store: lane holds O[row 16qb + r][16t + 4g + i] ----
   lds_barrier();
   const bool poisoned = sh_bad != 0;
+  if (nsplit > 1) {
+    // a split's partial: its normalised output and the natural-log sum of
+    // exp(scores) over its keys; a row that saw none of them weighs nothing
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float l = lacc[qb][0];
+      const int qi = qw0 + 16 * qb + r;
+      if (qi >= chunk) continue;
+      const float inv = l > 0.f ? (kFp8 ? a.v_scale : 1.f) / l : 0.f;
+      const int64_t row = ((int64_t)(q0 + qi) * hq + h) * nsplit_max + split;
+      float* dst = a.part_o + row * D;
+      const float nan = __builtin_nanf("");
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+        *reinterpret_cast<f32x4*>(dst + 16 * t + 4 * g) =
+            poisoned ? f32x4{nan, nan, nan, nan} : o[qb][t] * inv;
+      if (g == 0)
+        a.part_lse[row] = poisoned ? nan : l > 0.f ? (mref[qb] + log2f(l)) * kLn2 : -INFINITY;
+    }
+    return;
+  }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l = lacc[qb][0];
@@ -361,15 +423,118 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
 // blocks (16 rows per wave measured 15% slower on the mixed workload's chunks).
 constexpr int kPrefillRowsPerWave = 32;
 
+// Merge of a split query tile's partials: for each of its rows,
+// out = sum_p exp(lse_p - M) o_p / sum_p exp(lse_p - M) with M = max_p lse_p
+// (exact in real arithmetic), the split-K rule of decode applied to the key
+// runs of a prefill tile.  One workgroup per (quarter of a query tile, head,
+// sequence): it finds the tile's number of splits as the prefill kernel did
+// and returns at once for an unsplit tile or a sequence that broke the
+// contract (its NaN is already written).  Threads first take one row each for
+// M and the sum of weights (LDS), then pieces of 8 columns of the rows, whose
+// partial loads are independent of each other.
+constexpr int kMergeParts = 4;          // workgroups per query tile
+template <int D, int QT>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(DecodeArgs a) {
+  constexpr int CW = 8;                 // columns per piece
+  constexpr int QR = QT / kMergeParts;  // rows of this workgroup
+  constexpr int NPIECE = QR * (D / CW);
+  __shared__ float sh_m[QR];
+  __shared__ float sh_inv[QR];
+  const int qtile = blockIdx.x / kMergeParts;
+  const int quarter = blockIdx.x % kMergeParts;
+  const int h = blockIdx.y;
+  const int s = blockIdx.z;
+  const int q0 = a.query_start_loc[s];
+  const int q1 = a.query_start_loc[s + 1];
+  if (q0 < 0 || q1 < q0 || q1 > a.num_items) return;
+  const int chunk = q1 - q0;
+  const int len = a.context_lens[s];
+  const int qr0 = qtile * QT;
+  if (qr0 >= chunk) return;
+  if (chunk > len || chunk > a.max_query_len || len > a.max_blocks_per_seq * kBlock ||
+      len > a.max_context_len)
+    return;
+  const int kend = len - chunk + min(chunk, qr0 + QT);
+  const int ntiles = (kend + kKeys - 1) / kKeys;
+  const int split_tiles = a.partition_blocks / 4;
+  const int n = (ntiles + split_tiles - 1) / split_tiles;
+  if (n <= 1) return;
+  const int r0 = qr0 + quarter * QR;   // first chunk row of this workgroup
+  const int rows = min(QR, chunk - r0);
+  if (rows <= 0) return;
+  const int hq = a.num_heads;
+  const int P = a.max_partitions;
+  const auto row_base = [&](int rr) { return ((int64_t)(q0 + r0 + rr) * hq + h) * P; };
+  for (int rr = threadIdx.x; rr < QR; rr += blockDim.x) {
+    float mm = -INFINITY, sum = 0.f;
+    bool nan = false;
+    if (rr < rows) {
+      const float* lse = a.part_lse + row_base(rr);
+      for (int p = 0; p < n; ++p) {
+        const float x = lse[p];
+        nan |= isnan(x);
+        mm = fmaxf(mm, x);
+      }
+      for (int p = 0; p < n; ++p) sum += expf(lse[p] - mm);
+    }
+    sh_m[rr] = mm;
+    sh_inv[rr] = nan ? __builtin_nanf("") : 1.f / sum;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < NPIECE; i += blockDim.x) {
+    const int rr = i / (D / CW);
+    if (rr >= rows) break;
+    const int c = (i - rr * (D / CW)) * CW;
+    const int64_t base = row_base(rr);
+    const float mm = sh_m[rr];
+    float acc[CW];
+#pragma unroll
+    for (int e = 0; e < CW; ++e) acc[e] = 0.f;
+    for (int p = 0; p < n; ++p) {
+      const float wt = expf(a.part_lse[base + p] - mm);
+      const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o + (base + p) * D + c);
+      const f32x4 lo = src[0], hi = src[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] = fmaf(wt, lo[e], acc[e]);
+        acc[4 + e] = fmaf(wt, hi[e], acc[4 + e]);
+      }
+    }
+    const float inv = sh_inv[rr];
+    u32x4 wv;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) wv[x] = pack_bf16x2(acc[2 * x] * inv, acc[2 * x + 1] * inv);
+    *reinterpret_cast<u32x4*>(static_cast<bf16_t*>(a.out) + (int64_t)(q0 + r0 + rr) * hq * D +
+                              (int64_t)h * D + c) = wv;
+  }
+}
+
 template <typename KV>
 hipError_t launch_prefill(const DecodeArgs& a, int head_dim, hipStream_t stream) {
   constexpr int RW = kPrefillRowsPerWave;
   if (a.num_seqs == 0 || a.max_query_len == 0) return hipSuccess;
-  dim3 grid((a.max_query_len + 4 * RW - 1) / (4 * RW), a.num_heads, a.num_seqs);
+  const int nsplit_max = a.partition_blocks > 0 ? a.max_partitions : 1;
+  // one dimension: (XCD, group, member) as the kernel decodes it, padded to
+  // whole rounds of the XCDs
+  const int64_t gsize = (int64_t)(a.max_query_len + 4 * RW - 1) / (4 * RW) * nsplit_max * a.group;
+  const int64_t ngroups = (int64_t)a.num_seqs * a.num_kv_heads;
+  const int64_t nwg = kXcds * ((ngroups + kXcds - 1) / kXcds) * gsize;
+  if (nwg > INT32_MAX) return hipErrorInvalidValue;
+  dim3 grid((unsigned)nwg);
   if (head_dim == 64)
     hipLaunchKernelGGL((prefill_mfma_kernel<KV, 64, RW>), grid, dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL((prefill_mfma_kernel<KV, 128, RW>), grid, dim3(256), 0, stream, a);
+  if (a.partition_blocks > 0 && nsplit_max > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 mgrid((a.max_query_len + 4 * RW - 1) / (4 * RW) * kMergeParts, a.num_heads,
+                     a.num_seqs);
+    if (head_dim == 64)
+      hipLaunchKernelGGL((prefill_merge_kernel<64, 4 * RW>), mgrid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((prefill_merge_kernel<128, 4 * RW>), mgrid, dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

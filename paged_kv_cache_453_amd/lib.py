@@ -89,6 +89,15 @@ def load() -> ctypes.CDLL:
                                                 i32, i32, i32, i32, i64, i32, f32, f32, f32, i32,
                                                 vp, sz, i32, vp]
     lib.pa_decode_fp8_shared_prefix.restype = i32
+    lib.pa_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.pa_prefill_workspace_bytes.restype = sz
+    lib.pa_prefill_chunk_split.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                           i32, i32, i64, i32, i32, i32, f32, vp, sz, i32, vp]
+    lib.pa_prefill_chunk_split.restype = i32
+    lib.pa_prefill_chunk_fp8_split.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                               i32, i32, i32, i64, i32, i32, i32, f32, f32, f32,
+                                               vp, sz, i32, vp]
+    lib.pa_prefill_chunk_fp8_split.restype = i32
     lib.pa_sample.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp, vp, i32, vp]
     lib.pa_sample.restype = i32
     lib.pa_copy_blocks.argtypes = [vp, vp, vp, i64, i32, i32, i32, i64, i32, vp]
@@ -137,7 +146,8 @@ def load() -> ctypes.CDLL:
 EXPORTED = ("pa_reshape_and_cache", "pa_decode_workspace_bytes", "pa_decode",
             "pa_decode_splitk_reduce", "pa_prefill_chunk", "pa_reshape_and_cache_fp8",
             "pa_decode_fp8", "pa_prefill_chunk_fp8", "pa_decode_shared_prefix",
-            "pa_decode_fp8_shared_prefix", "pa_sample", "pa_copy_blocks",
+            "pa_decode_fp8_shared_prefix", "pa_prefill_workspace_bytes", "pa_prefill_chunk_split",
+            "pa_prefill_chunk_fp8_split", "pa_sample", "pa_copy_blocks",
             "pa_swap_blocks", "pa_stream_read_sink_words", "pa_stream_read", "pa_status_string")
 
 
@@ -345,6 +355,67 @@ def pa_prefill_chunk(out, query, key_cache, value_cache, block_tables, query_sta
         _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
         _ptr(query_start_loc), _ptr(context_lens), s, tq, hq, hkv, d, bs, block_tables.shape[1],
         nb, int(max_query_len), float(scale), _dtype_code(query), _stream(stream)))
+
+
+def pa_prefill_workspace_bytes(num_query_tokens: int, num_heads: int, head_dim: int,
+                               max_context_len: int, split_tokens: int) -> int:
+    return int(load().pa_prefill_workspace_bytes(num_query_tokens, num_heads, head_dim,
+                                                 max_context_len, split_tokens))
+
+
+def _prefill_marshal(out, query, key_cache, value_cache, block_tables, query_start_loc,
+                     context_lens, workspace, fp8: bool):
+    torch = _torch()
+    _on_gpu(out, query, key_cache, value_cache, block_tables, query_start_loc, context_lens,
+            workspace)
+    _need(block_tables.dtype == torch.int32 and query_start_loc.dtype == torch.int32 and
+          context_lens.dtype == torch.int32, "index arrays must be int32")
+    tq, hq, d = query.shape
+    nb, hkv, bs, d2 = key_cache.shape
+    s = context_lens.numel()
+    _need(d2 == d and tuple(out.shape) == (tq, hq, d) and value_cache.shape == key_cache.shape,
+          "shape mismatch")
+    _need(query_start_loc.numel() == s + 1 and block_tables.shape[0] == s, "sequence count mismatch")
+    if fp8:
+        _need(key_cache.dtype == torch.uint8 and value_cache.dtype == torch.uint8,
+              "FP8 caches are uint8 tensors of E4M3 codes")
+        _need(out.dtype == query.dtype, "query and output dtypes differ")
+    else:
+        _need(out.dtype == query.dtype == key_cache.dtype == value_cache.dtype, "dtype mismatch")
+    return s, tq, hq, hkv, d, bs, nb, workspace.numel() * workspace.element_size()
+
+
+def pa_prefill_chunk_split(out, query, key_cache, value_cache, block_tables, query_start_loc,
+                           context_lens, scale: float, max_query_len: int, max_context_len: int,
+                           split_tokens: int, workspace, stream=None) -> None:
+    """pa_prefill_chunk with long causal key ranges split over workgroups (split_tokens keys
+    each) and merged; workspace of pa_prefill_workspace_bytes() bytes."""
+    lib = load()
+    s, tq, hq, hkv, d, bs, nb, wsb = _prefill_marshal(
+        out, query, key_cache, value_cache, block_tables, query_start_loc, context_lens,
+        workspace, fp8=False)
+    _check("pa_prefill_chunk_split", lib.pa_prefill_chunk_split(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(query_start_loc), _ptr(context_lens), s, tq, hq, hkv, d, bs, block_tables.shape[1],
+        nb, int(max_query_len), int(max_context_len), int(split_tokens), float(scale),
+        _ptr(workspace), wsb, _dtype_code(query), _stream(stream)))
+
+
+def pa_prefill_chunk_fp8_split(out, query, key_cache, value_cache, block_tables, query_start_loc,
+                               context_lens, scale: float, k_scale: float, v_scale: float,
+                               max_query_len: int, max_context_len: int, split_tokens: int,
+                               workspace, stream=None) -> None:
+    """pa_prefill_chunk_split over uint8 E4M3 caches."""
+    lib = load()
+    s, tq, hq, hkv, d, bs, nb, wsb = _prefill_marshal(
+        out, query, key_cache, value_cache, block_tables, query_start_loc, context_lens,
+        workspace, fp8=True)
+    _check("pa_prefill_chunk_fp8_split", lib.pa_prefill_chunk_fp8_split(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(query_start_loc), _ptr(context_lens), s, tq, hq, hkv, d, bs, block_tables.shape[1],
+        nb, int(max_query_len), int(max_context_len), int(split_tokens), float(scale),
+        float(k_scale), float(v_scale), _ptr(workspace), wsb, _dtype_code(query),
+        _stream(stream)))
 
 
 # --------------------------------------------------------------------------

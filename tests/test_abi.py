@@ -313,3 +313,33 @@ def test_prefix_groups_validation(lib):
         assert n.value == 0
     finally:
         lib.pa_bm_destroy(h)
+
+
+def prefill_split(lib, fp8=False, **kw):
+    args = dict(out=P, query=P, k=P, v=P, bt=P, qsl=P, cl=P, S=2, tq=64, hq=8, hkv=8, d=128,
+                bs=16, mb=8, nb=64, maxq=32, maxc=128, split=64, scale=0.1, ws=None, wsb=0,
+                dtype=BF16, stream=None)
+    args.update(kw)
+    a = args
+    head = (a["out"], a["query"], a["k"], a["v"], a["bt"], a["qsl"], a["cl"], a["S"], a["tq"],
+            a["hq"], a["hkv"], a["d"], a["bs"], a["mb"], a["nb"], a["maxq"], a["maxc"],
+            a["split"], a["scale"])
+    tail = (a["ws"], a["wsb"], a["dtype"], a["stream"])
+    if fp8:
+        return lib.pa_prefill_chunk_fp8_split(*head, 0.5, 0.5, *tail)
+    return lib.pa_prefill_chunk_split(*head, *tail)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_prefill_split_validation(lib, fp8):
+    need = lib.pa_prefill_workspace_bytes(64, 8, 128, 128, 64)
+    assert need == 64 * 8 * 2 * 129 * 4
+    assert lib.pa_prefill_workspace_bytes(64, 8, 128, 128, 0) == 0
+    assert prefill_split(lib, fp8, split=0) == PA_ERR_SHAPE
+    assert prefill_split(lib, fp8, split=96) == PA_ERR_SHAPE          # not a multiple of 64
+    assert prefill_split(lib, fp8, dtype=F32) == PA_ERR_UNSUPPORTED
+    assert prefill_split(lib, fp8) == PA_ERR_WORKSPACE
+    assert prefill_split(lib, fp8, ws=P, wsb=need - 1) == PA_ERR_WORKSPACE
+    assert prefill_split(lib, fp8, ws=P + 8, wsb=need) == PA_ERR_WORKSPACE
+    assert prefill_split(lib, fp8, out=None, ws=P, wsb=need) == PA_ERR_NULL
+    assert prefill_split(lib, fp8, S=0, out=None, query=None) == PA_OK
