@@ -582,7 +582,7 @@ def bench_prefix_cache(args, torch, dev, lib, timer) -> int:
         "ms_per_step": round(ms["with_hits"], 5), "higher_is_better": False, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "32 prompts sharing a 2048-token system prompt + 256 own tokens, "
-                               "40 = 40 heads, head_dim 128, bf16, block size 16",
+                               "40 query and 40 kv heads, head_dim 128, bf16, block size 16",
                    "cached_tokens_per_prompt": sys_len, "seed": 453},
         "whole_prompt_prefill_us": round(ms["whole"] * 1e3, 2),
         "prefill_speedup": round(ms["whole"] / ms["with_hits"], 2),
@@ -648,7 +648,7 @@ def bench_prefill_long(args, torch, dev, lib, timer) -> int:
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{nseq} chunks of {chunk} query tokens over {prefix}-token paged "
-                               f"prefixes, 40 = 40 heads, head_dim 128, bf16, block size 16",
+                               f"prefixes, 40 query and 40 kv heads, head_dim 128, bf16, block size 16",
                    "split_tokens": split, "seed": 453},
         "prefill_us": {"split": round(ms["split"] * 1e3, 2),
                        "unsplit": round(ms["unsplit"] * 1e3, 2)},
