@@ -196,16 +196,23 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
   const KV* vpool = static_cast<const KV*>(a.v_cache);
 
   // Staging: thread (key row kr0 + KPP*p, chunk cc) for p < NPASS.  Block ids
-  // of a tile sit in lanes 0..3 of ids (fetched two tiles ahead from an
-  // in-bounds, clamped index); the block a thread's row falls in is the same
-  // for the whole wave.  Each block is read through a buffer resource sized to
-  // its live rows (keys < kend), so rows past the end, blocks past the last
-  // one and ids outside the pool read as zeros without touching memory.  All
-  // staging loads are unconditional, which keeps the compiler's load counting
-  // exact: the waits before the LDS stores cover only what they store.
+  // of a tile sit in lanes 0..3 of ids, repeated across the wave (fetched two
+  // tiles ahead from an in-bounds, clamped index).  Each lane works out, on
+  // the vector ALUs and once per tile, the pool offset and live bytes of
+  // block lane & 3; every pass then reads its block's pair into scalars.  The
+  // rows of one pass of one wave lie in one block.  Each block is read
+  // through a buffer resource sized to its live rows (keys < kend), so rows
+  // past the end, blocks past the last one and ids outside the pool read as
+  // zeros without touching memory.  All staging loads are unconditional,
+  // which keeps the compiler's load counting exact: the waits before the LDS
+  // stores cover only what they store.
+  static_assert(kKeys == 4 * kBlock && KPP % kBlock == 0 && (64 / CH) <= kBlock,
+                "a pass of a wave stays in one block");
   const int cc = tid % CH;
   const int kr0 = tid / CH;
   const int row_bytes = D * (int)sizeof(KV);
+  // the byte of its row a thread loads, the same in every pass (KPP rows apart)
+  const int lane_off = (kr0 % kBlock) * row_bytes + cc * 8 * (int)sizeof(KV);
   // what one thread loads per key row: 8 elements (16 bytes of bf16, 8 of fp8)
   typedef typename std::conditional<kFp8, u32x2, u32x4>::type piece_t;
   const auto fetch_ids = [&](int kt) {
@@ -214,23 +221,26 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
   };
   piece_t kst[NPASS], vst[NPASS];
   const auto stage_load = [&](int kt, int ids) {
+    const int gb = kt * 4 + (lane & 3);                     // block within the sequence
+    const bool in_pool = ids >= 0 && (int64_t)ids < a.num_blocks;
+    const int rows = gb < nblk ? min(kBlock, kend - gb * kBlock) : 0;
+    if (rows > 0 && !in_pool) sh_bad = 1;
+    const bool live = rows > 0 && in_pool;
+    const int64_t off =
+        live ? ((int64_t)ids * a.num_kv_heads + kvh) * (kBlock * D * (int)sizeof(KV)) : 0;
+    const int nbytes = live ? rows * row_bytes : 0;
+    const uint32_t off_lo = (uint32_t)off, off_hi = (uint32_t)((uint64_t)off >> 32);
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
-      const int key = kr0 + KPP * p;
-      const int bt = wave_uniform(key / kBlock);           // block within the tile
-      const int gb = kt * 4 + bt;                           // block within the sequence
-      const int bid = __builtin_amdgcn_readlane(ids, bt);
-      const bool in_pool = bid >= 0 && (int64_t)bid < a.num_blocks;
-      const int rows = gb < nblk ? min(kBlock, kend - gb * kBlock) : 0;
-      if (rows > 0 && !in_pool) sh_bad = 1;
-      const bool live = rows > 0 && in_pool;
-      const int64_t off = live ? ((int64_t)bid * a.num_kv_heads + kvh) * kBlock * D : 0;
-      const int nbytes = live ? rows * row_bytes : 0;
-      const int lane_off = (key % kBlock) * row_bytes + cc * 8 * (int)sizeof(KV);
-      const auto krs =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<KV*>(kpool + off), 0, nbytes, kBufferWord3);
-      const auto vrs =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<KV*>(vpool + off), 0, nbytes, kBufferWord3);
+      const int bt = (KPP * p + (64 / CH) * w) / kBlock;   // this wave's block in the tile
+      const uint64_t boff =
+          ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)off_hi, bt) << 32) |
+          (uint32_t)__builtin_amdgcn_readlane((int)off_lo, bt);
+      const int nb = __builtin_amdgcn_readlane(nbytes, bt);
+      const auto krs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(kpool) + boff), 0, nb, kBufferWord3);
+      const auto vrs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(vpool) + boff), 0, nb, kBufferWord3);
       if constexpr (kFp8) {
         kst[p] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(krs, lane_off, 0, 0));
         vst[p] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(vrs, lane_off, 0, 0));
