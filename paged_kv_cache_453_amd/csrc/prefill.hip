@@ -88,17 +88,18 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* base, int off) {
 
 }  // namespace
 
-template <typename KV, int D, int RW>
-__global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
+template <typename KV, int D, int RW, int NW>
+__global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(DecodeArgs a) {
   constexpr bool kFp8 = sizeof(KV) == 1;
   constexpr int KS = D / 32;            // k-steps of the score MFMA
   constexpr int DT = D / 16;            // d-tiles of the output (= columns per lane per key)
   constexpr int QB = RW / 16;           // 16-row query blocks per wave
-  constexpr int QT = 4 * RW;            // query rows per workgroup
+  constexpr int QT = NW * RW;           // query rows per workgroup (NW waves)
+  constexpr int NT = 64 * NW;           // threads per workgroup
   constexpr int ROW = D * 2 + 16;       // padded LDS row of K, bytes
   constexpr int ROWV = D * 2 + 32;      // padded LDS row of V, bytes
   constexpr int CH = D / 8;             // 16-byte chunks per row
-  constexpr int KPP = 256 / CH;         // key rows staged per pass of the workgroup
+  constexpr int KPP = NT / CH;          // key rows staged per pass of the workgroup
   constexpr int NPASS = kKeys / KPP;    // staging passes per tile
   constexpr int TILE = kKeys * (ROW + ROWV);   // K rows, then V rows
   __shared__ __attribute__((aligned(16))) uint8_t smem[TILE];
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
     // the whole chunk of this sequence is reported as NaN (by the first split;
     // the merge leaves such rows alone)
     if (split != 0) return;
-    for (int i = tid; i < QT * D; i += 256) {
+    for (int i = tid; i < QT * D; i += NT) {
       const int rr = qr0 + i / D;
       if (rr < chunk) out[((int64_t)(q0 + rr) * hq + h) * D + i % D] = 0x7FC0;
     }
@@ -432,6 +433,11 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
 // 32 query rows per wave: each K/V operand read from LDS feeds two 16-row
 // blocks (16 rows per wave measured 15% slower on the mixed workload's chunks).
 constexpr int kPrefillRowsPerWave = 32;
+// waves per workgroup: they share each staged K/V tile.  8 waves (256 query
+// rows) stage half as much per row but measured mixed: 3% faster on 256-row
+// chunks over cached prefixes, 7% on long unsplit prefixes, 16% slower on
+// grouped-query chunks and 9% slower split over keys.
+constexpr int kPrefillWaves = 4;
 
 // Merge of a split query tile's partials: for each of its rows,
 // out = sum_p exp(lse_p - M) o_p / sum_p exp(lse_p - M) with M = max_p lse_p
@@ -522,28 +528,29 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(DecodeArgs a) {
 template <typename KV>
 hipError_t launch_prefill(const DecodeArgs& a, int head_dim, hipStream_t stream) {
   constexpr int RW = kPrefillRowsPerWave;
+  constexpr int NW = kPrefillWaves;
+  constexpr int QT = NW * RW;
   if (a.num_seqs == 0 || a.max_query_len == 0) return hipSuccess;
   const int nsplit_max = a.partition_blocks > 0 ? a.max_partitions : 1;
   // one dimension: (XCD, group, member) as the kernel decodes it, padded to
   // whole rounds of the XCDs
-  const int64_t gsize = (int64_t)(a.max_query_len + 4 * RW - 1) / (4 * RW) * nsplit_max * a.group;
+  const int64_t gsize = (int64_t)(a.max_query_len + QT - 1) / QT * nsplit_max * a.group;
   const int64_t ngroups = (int64_t)a.num_seqs * a.num_kv_heads;
   const int64_t nwg = kXcds * ((ngroups + kXcds - 1) / kXcds) * gsize;
   if (nwg > INT32_MAX) return hipErrorInvalidValue;
   dim3 grid((unsigned)nwg);
   if (head_dim == 64)
-    hipLaunchKernelGGL((prefill_mfma_kernel<KV, 64, RW>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((prefill_mfma_kernel<KV, 64, RW, NW>), grid, dim3(64 * NW), 0, stream, a);
   else
-    hipLaunchKernelGGL((prefill_mfma_kernel<KV, 128, RW>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((prefill_mfma_kernel<KV, 128, RW, NW>), grid, dim3(64 * NW), 0, stream, a);
   if (a.partition_blocks > 0 && nsplit_max > 1) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 mgrid((a.max_query_len + 4 * RW - 1) / (4 * RW) * kMergeParts, a.num_heads,
-                     a.num_seqs);
+    const dim3 mgrid((a.max_query_len + QT - 1) / QT * kMergeParts, a.num_heads, a.num_seqs);
     if (head_dim == 64)
-      hipLaunchKernelGGL((prefill_merge_kernel<64, 4 * RW>), mgrid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((prefill_merge_kernel<64, QT>), mgrid, dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL((prefill_merge_kernel<128, 4 * RW>), mgrid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((prefill_merge_kernel<128, QT>), mgrid, dim3(256), 0, stream, a);
   }
   return hipGetLastError();
 }
