@@ -102,6 +102,29 @@ def test_prefill_contract_violation_gives_nan(gpu):
     assert_close(out[:20], oracle_prefill(w)[:20], "bf16", "healthy sequence")
 
 
+@pytest.mark.parametrize("bad_id", ["past_pool", "negative"])
+def test_prefill_block_outside_pool_gives_nan(gpu, bad_id):
+    """A live block id outside the pool (past its end, or negative) turns that
+    sequence's chunk into NaN; nothing is read for it, and the other sequences
+    are unchanged."""
+    import torch
+    w = make_prefill("bad-id", 77, "bf16", [40, 100, 30], [20, 70, 90], 4, 2, 128, 64)
+    dw = to_device(w)
+    g = dw.prefill
+    bt = g.block_tables.clone()
+    bt[1, 3] = w.num_blocks if bad_id == "past_pool" else -7   # keys 48..63 of 170: live
+    g.block_tables = bt
+    say(f"prefill with block id {int(bt[1, 3])} in sequence 1 of 3")
+    gpu_prefill(dw)
+    torch.cuda.synchronize()
+    out = as_f64(g.out)
+    ref = oracle_prefill(w)
+    q = w.prefill.query_start_loc
+    assert np.isnan(out[q[1]:q[2]]).all()
+    for s in (0, 2):
+        assert_close(out[q[s]:q[s + 1]], ref[q[s]:q[s + 1]], "bf16", f"sequence {s}")
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("ps", [512, 2048])   # 2048: the launch bench.py times
 def test_mixed_step_prefill_then_decode(gpu, ps):

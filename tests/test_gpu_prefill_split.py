@@ -76,6 +76,35 @@ def test_fp8_split(gpu):
     assert_close(as_f64(out), want, "bf16", "fp8 split prefill")
 
 
+def test_split_block_outside_pool_gives_nan(gpu):
+    """A negative block id in one key run: that run's partials are NaN, so the
+    merge gives NaN for the whole chunk of its sequence; other sequences match."""
+    import torch
+    L = lib()
+    w = make_prefill("split-bad-id", 89, "bf16", [300, 900, 50], [40, 100, 60], 4, 2, 128, 128)
+    dw = to_device(w)
+    g = dw.prefill
+    bt = g.block_tables.clone()
+    bt[1, 20] = -3                  # keys 320..335 of 1000: the second run of 256
+    g.block_tables = bt
+    tq, hq, d = g.query.shape
+    maxc = int(w.prefill.context_lens.max())
+    ws = torch.empty(L.pa_prefill_workspace_bytes(tq, hq, d, maxc, 256), dtype=torch.uint8,
+                     device="cuda")
+    ws.fill_(0xFF)
+    say("split prefill (runs of 256) with block id -3 in sequence 1 of 3")
+    L.pa_prefill_chunk_split(g.out, g.query, dw.k_cache, dw.v_cache, g.block_tables,
+                             g.query_start_loc, g.context_lens, w.scale, g.max_query_len, maxc,
+                             256, ws)
+    torch.cuda.synchronize()
+    out = as_f64(g.out)
+    ref = oracle_prefill(w)
+    q = w.prefill.query_start_loc
+    assert np.isnan(out[q[1]:q[2]]).all()
+    for s in (0, 2):
+        assert_close(out[q[s]:q[s + 1]], ref[q[s]:q[s + 1]], "bf16", f"sequence {s}")
+
+
 def test_split_contract(gpu):
     """A sequence longer than max_context_len gets NaN rows and nobody else
     changes; a short workspace and an fp32 query are refused."""
