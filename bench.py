@@ -20,7 +20,7 @@ shuffled pool) with split-K partitions and their merge.
             one scale per pool: quantising scatter (llama13b), chunked prefill
             (mixed), decode, merge; KV bytes count one byte per element
   prefill_long  4 chunks of 128 tokens over 16384-token paged prefixes (40
-            heads): the split prefill (runs of 2048 keys) against one workgroup
+            heads): the split prefill (runs of 3072 keys) against one workgroup
             per query tile
   prefix_cache  32 prompts at Llama-2-13B shape sharing a 2048-token system
             prompt, each with 256 tokens of its own: the chunked prefill of
@@ -594,7 +594,7 @@ def bench_prefix_cache(args, torch, dev, lib, timer) -> int:
                               "lookup, slots) and the batch's take_moves, through the C ABI",
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "kernel": "prefill_mfma_kernel<128,32>",
+                     "traffic": None, "kernel": "prefill_mfma_kernel<bf16,128,32,4>",
                      "algorithmic_flops_per_launch": int(flops_hit),
                      "whole_prompt_flops": int(flops_whole)},
         "cpu_baseline": None if args.no_cpu_baseline else prefix_cpu_baseline(d, hq, own, total),
@@ -613,7 +613,9 @@ def bench_prefill_long(args, torch, dev, lib, timer) -> int:
     from workloads.device import to_device
 
     nseq, prefix, chunk, h, d = 4, 16384, 128, 40, 128
-    split = args.prefill_split or 2048
+    # runs of 3072 keys: 6 per query tile, 960 workgroups, just under two rounds
+    # of the part's 512 workgroup slots (the fastest of 1536-4096)
+    split = args.prefill_split or 3072
     w = make_prefill("prefill-long", 453, "bf16", [prefix] * nseq, [chunk] * nseq, h, h, d,
                      nseq * ((prefix + chunk) // 16 + 1))
     dw = to_device(w, device=dev)
@@ -656,7 +658,7 @@ def bench_prefill_long(args, torch, dev, lib, timer) -> int:
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": None,
-                     "kernel": f"prefill_mfma_kernel<bf16,128,32> in runs of {split} keys + "
+                     "kernel": f"prefill_mfma_kernel<bf16,128,32,4> in runs of {split} keys + "
                                "prefill_merge_kernel (one pa_prefill_chunk_split call)",
                      "algorithmic_flops_per_launch": int(flops),
                      "unsplit_achieved": round(tf_plain, 2),
@@ -773,7 +775,7 @@ def main(argv=None):
     ap.add_argument("--prefill-split", type=int, default=None,
                     help="keys per run of the split prefill (pa_prefill_chunk_split): mixed "
                          "workloads default to 0 = pa_prefill_chunk, one workgroup per query "
-                         "tile; prefill_long defaults to 2048")
+                         "tile; prefill_long defaults to 3072")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode call and its merge (for counter runs); prints "
                          "a short JSON line")
@@ -1023,7 +1025,7 @@ def main(argv=None):
         extra["roofline_prefill"] = {
             "bound": "mfma", "achieved": round(pf_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(pf_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None, "kernel": f"prefill_mfma_kernel<{kv_name},128,32>" + (
+            "traffic": None, "kernel": f"prefill_mfma_kernel<{kv_name},128,32,4>" + (
                 f" in runs of {pf_split} keys + prefill_merge_kernel (one "
                 "pa_prefill_chunk_split call)" if pf_split else ""),
             "algorithmic_flops_per_launch": int(flops)}

@@ -136,10 +136,10 @@ def test_split_contract(gpu):
 
 @pytest.mark.slow
 def test_long_prefix_split_launch(gpu):
-    """The launch bench.py --workload prefill_long times: runs of 2048 keys over
+    """The launch bench.py --workload prefill_long times: runs of 3072 keys over
     a 16384-token prefix with a 128-token chunk (one sequence, 8 heads, so the
     oracle finishes in seconds)."""
-    say("split prefill: 128-token chunk over a 16384-token prefix, runs of 2048 keys")
+    say("split prefill: 128-token chunk over a 16384-token prefix, runs of 3072 keys")
     w = make_prefill("split-long", 89, "bf16", [16384], [128], 8, 8, 128, 1040)
-    out = run_split(w, 2048)
+    out = run_split(w, 3072)
     assert_close(as_f64(out), oracle_prefill(w), "bf16", "long prefix split")
