@@ -154,12 +154,14 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(DecodeArgs a) {
 
   if (bad) {
     // the whole chunk of this sequence is reported as NaN (by the first split;
-    // the merge leaves such rows alone)
+    // the merge leaves such rows alone).  The grid has tiles for max_query_len
+    // rows only, so a longer chunk is covered by striding over them.
     if (split != 0) return;
-    for (int i = tid; i < QT * D; i += NT) {
-      const int rr = qr0 + i / D;
-      if (rr < chunk) out[((int64_t)(q0 + rr) * hq + h) * D + i % D] = 0x7FC0;
-    }
+    for (int base = qr0; base < chunk; base += qt_count * QT)
+      for (int i = tid; i < QT * D; i += NT) {
+        const int rr = base + i / D;
+        if (rr < chunk) out[((int64_t)(q0 + rr) * hq + h) * D + i % D] = 0x7FC0;
+      }
     return;
   }
   if (tid == 0) sh_bad = 0;

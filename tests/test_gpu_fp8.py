@@ -115,7 +115,7 @@ def fp8_workload(qdtype, hq, hkv, d, ps, seed=71, nseq=24):
                        hkv, d, num_blocks=1024, with_scatter=False, partition_size=ps)
 
 
-def run_fp8_decode(gpu, w, k_codes, v_codes, ps, hint=None):
+def run_fp8_decode(gpu, w, k_codes, v_codes, ps, hint=None, scales=(K_SCALE, V_SCALE)):
     import torch
     dw = to_device(w)
     kc, vc = upload_fp8_pools(w, k_codes, v_codes)
@@ -126,7 +126,7 @@ def run_fp8_decode(gpu, w, k_codes, v_codes, ps, hint=None):
                                                g.max_context_len, ps)
         ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
     gpu.pa_decode_fp8(g.out, g.query, kc, vc, g.block_tables, g.context_lens, float(w.scale),
-                      K_SCALE, V_SCALE, g.max_context_len, ps, ws, shared_prefix_blocks=hint)
+                      scales[0], scales[1], g.max_context_len, ps, ws, shared_prefix_blocks=hint)
     if ps:
         gpu.pa_decode_splitk_reduce(g.out, ws, g.context_lens, g.max_context_len, ps)
     torch.cuda.synchronize()
@@ -143,6 +143,30 @@ def test_fp8_decode_matches_oracle(gpu, qdtype, hq, hkv, d, ps):
     want = kv_fp8.decode(g.query, kq, vq, w.host_tables(g.block_tables), g.context_lens, w.scale,
                          K_SCALE, V_SCALE, qdtype)
     assert_close(as_f64(out), want, qdtype, f"fp8 decode {qdtype} {hq}/{hkv} d={d} ps={ps}")
+
+
+# Every finite code (exponent fields 0..14, magnitudes up to 448) in K and V, on
+# each decode path: the vector ALUs with fp32 and bf16 queries, and the matrix
+# cores.  Power-of-two scales keep the values the size of the N(0, 1) workloads
+# the tolerance is stated for: |k| <= 448 / 256 = 1.75, |v| <= 448 / 512 = 0.875.
+# (The matrix-core paths round each weight to bf16, an error that grows with the
+# spread of V: with |v| up to 22, a few elements in 10^5 passed the absolute
+# 4e-3 bound, while the vector-ALU paths, which keep fp32 weights, did not.)
+FULL_RANGE_SCALES = (2.0 ** -8, 2.0 ** -9)
+
+
+@pytest.mark.parametrize("qdtype,hq,hkv,d,ps", [("f32", 8, 8, 128, 256), ("bf16", 8, 2, 64, 0),
+                                                ("bf16", 16, 4, 128, 256),
+                                                ("bf16", 32, 8, 128, 512)])
+def test_fp8_decode_full_code_range(gpu, qdtype, hq, hkv, d, ps):
+    say(f"fp8 decode, full code range, q={qdtype} hq={hq} hkv={hkv} d={d} ps={ps}")
+    w = fp8_workload(qdtype, hq, hkv, d, ps, seed=93)
+    kq, vq = fp8_pools(w, 94, max_exp_field=14)
+    _, out = run_fp8_decode(gpu, w, kq, vq, ps, scales=FULL_RANGE_SCALES)
+    g = w.decode
+    want = kv_fp8.decode(g.query, kq, vq, w.host_tables(g.block_tables), g.context_lens, w.scale,
+                         *FULL_RANGE_SCALES, qdtype)
+    assert_close(as_f64(out), want, qdtype, f"fp8 full-range decode {qdtype} {hq}/{hkv} ps={ps}")
 
 
 @pytest.mark.parametrize("qdtype,hq,hkv,d,ps", [("bf16", 8, 8, 128, 0), ("bf16", 32, 4, 128, 512)])
@@ -211,21 +235,35 @@ def test_fp8_llama13b_scatter_then_decode(gpu):
     assert_close(as_f64(g.out)[pick], want, "bf16", "fp8 13B decode (sampled)")
 
 
-def run_fp8_prefill(gpu, w, k_codes, v_codes):
+def run_fp8_prefill(gpu, w, k_codes, v_codes, scales=(K_SCALE, V_SCALE)):
     import torch
     dw = to_device(w)
     kc, vc = upload_fp8_pools(w, k_codes, v_codes)
     g = dw.prefill
     gpu.pa_prefill_chunk_fp8(g.out, g.query, kc, vc, g.block_tables, g.query_start_loc,
-                             g.context_lens, float(w.scale), K_SCALE, V_SCALE, g.max_query_len)
+                             g.context_lens, float(w.scale), scales[0], scales[1],
+                             g.max_query_len)
     torch.cuda.synchronize()
     return dw, kc, vc
 
 
-def oracle_fp8_prefill(w, k_codes, v_codes):
+def oracle_fp8_prefill(w, k_codes, v_codes, scales=(K_SCALE, V_SCALE)):
     g = w.prefill
     return kv_fp8.prefill(g.query, k_codes, v_codes, w.host_tables(g.block_tables),
-                          g.query_start_loc, g.context_lens, w.scale, K_SCALE, V_SCALE, "bf16")
+                          g.query_start_loc, g.context_lens, w.scale, scales[0], scales[1],
+                          "bf16")
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(8, 2, 128), (6, 3, 64)])
+def test_fp8_prefill_full_code_range(gpu, hq, hkv, d):
+    """Every finite code in K and V through the prefill's staging widening."""
+    say(f"fp8 prefill, full code range, hq={hq} hkv={hkv} d={d}")
+    w = make_prefill(f"fp8-prefill-full-{hq}-{hkv}-{d}", 95, "bf16", [0, 37, 300, 1000],
+                     [130, 64, 200, 77], hq, hkv, d, 256)
+    kq, vq = fp8_pools(w, 96, max_exp_field=14)
+    dw, _, _ = run_fp8_prefill(gpu, w, kq, vq, scales=FULL_RANGE_SCALES)
+    assert_close(as_f64(dw.prefill.out), oracle_fp8_prefill(w, kq, vq, scales=FULL_RANGE_SCALES),
+                 "bf16", f"fp8 full-range prefill {hq}/{hkv} d={d}")
 
 
 @pytest.mark.parametrize("hq,hkv,d", [(4, 4, 128), (8, 2, 128), (6, 3, 64), (32, 8, 128)])

@@ -102,6 +102,25 @@ def test_prefill_contract_violation_gives_nan(gpu):
     assert_close(out[:20], oracle_prefill(w)[:20], "bf16", "healthy sequence")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_chunk_longer_than_max_query_len_gives_nan(gpu, dtype):
+    """max_query_len = 100 while sequence 1 brings 300 query rows: its whole
+    chunk is NaN, rows past the first 128-row tile included; sequence 0 (100
+    rows) is unchanged."""
+    import torch
+    from paged_kv_cache_453_amd import lib as L
+    w = make_prefill("too-long", 78, dtype, [10, 10], [100, 300], 4, 4, 128, 64)
+    dw = to_device(w)
+    g = dw.prefill
+    say(f"prefill {dtype}: chunk of 300 rows with max_query_len 100")
+    L.pa_prefill_chunk(g.out, g.query, dw.k_cache, dw.v_cache, g.block_tables,
+                       g.query_start_loc, g.context_lens, w.scale, 100)
+    torch.cuda.synchronize()
+    out = as_f64(g.out)
+    assert np.isnan(out[100:]).all()
+    assert_close(out[:100], oracle_prefill(w)[:100], dtype, "healthy sequence")
+
+
 @pytest.mark.parametrize("bad_id", ["past_pool", "negative"])
 def test_prefill_block_outside_pool_gives_nan(gpu, bad_id):
     """A live block id outside the pool (past its end, or negative) turns that

@@ -38,10 +38,12 @@ def test_partials_match_oracle(gpu, dtype, hq, hkv):
             continue   # written straight to the output, no partials
         assert_close(o_part[s, :, :n[s]], ro[s, :, :n[s]], dtype, f"o_part seq {s}")
         # lse: scores come from fp32 dot products of 128 terms; 1e-4 absolute covers
-        # their rounding.  The bf16 matrix-core path also rounds each probability
-        # to bf16 (relative error <= 2^-8) and sums the rounded weights, which
-        # moves the log of the sum by at most ln(1 + 2^-8) < 3.9e-3.
-        lse_atol = 1e-4 if dtype == "f32" else 1e-4 + 3.9e-3
+        # their rounding.  The matrix-core path (bf16, head_dim 128, 4 or more query
+        # heads per kv head) also rounds each probability to bf16 (relative error
+        # <= 2^-8) and sums the rounded weights, which moves the log of the sum by
+        # at most ln(1 + 2^-8) < 3.9e-3; the vector-ALU path keeps fp32 weights.
+        matrix_cores = dtype == "bf16" and hq // hkv >= 4
+        lse_atol = 1e-4 + 3.9e-3 if matrix_cores else 1e-4
         err = np.abs(lse[s, :, :n[s]].astype(np.float64) - rl[s, :, :n[s]])
         assert (err <= lse_atol + 1e-5 * np.abs(rl[s, :, :n[s]])).all(), err.max()
     assert_close(as_f64(g.out), oracle_decode(w), dtype, "merged")

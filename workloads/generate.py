@@ -153,14 +153,15 @@ def fp8_codes(shape, seed_seq: np.random.SeedSequence, max_exp_field: int = 9) -
     return out
 
 
-def fp8_pools(w: "Workload", seed: int):
+def fp8_pools(w: "Workload", seed: int, max_exp_field: int = 9):
     """Host code pools shaped like w.k_host / w.v_host: random codes where w's
     pools hold data, the NaN code where they hold NaN (unused rows, slots a
-    scatter fills), so the same rows stay poisoned."""
+    scatter fills), so the same rows stay poisoned.  max_exp_field = 14 spans
+    every finite code (magnitudes up to 448)."""
     kids = np.random.SeedSequence(seed).spawn(2)
     out = []
     for src, kid in ((w.k_host, kids[0]), (w.v_host, kids[1])):
-        codes = fp8_codes(src.shape, kid)
+        codes = fp8_codes(src.shape, kid, max_exp_field)
         poison = np.isnan(src) if w.dtype == "f32" else (src == BF16_NAN)
         codes[poison] = FP8_NAN_CODE
         out.append(codes)
