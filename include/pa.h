@@ -66,7 +66,9 @@ typedef enum {
   PA_ERR_BUSY = -8,        /* block manager: the call needs data a pending move has not
                               delivered yet; take and run the moves first.  Nothing changed */
   PA_ERR_NO_MEMORY = -9,   /* block manager: host allocation failed */
-  PA_ERR_STATE = -10       /* block manager: an internal invariant does not hold */
+  PA_ERR_STATE = -10,      /* block manager: an internal invariant does not hold */
+  PA_ERR_SCRATCH = -11     /* pa_decode_no_alloc: the split-K partials would not fit the
+                              library's fixed buffer (pa_decode_no_alloc_scratch_bytes()) */
 } pa_status;
 
 /*
@@ -203,6 +205,33 @@ int pa_decode_splitk_reduce(void* out, const void* workspace, size_t workspace_b
                             const int32_t* context_lens, int num_seqs, int num_heads,
                             int head_dim, int max_context_len, int partition_size,
                             pa_dtype out_dtype, hipStream_t stream);
+
+/*
+ * pa_decode_no_alloc -- pa_decode followed by pa_decode_splitk_reduce in one
+ * call that allocates nothing and takes no workspace.  For callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.
+ *
+ * The split-K partials live in a fixed buffer of
+ * pa_decode_no_alloc_scratch_bytes() (64 MiB) that the library holds on every
+ * GPU it runs on until the process ends.  Arguments are pa_decode's without
+ * the workspace; out receives the merged result.  A call whose partials
+ * (pa_decode_workspace_bytes() of the same sizes) exceed the buffer returns
+ * PA_ERR_SCRATCH and launches nothing; otherwise every pa_decode status
+ * applies.  The first call on a device looks the buffer up on the current
+ * device, so `stream` must belong to the current device.  All calls on one GPU
+ * share the buffer: calls that overlap on one GPU (other streams, other host
+ * threads) race on it, calls on one stream are ordered.  Nothing in the buffer
+ * needs to start at zero.
+ */
+size_t pa_decode_no_alloc_scratch_bytes(void);
+int pa_decode_no_alloc(void* out, const void* query, const void* key_cache,
+                       const void* value_cache, const int32_t* block_tables,
+                       const int32_t* context_lens, const int32_t* shared_prefix_blocks,
+                       int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                       int block_size, int max_blocks_per_seq, int64_t num_blocks,
+                       int max_context_len, float scale, int partition_size, pa_dtype dtype,
+                       hipStream_t stream);
 
 /*
  * pa_prefill_chunk -- causal attention for a chunk of new tokens per sequence.

@@ -6,6 +6,7 @@ binding.
 """
 from . import lib
 from .lib import (pa_decode, pa_decode_splitk_reduce, pa_decode_workspace_bytes,
+                  pa_decode_no_alloc, pa_decode_no_alloc_scratch_bytes,
                   pa_prefill_chunk, pa_reshape_and_cache, pa_reshape_and_cache_fp8,
                   pa_decode_fp8, pa_prefill_chunk_fp8, pa_decode_shared_prefix,
                   pa_decode_fp8_shared_prefix, pa_prefill_workspace_bytes,
@@ -20,6 +21,7 @@ from .lib import (pa_decode, pa_decode_splitk_reduce, pa_decode_workspace_bytes,
                   SequenceError, ShapeError)
 
 __all__ = ["lib", "pa_decode", "pa_decode_splitk_reduce", "pa_decode_workspace_bytes",
+           "pa_decode_no_alloc", "pa_decode_no_alloc_scratch_bytes",
            "pa_prefill_chunk", "pa_reshape_and_cache", "pa_reshape_and_cache_fp8",
            "pa_decode_fp8", "pa_prefill_chunk_fp8", "pa_decode_shared_prefix",
            "pa_decode_fp8_shared_prefix", "pa_prefill_workspace_bytes",

@@ -20,7 +20,8 @@ ARCH = "gfx950"
 
 SOURCES = ["pa_api.cpp", "block_manager.cpp", "reshape_and_cache.hip", "copy_blocks.hip",
            "decode.hip", "decode_valu_bf16.hip", "decode_valu_f32.hip", "decode_valu_fp8.hip",
-           "decode_mfma.hip", "prefill.hip", "sampler.hip", "stream_read.hip"]
+           "decode_mfma.hip", "prefill.hip", "sampler.hip", "stream_read.hip",
+           "decode_no_alloc.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}",

@@ -37,15 +37,14 @@ bool workspace_ok(const void* ws, size_t bytes, size_t need) {
   return ws && bytes >= need && (reinterpret_cast<uintptr_t>(ws) & 15) == 0;
 }
 
-// Shared by pa_decode and pa_decode_fp8: checks, then the kernel choice.
-int decode_impl(void* out, const void* query, const void* key_cache, const void* value_cache,
-                const int32_t* block_tables, const int32_t* context_lens,
-                const int32_t* shared_prefix_blocks, const int32_t* prefix_group,
-                int max_group_size, int num_seqs, int num_heads,
-                int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
-                int64_t num_blocks, int max_context_len, float scale, int partition_size,
-                void* workspace, size_t workspace_bytes, pa_dtype dtype, bool fp8,
-                float k_scale, float v_scale, hipStream_t stream) {
+// The scalar and pointer checks of every decode entry point, workspace aside.
+int decode_check(const void* out, const void* query, const void* key_cache,
+                 const void* value_cache, const int32_t* block_tables,
+                 const int32_t* context_lens, const int32_t* shared_prefix_blocks,
+                 const int32_t* prefix_group, int max_group_size, int num_seqs, int num_heads,
+                 int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                 int64_t num_blocks, int max_context_len, int partition_size, pa_dtype dtype,
+                 bool fp8, float k_scale, float v_scale) {
   if (num_seqs < 0) return PA_ERR_SHAPE;
   if (prefix_group != nullptr) {
     // the grouped pass writes split-K partials and needs the shared counts
@@ -68,6 +67,26 @@ int decode_impl(void* out, const void* query, const void* key_cache, const void*
     return PA_ERR_UNSUPPORTED;
   const int nparts = max_partitions(max_context_len, partition_size);
   if (nparts > kMaxGridY || (int64_t)num_seqs * num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+// Shared by pa_decode and pa_decode_fp8: checks, then the kernel choice.
+int decode_impl(void* out, const void* query, const void* key_cache, const void* value_cache,
+                const int32_t* block_tables, const int32_t* context_lens,
+                const int32_t* shared_prefix_blocks, const int32_t* prefix_group,
+                int max_group_size, int num_seqs, int num_heads,
+                int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                int64_t num_blocks, int max_context_len, float scale, int partition_size,
+                void* workspace, size_t workspace_bytes, pa_dtype dtype, bool fp8,
+                float k_scale, float v_scale, hipStream_t stream) {
+  const int st = decode_check(out, query, key_cache, value_cache, block_tables, context_lens,
+                              shared_prefix_blocks, prefix_group, max_group_size, num_seqs,
+                              num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                              num_blocks, max_context_len, partition_size, dtype, fp8, k_scale,
+                              v_scale);
+  if (st != PA_OK) return st;
+  const int group = num_heads / num_kv_heads;
+  const int nparts = max_partitions(max_context_len, partition_size);
   if (partition_size > 0) {
     const size_t need = pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len,
                                                   partition_size);
@@ -110,6 +129,19 @@ int decode_impl(void* out, const void* query, const void* key_cache, const void*
 
 }  // namespace
 
+namespace pa {
+int check_decode_args(const void* out, const void* query, const void* key_cache,
+                      const void* value_cache, const int32_t* block_tables,
+                      const int32_t* context_lens, int num_seqs, int num_heads, int num_kv_heads,
+                      int head_dim, int block_size, int max_blocks_per_seq, int64_t num_blocks,
+                      int max_context_len, int partition_size, pa_dtype dtype) {
+  return decode_check(out, query, key_cache, value_cache, block_tables, context_lens, nullptr,
+                      nullptr, 0, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                      max_blocks_per_seq, num_blocks, max_context_len, partition_size, dtype,
+                      false, 1.f, 1.f);
+}
+}  // namespace pa
+
 extern "C" {
 
 const char* pa_status_string(int status) {
@@ -125,6 +157,9 @@ const char* pa_status_string(int status) {
     case PA_ERR_BUSY: return "pending block moves must be taken and run first";
     case PA_ERR_NO_MEMORY: return "host allocation failed";
     case PA_ERR_STATE: return "block manager invariant violated";
+    case PA_ERR_SCRATCH:
+      return "split-K partials larger than the fixed buffer of pa_decode_no_alloc "
+             "(pa_decode_no_alloc_scratch_bytes())";
     default: return "unknown status";
   }
 }

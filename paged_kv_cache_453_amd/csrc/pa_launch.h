@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pa.h"
+
 namespace pa {
 
 struct ScatterArgs {
@@ -106,6 +108,12 @@ constexpr int kSwapPairsPerLaunch = 256;
 
 hipError_t launch_reshape_and_cache(const ScatterArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t stream);
+// pa_decode's scalar and pointer checks (no HIP call): PA_OK or the status pa_decode returns.
+int check_decode_args(const void* out, const void* query, const void* key_cache,
+                      const void* value_cache, const int32_t* block_tables,
+                      const int32_t* context_lens, int num_seqs, int num_heads, int num_kv_heads,
+                      int head_dim, int block_size, int max_blocks_per_seq, int64_t num_blocks,
+                      int max_context_len, int partition_size, pa_dtype dtype);
 // FP8 caches: which (group, head_dim, query type) combinations have a kernel.
 bool decode_fp8_supported(int group, int head_dim, bool bf16_query);
 hipError_t launch_decode_fp8(const DecodeArgs& a, int head_dim, bool bf16_query,

@@ -73,6 +73,11 @@ def load() -> ctypes.CDLL:
     lib.pa_decode.restype = i32
     lib.pa_decode_splitk_reduce.argtypes = [vp, vp, sz, vp, i32, i32, i32, i32, i32, i32, vp]
     lib.pa_decode_splitk_reduce.restype = i32
+    lib.pa_decode_no_alloc_scratch_bytes.argtypes = []
+    lib.pa_decode_no_alloc_scratch_bytes.restype = sz
+    lib.pa_decode_no_alloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                       i64, i32, f32, i32, i32, vp]
+    lib.pa_decode_no_alloc.restype = i32
     lib.pa_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                      i32, i64, i32, f32, i32, vp]
     lib.pa_prefill_chunk.restype = i32
@@ -144,7 +149,7 @@ def load() -> ctypes.CDLL:
 
 
 EXPORTED = ("pa_reshape_and_cache", "pa_decode_workspace_bytes", "pa_decode",
-            "pa_decode_splitk_reduce", "pa_prefill_chunk", "pa_reshape_and_cache_fp8",
+            "pa_decode_splitk_reduce", "pa_decode_no_alloc", "pa_decode_no_alloc_scratch_bytes", "pa_prefill_chunk", "pa_reshape_and_cache_fp8",
             "pa_decode_fp8", "pa_prefill_chunk_fp8", "pa_decode_shared_prefix",
             "pa_decode_fp8_shared_prefix", "pa_prefill_workspace_bytes", "pa_prefill_chunk_split",
             "pa_prefill_chunk_fp8_split", "pa_sample", "pa_copy_blocks",
@@ -255,6 +260,27 @@ def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, sc
         _ptr(context_lens), _ptr(shared_prefix_blocks), s, hq, hkv, d, bs, block_tables.shape[1],
         nb, int(max_context_len),
         float(scale), int(partition_size), ws_ptr, ws_bytes, _dtype_code(query), _stream(stream)))
+
+
+def pa_decode_no_alloc_scratch_bytes() -> int:
+    return int(load().pa_decode_no_alloc_scratch_bytes())
+
+
+def pa_decode_no_alloc(out, query, key_cache, value_cache, block_tables, context_lens,
+                       scale: float, max_context_len: int, partition_size: int = 0, stream=None,
+                       shared_prefix_blocks=None) -> None:
+    """pa_decode plus the split-K merge in one call, with the partials in the library's fixed
+    device buffer (no workspace, nothing allocated); raises for PA_ERR_SCRATCH when they do not
+    fit pa_decode_no_alloc_scratch_bytes()."""
+    lib = load()
+    s, hq, d, nb, hkv, bs, _, _ = _decode_marshal(
+        out, query, key_cache, value_cache, block_tables, context_lens, None,
+        shared_prefix_blocks)
+    _check("pa_decode_no_alloc", lib.pa_decode_no_alloc(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), _ptr(shared_prefix_blocks), s, hq, hkv, d, bs, block_tables.shape[1],
+        nb, int(max_context_len), float(scale), int(partition_size), _dtype_code(query),
+        _stream(stream)))
 
 
 def _decode_marshal(out, query, key_cache, value_cache, block_tables, context_lens,

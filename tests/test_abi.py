@@ -343,3 +343,25 @@ def test_prefill_split_validation(lib, fp8):
     assert prefill_split(lib, fp8, ws=P + 8, wsb=need) == PA_ERR_WORKSPACE
     assert prefill_split(lib, fp8, out=None, ws=P, wsb=need) == PA_ERR_NULL
     assert prefill_split(lib, fp8, S=0, out=None, query=None) == PA_OK
+
+
+def test_no_alloc_decode_validation(lib):
+    """pa_decode_no_alloc makes pa_decode's checks first, then refuses partials
+    larger than its fixed buffer -- all before any HIP call."""
+    assert lib.pa_decode_no_alloc_scratch_bytes() == 64 << 20
+
+    def call(**kw):
+        a = dict(out=P, q=P, k=P, v=P, bt=P, cl=P, sh=None, S=4, hq=8, hkv=8, d=128, bs=16, mb=4,
+                 nb=64, maxc=64, scale=0.1, ps=16, dtype=BF16, stream=None)
+        a.update(kw)
+        return lib.pa_decode_no_alloc(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"],
+                                      a["sh"], a["S"], a["hq"], a["hkv"], a["d"], a["bs"], a["mb"],
+                                      a["nb"], a["maxc"], a["scale"], a["ps"], a["dtype"],
+                                      a["stream"])
+    assert call(d=96) == PA_ERR_UNSUPPORTED
+    assert call(out=None) == PA_ERR_NULL
+    assert call(ps=24) == PA_ERR_SHAPE
+    assert call(hq=6, hkv=4) == PA_ERR_SHAPE
+    # 4 x 8 x 32768 partitions of (128 + 1) fp32: 541 MB of partials > 64 MiB
+    assert call(maxc=1 << 19) == -11
+    assert b"fixed buffer" in lib.pa_status_string(-11)
