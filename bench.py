@@ -130,8 +130,9 @@ def measured_traffic(kind: str):
 FP8_K_SCALE, FP8_V_SCALE = 0.07, 0.11
 
 
-def cpu_baseline(w, budget_s: float = 10.0, fp8_pools=None):
-    """The fp64 oracle on a bounded sample of the same workload, one host thread.
+def cpu_baseline(w, budget_s: float = 10.0, fp8_pools=None, threads: int = 1):
+    """The fp64 oracle on a bounded sample of the same workload, with its BLAS
+    limited to `threads` host threads.
 
     Decode: the first sequences in order (scatter included where the workload
     has one) until budget_s of CPU time.  Prefill (mixed workload): the first
@@ -149,7 +150,7 @@ def cpu_baseline(w, budget_s: float = 10.0, fp8_pools=None):
     k, v = fp8_pools if fp8 else (w.k_host, w.v_host)
     t_total = 0.0
     notes = []
-    with threadpool_limits(1):
+    with threadpool_limits(threads):
         if w.slot_mapping is not None:
             t0 = time.perf_counter()
             if fp8:
@@ -192,9 +193,88 @@ def cpu_baseline(w, budget_s: float = 10.0, fp8_pools=None):
                                     1 if fp8 else w.elem_bytes)
     notes.append(f"decode of the first {done} of {g.num_seqs} sequences "
                  f"({int(g.context_lens[:done].sum())} tokens, {t_dec:.1f} s)")
-    return {"value": round(kv / t_dec / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "fp64 numpy oracle on 1 host thread: " + "; ".join(notes) +
-                      "; value = decode KV bytes / decode time"}
+    return {"value": round(kv / t_dec / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle, BLAS limited to {threads} host thread(s): " +
+                      "; ".join(notes) + "; value = decode KV bytes / decode time"}
+
+
+def host_description():
+    """The host the CPU baseline runs on: cores this process may use (its
+    affinity mask), capped by OMP_NUM_THREADS where the box sets its CPU share
+    there; the CPU model; the BLAS numpy calls."""
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count() or 1
+    threads = affinity
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        threads = min(threads, int(omp))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        import numpy  # noqa: F401  (loads its BLAS so threadpoolctl can see it)
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in libs)
+    except Exception:  # pragma: no cover
+        pass
+    return {"affinity_cores": affinity, "threads": threads, "cpu_model": model, "blas": blas}
+
+
+def cpu_baseline_report(w, fp8_pools=None):
+    """The oracle baseline on every core this process may use (the reported
+    value), and again on one thread for reference."""
+    host = host_description()
+    allc = cpu_baseline(w, budget_s=10.0, fp8_pools=fp8_pools, threads=host["threads"])
+    one = cpu_baseline(w, budget_s=6.0, fp8_pools=fp8_pools, threads=1)
+    allc.update({"affinity_cores": host["affinity_cores"], "cpu_model": host["cpu_model"],
+                 "blas": host["blas"],
+                 "one_thread": {"value": one["value"], "unit": one["unit"],
+                                "sample": one["sample"]}})
+    return allc
+
+
+def other_configs(args, torch, dev, lib):
+    """The other decode configurations, each timed like the headline step:
+    the Llama-2-7B-shaped batch, the GQA long-context batch (512-token split-K
+    partitions as configured) and the mixed prefill + decode step."""
+    out = {}
+    for name, ps in (("llama7b", 2048), ("gqa", 512), ("mixed", 2048)):
+        r = bench_attention(args, torch, dev, lib, name, partition_size=ps, with_cpu=False)
+        torch.cuda.empty_cache()
+        rf = r["roofline"]
+        entry = {"workload": r["config"]["workload"], "num_seqs": r["config"]["num_seqs"],
+                 "partition_size": ps, "ms_per_step": r["ms_per_step"],
+                 "ms_per_step_p10_p50_p90": r["ms_per_step_p10_p50_p90"],
+                 "kv_gbs": r["value"], "pct_hbm_peak": r["pct_hbm_peak"],
+                 "tokens_per_s": r["tokens_per_s"], "kernel_us": r["kernel_us"],
+                 "kv_bytes_per_step": r["kv_bytes_per_step"],
+                 "decode_roofline": {"achieved": rf["achieved"], "frac": rf["frac"],
+                                     "unit": rf["unit"], "kernel": rf["kernel"],
+                                     "traffic": rf["traffic"]}}
+        if "roofline_prefill" in r:
+            pf = r["roofline_prefill"]
+            entry["value_note"] = r["value_note"]
+            entry["kv_gbs_logical"] = r["kv_gbs_logical"]
+            entry["kv_bytes_unique_per_step"] = r["kv_bytes_unique_per_step"]
+            entry["decode_roofline"]["logical_gbs"] = rf.get("logical_gbs")
+            entry["prefill_roofline"] = {"achieved": pf["achieved"], "frac": pf["frac"],
+                                         "unit": pf["unit"], "kernel": pf["kernel"]}
+            entry["overlapped_two_streams"] = r["overlapped_two_streams"]
+        out[name] = entry
+        log(f"bench: {name}: {json.dumps(entry)}")
+    return out
 
 
 def _counter_rows(path: str, kernel_prefix: str):
@@ -675,7 +755,8 @@ def bench_prefill_long(args, torch, dev, lib, timer) -> int:
 
 def prefix_cpu_baseline(d: int, hq: int, own: int, total: int, n: int = 32):
     """The fp64 prefill oracle on one prompt's chunk (own query tokens over a
-    total-token context), one host thread, scaled to the 32-prompt batch."""
+    total-token context), BLAS on every core the process may use, scaled to the
+    32-prompt batch."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -687,14 +768,17 @@ def prefix_cpu_baseline(d: int, hq: int, own: int, total: int, n: int = 32):
     k = f32_to_bf16_bits(rng.standard_normal((nblk, hq, 16, d)).astype(np.float32))
     v = f32_to_bf16_bits(rng.standard_normal((nblk, hq, 16, d)).astype(np.float32))
     q = f32_to_bf16_bits(rng.standard_normal((own, hq, d)).astype(np.float32))
-    with threadpool_limits(1):
+    host = host_description()
+    with threadpool_limits(host["threads"]):
         t0 = time.perf_counter()
         oracle.prefill(q, k, v, np.arange(nblk)[None, :], np.array([0, own], dtype=np.int32),
                        np.array([total], dtype=np.int32), np.float32(1 / np.sqrt(d)), "bf16")
         t = time.perf_counter() - t0
-    return {"value": round(t * n * 1e6, 1), "unit": "us", "cores": 1, "kind": "oracle",
-            "sample": f"fp64 numpy prefill oracle, 1 thread: one prompt's {own}-token chunk over "
-                      f"{total} tokens of context, {hq} heads ({t:.2f} s), times {n} prompts"}
+    return {"value": round(t * n * 1e6, 1), "unit": "us", "cores": host["threads"],
+            "kind": "oracle", "cpu_model": host["cpu_model"], "blas": host["blas"],
+            "sample": f"fp64 numpy prefill oracle, BLAS on {host['threads']} thread(s): one "
+                      f"prompt's {own}-token chunk over {total} tokens of context, {hq} heads "
+                      f"({t:.2f} s), times {n} prompts"}
 
 
 def bench_sampler(args, torch, dev, lib, timer) -> int:
@@ -731,7 +815,8 @@ def bench_sampler(args, torch, dev, lib, timer) -> int:
     cpu = None
     if not args.no_cpu_baseline:
         import oracle.sampler as osamp
-        with threadpool_limits(1):
+        host = host_description()
+        with threadpool_limits(host["threads"]):
             t0 = time.perf_counter()
             rows = 0
             while rows < 4 * s * SAMPLER_BUFFERS and time.perf_counter() - t0 < 10.0:
@@ -740,9 +825,10 @@ def bench_sampler(args, torch, dev, lib, timer) -> int:
                 rows += 1
             el = time.perf_counter() - t0
         cpu = {"value": round(rows / el, 1), "unit": "rows/s", "cores": 1, "kind": "oracle",
+               "cpu_model": host["cpu_model"], "blas": host["blas"],
                "sample": f"reference sampler (numpy float64, sorts the row) on {rows} rows "
-                         f"taken in turn from the {SAMPLER_BUFFERS} logits batches, {el:.2f} s, "
-                         f"one thread"}
+                         f"taken in turn from the {SAMPLER_BUFFERS} logits batches, {el:.2f} s; "
+                         f"it runs row by row in one thread (BLAS allowed {host['threads']})"}
     result = {
         "metric": SAMPLER_METRIC, "value": round(s / (ms * 1e-3), 1), "unit": "rows/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -772,6 +858,9 @@ def main(argv=None):
                     help="split-K partition length in tokens (default: 2048 for the Llama "
                          "shapes, 512 for gqa as its configuration states, 2048 for mixed)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="default workload only: skip the Llama-2-7B, GQA and mixed "
+                         "sub-results the default line carries")
     ap.add_argument("--prefill-split", type=int, default=None,
                     help="keys per run of the split prefill (pa_prefill_chunk_split): mixed "
                          "workloads default to 0 = pa_prefill_chunk, one workgroup per query "
@@ -822,12 +911,36 @@ def main(argv=None):
         return bench_sampler(args, torch, dev, lib, StepTimer(torch))
     if args.workload == "stream_read":
         return bench_stream_read(args, torch, dev, lib, StepTimer(torch))
-    fp8 = args.workload.endswith("_fp8")
-    base = args.workload[:-len("_fp8")] if fp8 else args.workload
+    result = bench_attention(args, torch, dev, lib, args.workload)
+    if result is None:
+        return 0
+    if args.workload == "llama13b" and not args.no_other_configs:
+        # the other decode configurations of the hot path, each in its own
+        # allocation after the headline one is freed, timed the same way
+        torch.cuda.empty_cache()
+        result["other_configs"] = other_configs(args, torch, dev, lib)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def bench_attention(args, torch, dev, lib, name: str, partition_size=None, steps=None,
+                    with_cpu: bool = True):
+    """One attention workload (decode, scatter, prefill as the workload has them):
+    returns the result dict of its JSON line (None for --decode-only, which
+    prints its own short line)."""
+    import numpy as np
+
+    from workloads import accounting
+    from workloads.device import to_device
+
+    ps = args.partition_size if partition_size is None else partition_size
+    steps = args.steps if steps is None else steps
+    fp8 = name.endswith("_fp8")
+    base = name[:-len("_fp8")] if fp8 else name
     if ps is None:
         ps = 512 if base == "gqa" else 2048
 
-    log(f"bench: generating the {args.workload} workload")
+    log(f"bench: generating the {name} workload")
     t0 = time.time()
     w, cfg = build_workload(base, ps)
     g = w.decode
@@ -952,9 +1065,9 @@ def main(argv=None):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log(f"bench: timing {args.steps} steps")
-    ms_per_step = timer.per_step(step, args.steps, [stream])
-    kernel_ms = timer.per_launch(launches, args.steps, stream)
+    log(f"bench: timing {steps} steps")
+    ms_per_step = timer.per_step(step, steps, [stream])
+    kernel_ms = timer.per_launch(launches, steps, stream)
     log("bench: step %.1f us (%s)" % (ms_per_step * 1e3, ", ".join(
         f"{k} {v * 1e3:.1f}" for k, v in kernel_ms.items())))
 
@@ -964,20 +1077,20 @@ def main(argv=None):
         unique = accounting.unique_kv_bytes(g.block_tables, g.context_lens, w.num_kv_heads,
                                             w.head_dim, 1 if fp8 else w.elem_bytes)
         print(json.dumps({
-            "mode": "decode_only", "workload": args.workload, "partition_size": ps,
+            "mode": "decode_only", "workload": name, "partition_size": ps,
             "entry_point": ("pa_decode_shared_prefix" if grouped else "pa_decode"),
             "decode_us": round(kernel_ms["decode"] * 1e3, 2),
             "kv_bytes_logical": int(kv), "kv_bytes_unique": int(unique)}), flush=True)
-        return 0
+        return None
 
     if pf_split:
         # the same prefill without splitting, for comparison
-        pf_ms = timer.per_launch([("prefill_unsplit", plain_prefill)], args.steps, stream)
+        pf_ms = timer.per_launch([("prefill_unsplit", plain_prefill)], steps, stream)
         log("bench: prefill without splitting %.1f us" % (pf_ms["prefill_unsplit"] * 1e3))
 
     if grouped:
         # the same decode without the grouped pass, for comparison
-        extra_ms = timer.per_launch([("decode_ungrouped", plain_decode)], args.steps, stream)
+        extra_ms = timer.per_launch([("decode_ungrouped", plain_decode)], steps, stream)
         log("bench: decode without prefix groups %.1f us" % (extra_ms["decode_ungrouped"] * 1e3))
 
     kv_elem = 1 if fp8 else w.elem_bytes
@@ -999,7 +1112,7 @@ def main(argv=None):
                       "(one pa_decode_shared_prefix call)")
     roofline = {"bound": "hbm", "achieved": round(decode_gbs, 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(decode_gbs / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic("decode") if args.workload == "llama13b" else None,
+                "traffic": measured_traffic("decode") if name == "llama13b" else None,
                 "kernel": dec_kernel, "algorithmic_bytes_per_launch": int(kv)}
 
     if w.prefill is not None:
@@ -1012,7 +1125,7 @@ def main(argv=None):
         pf_tflops = flops / (kernel_ms["prefill"] * 1e-3) / 1e12
         unique_gbs = unique / (kernel_ms["decode"] * 1e-3) / 1e9
         # the decode of shared prefixes must read each physical row once at least
-        if args.workload == "mixed":
+        if name == "mixed":
             roofline["traffic"] = measured_traffic("mixed_decode" if grouped
                                                    else "mixed_decode_plain")
         roofline.update({"achieved": round(unique_gbs, 2),
@@ -1062,7 +1175,7 @@ def main(argv=None):
 
         for _ in range(args.warmup):
             step_overlap()
-        ms_overlap = timer.per_step(step_overlap, args.steps, [stream, side])
+        ms_overlap = timer.per_step(step_overlap, steps, [stream, side])
         extra["overlapped_two_streams"] = {
             "ms_per_step": round(ms_overlap, 5),
             "kv_gbs_logical": round(kv / (ms_overlap * 1e-3) / 1e9, 2),
@@ -1070,9 +1183,9 @@ def main(argv=None):
         log(f"bench: overlapped step {ms_overlap * 1e3:.1f} us")
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if with_cpu and not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a sample")
-        cpu = cpu_baseline(w, fp8_pools=codes)
+        cpu = cpu_baseline_report(w, fp8_pools=codes)
 
     config = {"workload": cfg.pop("workload"), "num_seqs": g.num_seqs,
               "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
@@ -1085,7 +1198,7 @@ def main(argv=None):
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "ms_per_step_p10_p50_p90": timer.spread,
@@ -1109,13 +1222,13 @@ def main(argv=None):
         "cpu_baseline": cpu,
     }
     result.update(extra)
-    if args.workload == "llama13b":
+    if name == "llama13b":
         # the part's achievable read rate, beside the 8 TB/s peak the roofline uses
         read = stream_read_gbs(torch, dev, lib, timer)
         result["achievable_read_gbs"] = round(read, 2)
         result["decode_pct_of_achievable_read"] = round(100.0 * decode_gbs / read, 2)
-    print(json.dumps(result), flush=True)
-    return 0
+    return result
+
 
 
 if __name__ == "__main__":
