@@ -96,6 +96,14 @@ int pa_reshape_and_cache(const void* key, const void* value, void* key_cache, vo
 /*
  * pa_decode_workspace_bytes -- workspace pa_decode needs for split-K.
  *
+ * Split-K is not on the pages: it is how this library spreads one long
+ * context over many workgroups, for the long-context grouped-query workload
+ * it is measured on (32 sequences of 8k-32k tokens, 32 query over 8 kv heads,
+ * context partitions of 512 tokens merged by log-sum-exp).  Each partition's
+ * result is exact softmax attention over its own keys, and the merge below
+ * recovers attention over all of them ("vLLM 基本原理", section "Transformer
+ * 和 Attention": the output is the softmax-weighted mean of V).
+ *
  * Zero when partition_size == 0 (single pass).  Otherwise room for
  *   o_part   fp32 [num_seqs, num_heads, P, head_dim]
  *   lse_part fp32 [num_seqs, num_heads, P]
@@ -196,7 +204,11 @@ int pa_decode_shared_prefix(void* out, const void* query, const void* key_cache,
 /*
  * pa_decode_splitk_reduce -- merge the partition results pa_decode left in the
  * workspace: with M = max_p lse_p and w_p = exp(lse_p - M),
- * out = sum_p w_p o_p / sum_p w_p.  Sequences with at most one partition are
+ * out = sum_p w_p o_p / sum_p w_p.  This is exact in real arithmetic: w_p is
+ * partition p's share of the softmax denominator (up to the common factor
+ * exp(M)), so the weighted mean of the partition means is the mean over all
+ * keys.  The split-K merge of the long-context workload (see
+ * pa_decode_workspace_bytes); the pages themselves have no split-K.  Sequences with at most one partition are
  * left untouched (pa_decode wrote them); when max_context_len <= partition_size
  * nothing is launched.  Arguments must match the pa_decode call that filled the
  * workspace (16-byte aligned).
