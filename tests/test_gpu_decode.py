@@ -66,8 +66,8 @@ def test_llama13b_bf16_decode_full(gpu, ps):
 
 @pytest.mark.slow
 def test_llama13b_fp32_twin_tight(gpu):
-    say("decode config2 fp32 twin (96 sequences)")
-    w = config2(dtype="f32", num_seqs=96)
+    say("decode config2 fp32 twin (all 256 sequences)")
+    w = config2(dtype="f32")
     dw = run(w)
     assert_close(as_f64(dw.decode.out), oracle_decode(w), "f32", "config2-f32")
 
