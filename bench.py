@@ -7,7 +7,8 @@ lognormal context lengths with median 1024 clipped to [16, 4096], 65536-block
 shuffled pool) with split-K partitions and their merge.
 
 --workload selects the other shapes the hot path is measured on:
-  llama7b   decode of 64 sequences, 32 = 32 heads, lengths U[128, 2048]
+  llama7b   decode of 64 sequences, 32 = 32 heads, lengths U[128, 2048], 512-token
+            split-K partitions + merge
   gqa       decode of 32 sequences, 32 query heads over 8 kv heads, lengths
             U[8192, 32768], 512-token split-K partitions + merge
   mixed     chunked prefill of 4 x 512-token chunks over paged prefixes, then
@@ -92,6 +93,21 @@ COUNTED = {
         "bench": "python3 bench.py --workload mixed --decode-only --no-prefix-groups --steps 3 "
                  "--warmup 1",
         "dir": "pmc_mixed_plain", "out": "mixed"},
+    # the Llama-2-7B-shaped batch (the headline kernel, other lengths and partitions)
+    "decode_7b": {
+        "json": os.path.join(ROOT, "profiles", "decode_llama7b_counters.json"),
+        "kernel": "void pa::decode_valu_kernel<unsigned short, unsigned short, 128, 1, false, false>",
+        "sources": _DECODE_SOURCES,
+        "bench": "python3 bench.py --workload llama7b --decode-only --steps 3 --warmup 1",
+        "dir": "pmc_7b", "out": "l7b"},
+    # the GQA long-context batch on the matrix-core decode
+    "decode_gqa": {
+        "json": os.path.join(ROOT, "profiles", "decode_gqa_counters.json"),
+        "kernel": "void pa::decode_gqa_mfma_kernel<unsigned short, false, false>",
+        "sources": [os.path.join(_CSRC, f) for f in
+                    ("decode_mfma.hip", "decode_groups.h", "pa_device.h")],
+        "bench": "python3 bench.py --workload gqa --decode-only --steps 3 --warmup 1",
+        "dir": "pmc_gqa", "out": "gqa"},
     "copy": {
         "json": os.path.join(ROOT, "profiles", "copy_blocks_13b_counters.json"),
         "kernel": "void pa::move_blocks_kernel<unsigned int __vector(4), pa::DeviceMapping>",
@@ -250,7 +266,7 @@ def other_configs(args, torch, dev, lib):
     the Llama-2-7B-shaped batch, the GQA long-context batch (512-token split-K
     partitions as configured) and the mixed prefill + decode step."""
     out = {}
-    for name, ps in (("llama7b", 2048), ("gqa", 512), ("mixed", 2048)):
+    for name, ps in (("llama7b", 512), ("gqa", 512), ("mixed", 2048)):
         r = bench_attention(args, torch, dev, lib, name, partition_size=ps, with_cpu=False)
         torch.cuda.empty_cache()
         rf = r["roofline"]
@@ -855,8 +871,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", choices=WORKLOADS, default="llama13b")
     ap.add_argument("--partition-size", type=int, default=None,
-                    help="split-K partition length in tokens (default: 2048 for the Llama "
-                         "shapes, 512 for gqa as its configuration states, 2048 for mixed)")
+                    help="split-K partition length in tokens (default: 2048 for llama13b "
+                         "and mixed, 512 for gqa as its configuration states and for llama7b, "
+                         "whose lengths of 128-2048 leave a long tail at 2048)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="default workload only: skip the Llama-2-7B, GQA and mixed "
@@ -938,7 +955,7 @@ def bench_attention(args, torch, dev, lib, name: str, partition_size=None, steps
     fp8 = name.endswith("_fp8")
     base = name[:-len("_fp8")] if fp8 else name
     if ps is None:
-        ps = 512 if base == "gqa" else 2048
+        ps = 512 if base in ("gqa", "llama7b") else 2048
 
     log(f"bench: generating the {name} workload")
     t0 = time.time()
@@ -1112,7 +1129,9 @@ def bench_attention(args, torch, dev, lib, name: str, partition_size=None, steps
                       "(one pa_decode_shared_prefix call)")
     roofline = {"bound": "hbm", "achieved": round(decode_gbs, 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(decode_gbs / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic("decode") if name == "llama13b" else None,
+                "traffic": {"llama13b": measured_traffic("decode"),
+                            "llama7b": measured_traffic("decode_7b"),
+                            "gqa": measured_traffic("decode_gqa")}.get(name),
                 "kernel": dec_kernel, "algorithmic_bytes_per_launch": int(kv)}
 
     if w.prefill is not None:
