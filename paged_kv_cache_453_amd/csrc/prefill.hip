@@ -502,6 +502,14 @@ __device__ __forceinline__ void load_lds_1k(__amdgpu_buffer_rsrc_t rs, uint8_t* 
                                            voff, 0, 0, 0);
 }
 
+// max(a, b, c) in one instruction, with fmaxf's rule for NaN operands (they
+// are ignored).  Written out because for fmaxf of matrix-core results the
+// compiler first quiets each operand with an extra max of it with itself.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float d;
+  __asm__("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
 // Orders this wave's memory accesses around a workgroup barrier without the
 // waits a memory fence implies: the loads into the next tile buffers must stay
 // in flight across it.
@@ -621,16 +629,29 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_dma_kernel(DecodeArgs a) {
   typedef __attribute__((address_space(4))) const int32_t const_i32;
   const_i32* ctable = (const_i32*)table;
   const auto block_id = [&](int kt) { return ctable[min(kt * 4 + w, a.max_blocks_per_seq - 1)]; };
-  const auto stage = [&](uint8_t* dst_base, const uint8_t* pool, const int (&off)[NLD], int kt,
-                         int id) {
+  // This wave's slab of tile kt (block id `id`): its byte offset in a pool and
+  // its live bytes (0: past the keys, or an id outside the pool, which
+  // poisons the workgroup's rows).  The K and V slabs of a tile share it.
+  struct Slab {
+    int64_t off;
+    int bytes;
+  };
+  const uint32_t pool_ids = (uint32_t)min<int64_t>(a.num_blocks, 0x80000000ll);
+  const int64_t id_stride = (int64_t)a.num_kv_heads * SLAB;
+  const int64_t head_off = (int64_t)kvh * SLAB;
+  int bad_id = 0;        // this wave staged a block id outside the pool
+  const auto describe = [&](int kt, int id) {
     const int gb = kt * 4 + w;
     const int rows = gb < nblk ? min(kBlock, kend - gb * kBlock) : 0;
-    const bool in_pool = id >= 0 && (int64_t)id < a.num_blocks;
-    if (rows > 0 && !in_pool) sh_bad = 1;
+    const bool in_pool = (uint32_t)id < pool_ids;
+    bad_id |= (int)(rows > 0) & (int)!in_pool;
     const bool live = rows > 0 && in_pool;
-    const uint8_t* base = pool + (live ? ((int64_t)id * a.num_kv_heads + kvh) * SLAB : 0);
-    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0,
-                                                      live ? rows * RB : 0, kBufferWord3);
+    return Slab{live ? id * id_stride + head_off : 0, live ? rows * RB : 0};
+  };
+  const auto stage = [&](uint8_t* dst_base, const uint8_t* pool, const int (&off)[NLD],
+                         const Slab& sl) {
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pool + sl.off), 0,
+                                                      sl.bytes, kBufferWord3);
 #pragma unroll
     for (int j = 0; j < NLD; ++j) load_lds_1k(rs, dst_base + w * SLAB + j * 1024, off[j]);
   };
@@ -670,16 +691,24 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_dma_kernel(DecodeArgs a) {
       }
     }
   };
-  // max of a tile's scores per row block, in base 2 (masked keys are -inf)
+  // max of a tile's scores per row block, in base 2 (masked keys are -inf):
+  // a tree of 8 three-way maxes over the lane's 16 scores, depth 3
   const auto row_max = [&](const f32x4 (&sc)[QB][4], float (&lm)[QB]) {
+    float m1[QB][5];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float x = fmaxf(fmaxf(sc[qb][0][0], sc[qb][0][1]), fmaxf(sc[qb][0][2], sc[qb][0][3]));
+      const f32x4* v = sc[qb];
+      m1[qb][0] = max3f(v[0][0], v[0][1], v[0][2]);
+      m1[qb][1] = max3f(v[0][3], v[1][0], v[1][1]);
+      m1[qb][2] = max3f(v[1][2], v[1][3], v[2][0]);
+      m1[qb][3] = max3f(v[2][1], v[2][2], v[2][3]);
+      m1[qb][4] = max3f(v[3][0], v[3][1], v[3][2]);
+    }
 #pragma unroll
-      for (int nt = 1; nt < 4; ++nt)
-        x = fmaxf(x, fmaxf(fmaxf(sc[qb][nt][0], sc[qb][nt][1]),
-                           fmaxf(sc[qb][nt][2], sc[qb][nt][3])));
-      lm[qb] = x * sl2;
+    for (int qb = 0; qb < QB; ++qb) {
+      const float a = max3f(m1[qb][0], m1[qb][1], m1[qb][2]);
+      const float b = max3f(m1[qb][3], m1[qb][4], sc[qb][3][3]);
+      lm[qb] = max3f(a, b, b) * sl2;
     }
   };
   // causal mask of tile kt: keys past a row's position get -inf
@@ -762,12 +791,13 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_dma_kernel(DecodeArgs a) {
   f32x4 sa[QB][4], sb[QB][4];
   float lm[QB] = {};
   int id_k = block_id(in_range(kt0 + 2));   // K of kt+2, staged in iteration kt
-  int id_v = block_id(in_range(kt0 + 1));   // V of kt+1
+  Slab slab_v;                              // V of kt+1: the slab its K was staged from
   {
-    const int id0 = block_id(kt0);
-    stage(kbuf0, kpool, koff, kt0, id0);
-    stage(vbuf0, vpool, voff, kt0, id0);
-    stage(kbuf1, kpool, koff, in_range(kt0 + 1), id_v);
+    const Slab s0 = describe(kt0, block_id(kt0));
+    slab_v = describe(in_range(kt0 + 1), block_id(in_range(kt0 + 1)));
+    stage(kbuf0, kpool, koff, s0);
+    stage(vbuf0, vpool, voff, s0);
+    stage(kbuf1, kpool, koff, slab_v);
     sync_tiles();
     if (kt0 < wave_end) {
       scores(kbuf0, sa);
@@ -785,10 +815,11 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_dma_kernel(DecodeArgs a) {
     uint8_t* const k_next = P ? kbuf1 : kbuf0;   // K of kt+2
     uint8_t* const v_now = P ? vbuf1 : vbuf0;    // V of kt
     uint8_t* const v_next = P ? vbuf0 : vbuf1;   // V of kt+1
-    stage(k_next, kpool, koff, in_range(kt + 2), id_k);
-    stage(v_next, vpool, voff, in_range(kt + 1), id_v);
+    const Slab slab_k = describe(in_range(kt + 2), id_k);
+    stage(k_next, kpool, koff, slab_k);
+    stage(v_next, vpool, voff, slab_v);
+    slab_v = slab_k;
     id_k = block_id(in_range(kt + 3));
-    id_v = block_id(in_range(kt + 2));
     if (kt < wave_end) {
       // cur holds tile kt's scores, masked where needed, and lm their max
       rescale(lm);
@@ -821,6 +852,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_dma_kernel(DecodeArgs a) {
     iteration(std::integral_constant<int, 1>(), kt + 1, sb, sa);
   }
 
+  // a wave that staged an id outside the pool poisons the workgroup's rows
+  if (bad_id) sh_bad = 1;
+  sync_tiles();
   const bool poisoned = sh_bad != 0;
   if (nsplit > 1) {
 #pragma unroll
