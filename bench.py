@@ -15,7 +15,8 @@ shuffled pool) with split-K partitions and their merge.
             decode of 192 sequences sharing 2048-token prefixes in groups of 3
             (also timed with prefill and decode on two streams)
   mixed_gqa, mixed_gqa_fp8
-            the mixed step with 32 query heads over 8 kv heads (Llama-3-8B shape)
+            the mixed step with 32 query heads over 8 kv heads (Llama-3-8B shape);
+            mixed_gqa splits the prefill into 2048-key runs
   llama13b_fp8, gqa_fp8, mixed_fp8
             the llama13b, gqa and mixed steps over an FP8 (OCP E4M3) cache with
             one scale per pool: quantising scatter (llama13b), chunked prefill
@@ -879,9 +880,10 @@ def main(argv=None):
                     help="default workload only: skip the Llama-2-7B, GQA and mixed "
                          "sub-results the default line carries")
     ap.add_argument("--prefill-split", type=int, default=None,
-                    help="keys per run of the split prefill (pa_prefill_chunk_split): mixed "
-                         "workloads default to 0 = pa_prefill_chunk, one workgroup per query "
-                         "tile; prefill_long defaults to 3072")
+                    help="keys per run of the split prefill (pa_prefill_chunk_split): "
+                         "mixed_gqa defaults to 2048, the other mixed workloads to 0 = "
+                         "pa_prefill_chunk, one workgroup per query tile; prefill_long "
+                         "defaults to 3072")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode call and its merge (for counter runs); prints "
                          "a short JSON line")
@@ -1029,7 +1031,9 @@ def bench_attention(args, torch, dev, lib, name: str, partition_size=None, steps
     # long causal key ranges of the prefill chunks split over workgroups
     pf_split = 0
     if w.prefill is not None:
-        pf_split = 0 if args.prefill_split is None else args.prefill_split
+        # grouped-query heads: the split pays (2048-key runs); 40 heads: one run per tile
+        default_split = 2048 if base == "mixed_gqa" and not fp8 else 0
+        pf_split = default_split if args.prefill_split is None else args.prefill_split
     pf_maxc = int(w.prefill.context_lens.max()) if w.prefill is not None else 0
     pws = None
     if pf_split:

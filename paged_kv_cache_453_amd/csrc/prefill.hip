@@ -106,10 +106,36 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* base, int off) {
 //    workgroups of a quad run on its die, longer query tiles first: the K/V
 //    tiles the quad stages are fetched from HBM about once per die instead of
 //    once per query tile (and once for the 4 heads when they share a kv head).
+//  * the quads are taken sequence by sequence, the sequences in decreasing
+//    order of their causal work (pairs of a query and a key it sees), so the
+//    longest workgroups start first on every die instead of whenever their
+//    sequence's index comes up.
 // A launch has kXcds * ceil(quads / kXcds) * (query tiles x key runs) * 4 ids.
 struct PrefillItem {
   int s, h, qtile, split;
 };
+
+// The sequence of rank r in decreasing order of causal work, ties by index.
+// Every wave works it out from the chunk bounds and context lengths, one
+// sequence per lane; batches of more than a wave of sequences keep their order.
+__device__ __forceinline__ int seq_by_work(const DecodeArgs& a, int r) {
+  const int n = a.num_seqs;
+  if (n <= 1 || n > kWave) return r;
+  const int lane = threadIdx.x & (kWave - 1);
+  float work = 0.f;
+  if (lane < n) {
+    const int chunk = a.query_start_loc[lane + 1] - a.query_start_loc[lane];
+    const int len = a.context_lens[lane];
+    if (chunk > 0 && len >= chunk) work = (float)chunk * (2.f * (float)len - (float)chunk);
+  }
+  int rank = 0;
+  for (int j = 0; j < n; ++j) {
+    const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, work), j));
+    rank += (wj > work) || (wj == work && j < lane);
+  }
+  const uint64_t hit = __ballot(lane < n && rank == r);
+  return hit != 0 ? (int)__builtin_ctzll(hit) : r;
+}
 __device__ __forceinline__ bool prefill_item(const DecodeArgs& a, int QT, PrefillItem& it) {
   const int nsplit_max = a.partition_blocks > 0 ? a.max_partitions : 1;
   const int qt_count = (a.max_query_len + QT - 1) / QT;
@@ -122,8 +148,9 @@ __device__ __forceinline__ bool prefill_item(const DecodeArgs& a, int QT, Prefil
   const int member = rem / kEngines;
   const int quad = round * kXcds + xcd;
   if (quad >= a.num_seqs * quads_per_seq) return false;
-  it.s = quad / quads_per_seq;
-  it.h = (quad - it.s * quads_per_seq) * kEngines + (rem - member * kEngines);
+  const int rank = quad / quads_per_seq;
+  it.s = seq_by_work(a, rank);
+  it.h = (quad - rank * quads_per_seq) * kEngines + (rem - member * kEngines);
   if (it.h >= a.num_heads) return false;
   it.qtile = qt_count - 1 - member / nsplit_max;     // later (longer) tiles first
   it.split = member % nsplit_max;
