@@ -691,7 +691,7 @@ def bench_prefix_cache(args, torch, dev, lib, timer) -> int:
                               "lookup, slots) and the batch's take_moves, through the C ABI",
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "kernel": "prefill_dma_kernel<128,4>",
+                     "traffic": None, "kernel": "prefill_x32_kernel<128,4>",
                      "algorithmic_flops_per_launch": int(flops_hit),
                      "whole_prompt_flops": int(flops_whole)},
         "cpu_baseline": None if args.no_cpu_baseline else prefix_cpu_baseline(d, hq, own, total),
@@ -755,7 +755,7 @@ def bench_prefill_long(args, torch, dev, lib, timer) -> int:
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": None,
-                     "kernel": f"prefill_dma_kernel<128,4> in runs of {split} keys + "
+                     "kernel": f"prefill_x32_kernel<128,4> in runs of {split} keys + "
                                "prefill_merge_kernel (one pa_prefill_chunk_split call)",
                      "algorithmic_flops_per_launch": int(flops),
                      "unsplit_achieved": round(tf_plain, 2),
@@ -1162,7 +1162,7 @@ def bench_attention(args, torch, dev, lib, name: str, partition_size=None, steps
             "bound": "mfma", "achieved": round(pf_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(pf_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
             "traffic": None, "kernel": ("prefill_mfma_kernel<fp8,128,32,4>" if fp8 else
-                                        "prefill_dma_kernel<128,4>") + (
+                                        "prefill_x32_kernel<128,4>") + (
                 f" in runs of {pf_split} keys + prefill_merge_kernel (one "
                 "pa_prefill_chunk_split call)" if pf_split else ""),
             "algorithmic_flops_per_launch": int(flops)}

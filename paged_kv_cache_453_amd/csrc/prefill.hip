@@ -521,6 +521,16 @@ template <int D> __device__ __forceinline__ int k_swizzle(int row) {
 template <int D> __device__ __forceinline__ int v_swizzle(int row) {
   return D == 128 ? (((row & 7) << 1) | ((row >> 3) & 1)) : (((row >> 1) & 3) << 1);
 }
+// V rows for the 32x32 products' transposed reads (8 rows x 64 bytes per
+// instruction): chunk p of row `row` is stored at chunk p ^ v32_swizzle(row).
+template <int D> __device__ __forceinline__ int v32_swizzle(int row) {
+  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 mfma_32x32x16(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
 
 // One direct-to-LDS load: 64 lanes x 16 bytes from buffer `rs` at the lanes'
 // byte offsets `voff`, written to the 1 KB of LDS at `lds` (lane i at lds + 16 i).
@@ -918,6 +928,361 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_dma_kernel(DecodeArgs a) {
   }
 }
 
+
+// The same pipeline on v_mfma_f32_32x32x16_bf16.
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void prefill_x32_kernel(DecodeArgs a) {
+  static_assert(NW == 4, "one wave per cache block of a 64-key tile");
+  constexpr int RW = 32;                // query rows per wave: the 32 columns of the products
+  constexpr int KS = D / 16;            // k-steps of the score MFMA (16 dims each)
+  constexpr int DB = D / 32;            // 32-dim blocks of the output
+  constexpr int QT = NW * RW;           // query rows per workgroup
+  constexpr int NT = 64 * NW;           // threads per workgroup
+  constexpr int RB = D * 2;             // bytes per K or V row
+  constexpr int TILE = kKeys * RB;      // bytes per K or V tile
+  constexpr int SLAB = kBlock * RB;     // bytes per (block, kv head) slab
+  constexpr int NLD = SLAB / 1024;      // 1 KB loads per slab
+  constexpr int RPL = 1024 / RB;        // rows per 1 KB load
+  // four separate LDS objects, so that the compiler's wait for loads into one
+  // buffer is not imposed on reads of the other
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf1[TILE];
+  __shared__ int sh_bad;
+
+  PrefillItem it;
+  if (!prefill_item(a, QT, it)) return;
+  const int s = it.s, h = it.h, qtile = it.qtile, split = it.split;
+  const int nsplit_max = a.partition_blocks > 0 ? a.max_partitions : 1;
+  const int qt_count = (a.max_query_len + QT - 1) / QT;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = wave_uniform(tid >> 6);
+  const int r = lane & 31;              // this lane's query row (column of the products)
+  const int hh = lane >> 5;             // which half of each k-step it supplies
+  const int hq = a.num_heads;
+  const int kvh = h / a.group;
+
+  const int q0 = a.query_start_loc[s];
+  const int q1 = a.query_start_loc[s + 1];
+  if (q0 < 0 || q1 < q0 || q1 > a.num_items) return;
+  const int chunk = q1 - q0;
+  const int len = a.context_lens[s];
+  const int qr0 = qtile * QT;
+  if (qr0 >= chunk) return;
+  const bool bad = chunk > len || chunk > a.max_query_len || len > a.max_blocks_per_seq * kBlock ||
+                   (a.partition_blocks > 0 && len > a.max_context_len);
+  const int prefix = len - chunk;
+  bf16_t* out = static_cast<bf16_t*>(a.out);
+
+  if (bad) {
+    if (split != 0) return;
+    for (int base = qr0; base < chunk; base += qt_count * QT)
+      for (int i = tid; i < QT * D; i += NT) {
+        const int rr = base + i / D;
+        if (rr < chunk) out[((int64_t)(q0 + rr) * hq + h) * D + i % D] = 0x7FC0;
+      }
+    return;
+  }
+  const int qw0 = qr0 + w * RW;
+  const int wave_rows = max(0, min(RW, chunk - qw0));
+  const int wave_first_pos = prefix + qw0;
+  const int wave_last_pos = prefix + qw0 + wave_rows - 1;
+
+  const int qlast = min(chunk, qr0 + QT) - 1;
+  const int kend = prefix + qlast + 1;
+  const int ntiles = (kend + kKeys - 1) / kKeys;
+  const int nblk = (kend + kBlock - 1) / kBlock;
+  const int split_tiles = a.partition_blocks > 0 ? a.partition_blocks / 4 : ntiles;
+  const int nsplit = a.partition_blocks > 0 ? (ntiles + split_tiles - 1) / split_tiles : 1;
+  if (split >= nsplit) return;   // the whole workgroup: no barrier is left waiting
+  const int kt0 = split * split_tiles;
+  const int kt1 = min(ntiles, kt0 + split_tiles);
+  // tiles this wave sees any key of: kt0 .. wave_end-1; from mask_from on, a
+  // tile holds keys past some of its rows (the causal diagonal, and the
+  // zero-filled rows past kend), masked before the tile's max is taken
+  const int wave_end = wave_rows > 0 ? max(kt0, min(kt1, wave_last_pos / kKeys + 1)) : kt0;
+  const int mask_from = (wave_first_pos + 1) / kKeys;
+  if (tid == 0) sh_bad = 0;
+  plain_barrier();   // before any staging can set it
+
+  // Q^T as the B operand: lane (hh, r) holds dims 16 ks + 8 hh .. +7 of query row r
+  u32x4 qop[KS];
+  {
+    const int qi = qw0 + r;
+    const bf16_t* qsrc = static_cast<const bf16_t*>(a.query) + ((int64_t)(q0 + qi) * hq + h) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qop[ks] = qi < chunk ? *reinterpret_cast<const u32x4*>(qsrc + 8 * (2 * ks + hh))
+                           : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  const float sl2 = a.scale_log2;
+  const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  const uint8_t* kpool = static_cast<const uint8_t*>(a.k_cache);
+  const uint8_t* vpool = static_cast<const uint8_t*>(a.v_cache);
+
+  // Byte offsets inside a slab that lane `lane` loads for load j: its LDS row
+  // (tile row 16 w + RPL j + lane / (RB / 16)) and the swizzled chunk there.
+  int koff[NLD], voff[NLD];
+#pragma unroll
+  for (int j = 0; j < NLD; ++j) {
+    const int row = RPL * j + lane / (RB / 16);    // row in the slab = tile row mod 16
+    const int p = lane % (RB / 16);
+    koff[j] = row * RB + 16 * (p ^ k_swizzle<D>(row));
+    voff[j] = row * RB + 16 * (p ^ v32_swizzle<D>(row));
+  }
+  // This wave's block of tile kt: its id, read through the constant address
+  // space (the table is not written during the call) so that it is a scalar
+  // load, counted apart from the vector loads into the tile buffers.
+  typedef __attribute__((address_space(4))) const int32_t const_i32;
+  const_i32* ctable = (const_i32*)table;
+  const auto block_id = [&](int kt) { return ctable[min(kt * 4 + w, a.max_blocks_per_seq - 1)]; };
+  // This wave's slab of tile kt (block id `id`): its byte offset in a pool and
+  // its live bytes (0: past the keys, or an id outside the pool, which
+  // poisons the workgroup's rows).  The K and V slabs of a tile share it.
+  struct Slab {
+    int64_t off;
+    int bytes;
+  };
+  const uint32_t pool_ids = (uint32_t)min<int64_t>(a.num_blocks, 0x80000000ll);
+  const int64_t id_stride = (int64_t)a.num_kv_heads * SLAB;
+  const int64_t head_off = (int64_t)kvh * SLAB;
+  int bad_id = 0;        // this wave staged a block id outside the pool
+  const auto describe = [&](int kt, int id) {
+    const int gb = kt * 4 + w;
+    const int rows = gb < nblk ? min(kBlock, kend - gb * kBlock) : 0;
+    const bool in_pool = (uint32_t)id < pool_ids;
+    bad_id |= (int)(rows > 0) & (int)!in_pool;
+    const bool live = rows > 0 && in_pool;
+    return Slab{live ? id * id_stride + head_off : 0, live ? rows * RB : 0};
+  };
+  const auto stage = [&](uint8_t* dst_base, const uint8_t* pool, const int (&off)[NLD],
+                         const Slab& sl) {
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pool + sl.off), 0,
+                                                      sl.bytes, kBufferWord3);
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) load_lds_1k(rs, dst_base + w * SLAB + j * 1024, off[j]);
+  };
+  // every load of this wave has landed and no LDS read is outstanding; then
+  // meet the other waves
+  const auto sync_tiles = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);
+    plain_barrier();
+  };
+
+  // O^T: o[db][4i + j] is dim 32 db + 8 i + 4 hh + j of query row r
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  float lsum = 0.f;      // this lane's half of the row's sum of weights
+  float mref = kNoMax;   // the row's reference max (base 2), the same in both its lanes
+
+  // S^T = K Q^T from a K buffer: sc[kb][4i + j] is key 32 kb + 8 i + 4 hh + j of row r
+  const auto scores = [&](const uint8_t* kbuf, f32x16 (&sc)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int row = 32 * kb + r;
+      sc[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 ka = *reinterpret_cast<const u32x4*>(
+            kbuf + row * RB + 16 * ((2 * ks + hh) ^ k_swizzle<D>(row)));
+        sc[kb] = mfma_32x32x16(ka, qop[ks], sc[kb]);
+      }
+    }
+  };
+  // max of the lane's 32 scores of a tile, in base 2 (masked keys are -inf):
+  // a tree of three-way maxes
+  const auto row_max = [&](const f32x16 (&sc)[2], float& lmax) {
+    float m1[11];
+#pragma unroll
+    for (int x = 0; x < 10; ++x) {
+      const int e = 3 * x;
+      m1[x] = max3f(sc[e / 16][e % 16], sc[(e + 1) / 16][(e + 1) % 16],
+                    sc[(e + 2) / 16][(e + 2) % 16]);
+    }
+    m1[10] = fmaxf(sc[1][14], sc[1][15]);
+    const float a = max3f(m1[0], m1[1], m1[2]);
+    const float b = max3f(m1[3], m1[4], m1[5]);
+    const float c = max3f(m1[6], m1[7], m1[8]);
+    lmax = max3f(max3f(a, b, c), m1[9], m1[10]) * sl2;
+  };
+  // causal mask of tile kt: keys past a row's position get -inf
+  const auto mask = [&](f32x16 (&sc)[2], int kt) {
+    const int rel = wave_first_pos + r - kt * kKeys - 4 * hh;   // key index limit, tile-relative
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        sc[kb][q] = (32 * kb + 8 * (q / 4) + (q % 4) <= rel) ? sc[kb][q] : -INFINITY;
+  };
+  // lazy reference-max check against a tile's visible max (rare rescale)
+  const auto rescale = [&](float lmax) {
+    if (__ballot(lmax > mref + kSlack) != 0) {
+      const float rmax = fmaxf(lmax, __shfl_xor(lmax, 32, 64));
+      const float mn = rmax > mref + kSlack ? rmax : mref;
+      const float alpha = __builtin_amdgcn_exp2f(mref - mn);
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      mref = mn;
+    }
+  };
+  // P^T as the B operand of the p.V steps: step (kb, p) covers keys
+  // 32 kb + 16 p + {0..15}; lane (hh, r) supplies keys 4 hh + {0..3} and
+  // 8 + 4 hh + {0..3} of it, which are its own scores sc[kb][8p .. 8p+7]
+  const auto weights = [&](const f32x16 (&sc)[2], u32x4 (&pk)[2][2]) {
+    const float nmr = -mref;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        uint32_t wv[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          wv[x] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sc[kb][8 * p + 2 * x], sl2, nmr)),
+                              __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * p + 2 * x + 1], sl2, nmr)));
+        pk[kb][p] = u32x4{wv[0], wv[1], wv[2], wv[3]};
+      }
+  };
+  // row sums of the bf16 weights (the values the products use), and
+  // O^T += V^T P^T from a V buffer: the A operand of step (kb, p), d-block db
+  // is dims 32 db + r of those keys, two transposed 8-byte reads per lane
+  const auto accumulate = [&](const uint8_t* vbuf, const u32x4 (&pk)[2][2]) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          // (a named copy: a bit_cast of the vector element itself compiled to
+          // element 0 for every x)
+          const uint32_t pair = pk[kb][p][x];
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), ones, lsum, false);
+        }
+    const int t = lane & 15;
+    const int c0 = 16 * ((lane >> 4) & 1) + 4 * (t & 3);   // this lane's first column in a d-block
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int row = 32 * kb + 16 * p + 4 * hh + (t >> 2);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int b = 2 * (32 * db + c0);
+          const u32x2 lo = lds_read_tr16(
+              vbuf, row * RB + 16 * ((b >> 4) ^ v32_swizzle<D>(row)) + (b & 15));
+          const u32x2 hi = lds_read_tr16(
+              vbuf, (row + 8) * RB + 16 * ((b >> 4) ^ v32_swizzle<D>(row + 8)) + (b & 15));
+          o[db] = mfma_32x32x16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pk[kb][p], o[db]);
+        }
+      }
+  };
+
+  const auto in_range = [&](int kt) { return kt < kt1 ? kt : ntiles; };
+
+  // prologue: K of kt0 and kt0+1, V of kt0; the scores of tile kt0
+  f32x16 sa[2], sb[2];
+  float lm = 0.f;
+  int id_k = block_id(in_range(kt0 + 2));   // K of kt+2, staged in iteration kt
+  Slab slab_v;                              // V of kt+1: the slab its K was staged from
+  {
+    const Slab s0 = describe(kt0, block_id(kt0));
+    slab_v = describe(in_range(kt0 + 1), block_id(in_range(kt0 + 1)));
+    stage(kbuf0, kpool, koff, s0);
+    stage(vbuf0, vpool, voff, s0);
+    stage(kbuf1, kpool, koff, slab_v);
+    sync_tiles();
+    if (kt0 < wave_end) {
+      scores(kbuf0, sa);
+      if (kt0 >= mask_from) mask(sa, kt0);
+      row_max(sa, lm);
+    }
+    sync_tiles();
+  }
+
+  // iteration kt, with P = (kt - kt0) mod 2: K of kt+1 is in kbuf(1-P), V of kt
+  // in vbuf(P); K of kt+2 goes to kbuf(P), V of kt+1 to vbuf(1-P)
+  const auto iteration = [&](auto parity, int kt, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    constexpr int P = decltype(parity)::value;
+    uint8_t* const k_now = P ? kbuf0 : kbuf1;    // K of kt+1
+    uint8_t* const k_next = P ? kbuf1 : kbuf0;   // K of kt+2
+    uint8_t* const v_now = P ? vbuf1 : vbuf0;    // V of kt
+    uint8_t* const v_next = P ? vbuf0 : vbuf1;   // V of kt+1
+    const Slab slab_k = describe(in_range(kt + 2), id_k);
+    stage(k_next, kpool, koff, slab_k);
+    stage(v_next, vpool, voff, slab_v);
+    slab_v = slab_k;
+    id_k = block_id(in_range(kt + 3));
+    if (kt < wave_end) {
+      // cur holds tile kt's scores, masked where needed, and lm their max
+      rescale(lm);
+      // The next tile's scores are computed even past the wave's last tile
+      // (then from zeros or keys it does not see, never used), so that each
+      // phase is one straight block whose matrix and vector work can be
+      // interleaved.
+      // (the compiler's own interleaving of the two: fixed orders of reads,
+      // products and vector work measured 2-5% slower)
+      u32x4 pk[2][2];
+      scores(k_now, nxt);
+      weights(cur, pk);
+      accumulate(v_now, pk);
+      // the next tile's max over the keys its rows see
+      if (__builtin_expect(kt + 1 >= mask_from && kt + 1 < wave_end, 0)) mask(nxt, kt + 1);
+      row_max(nxt, lm);
+    }
+    sync_tiles();
+  };
+  for (int kt = kt0; kt < kt1; kt += 2) {
+    iteration(std::integral_constant<int, 0>(), kt, sa, sb);
+    if (kt + 1 >= kt1) break;
+    iteration(std::integral_constant<int, 1>(), kt + 1, sb, sa);
+  }
+
+  // a wave that staged an id outside the pool poisons the workgroup's rows
+  if (bad_id) sh_bad = 1;
+  sync_tiles();
+  const bool poisoned = sh_bad != 0;
+  const float l = lsum + __shfl_xor(lsum, 32, 64);
+  const int qi = qw0 + r;
+  if (nsplit > 1) {
+    if (qi >= chunk) return;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int64_t row = ((int64_t)(q0 + qi) * hq + h) * nsplit_max + split;
+    float* dst = a.part_o + row * D;
+    const float nan = __builtin_nanf("");
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * i + 4 * hh) =
+            poisoned ? f32x4{nan, nan, nan, nan}
+                     : f32x4{o[db][4 * i] * inv, o[db][4 * i + 1] * inv, o[db][4 * i + 2] * inv,
+                             o[db][4 * i + 3] * inv};
+    if (hh == 0)
+      a.part_lse[row] = poisoned ? nan : l > 0.f ? (mref + log2f(l)) * kLn2 : -INFINITY;
+    return;
+  }
+  if (qi >= chunk) return;
+  const float inv = 1.f / l;
+  bf16_t* dst = out + ((int64_t)(q0 + qi) * hq + h) * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = poisoned ? 0x7FC07FC0u
+                                   : pack_bf16x2(o[db][4 * i] * inv, o[db][4 * i + 1] * inv);
+      const uint32_t hi = poisoned ? 0x7FC07FC0u
+                                   : pack_bf16x2(o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv);
+      *reinterpret_cast<u32x2*>(dst + 32 * db + 8 * i + 4 * hh) = u32x2{lo, hi};
+    }
+}
+
 // 32 query rows per wave: each K/V operand read from LDS feeds two 16-row
 // blocks (16 rows per wave measured 15% slower on the mixed workload's chunks).
 constexpr int kPrefillRowsPerWave = 32;
@@ -1030,7 +1395,15 @@ hipError_t launch_prefill(const DecodeArgs& a, int head_dim, hipStream_t stream)
 #ifndef PA_PREFILL_DMA
 #define PA_PREFILL_DMA 1
 #endif
-  if (PA_PREFILL_DMA && std::is_same<KV, bf16_t>::value) {
+#ifndef PA_PREFILL_X32
+#define PA_PREFILL_X32 1
+#endif
+  if (PA_PREFILL_X32 && std::is_same<KV, bf16_t>::value) {
+    if (head_dim == 64)
+      hipLaunchKernelGGL((prefill_x32_kernel<64, NW>), grid, dim3(64 * NW), 0, stream, a);
+    else
+      hipLaunchKernelGGL((prefill_x32_kernel<128, NW>), grid, dim3(64 * NW), 0, stream, a);
+  } else if (PA_PREFILL_DMA && std::is_same<KV, bf16_t>::value) {
     if (head_dim == 64)
       hipLaunchKernelGGL((prefill_dma_kernel<64, NW>), grid, dim3(64 * NW), 0, stream, a);
     else
