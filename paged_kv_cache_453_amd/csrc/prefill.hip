@@ -3,10 +3,15 @@
 // Chunked prefill splits one prompt's prefill over several rounds (xdnf.cn
 // article, section 六.4); each chunk's queries sit at the last C positions of
 // their sequence and must see every earlier token, the paged prefix included.
-// Prefill is compute-bound (xdnf.cn article, section 六.5), so this kernel is a
-// flash-attention loop on v_mfma_f32_16x16x32_bf16 with fp32 accumulation, K/V
-// tiles gathered through the block table.
+// Prefill is compute-bound (xdnf.cn article, section 六.5), so both kernels
+// here are flash-attention loops on the bf16 matrix cores with fp32
+// accumulation, K/V tiles gathered through the block table:
+//  - bf16 caches: prefill_x32_kernel (further down), 32x32x16 products over
+//    tiles staged by direct-to-LDS loads two tiles ahead;
+//  - FP8 caches: prefill_mfma_kernel (first), 16x16x32 products over tiles
+//    that its waves load, widen to bf16 and store to LDS.
 //
+// prefill_mfma_kernel.
 // Tiling.  A workgroup (4 waves) owns 4*RW query rows of one head of one
 // sequence; each wave owns RW rows as RW/16 blocks of 16.  Keys go in tiles of
 // 64 (4 cache blocks), staged in LDS row-major (padded rows) by coalesced
@@ -38,7 +43,8 @@
 // FP8 (E4M3) caches: the staging loads read 8 codes (8 bytes) where they would
 // read 8 bf16 (16 bytes), and widen them to bf16 as they store the tile to LDS
 // (exact: an E4M3 value has at most 4 significant bits); from there the
-// kernel is the bf16 one.  The per-tensor K scale is folded into the score
+// arithmetic is that of a bf16 tile (the template also builds for bf16
+// caches, which the launcher sends to the 32x32 kernel).  The per-tensor K scale is folded into the score
 // scale by the caller, the V scale into the final normalisation.
 //
 // Softmax in base 2 with lazy rescaling: a row's reference max moves only when
@@ -485,7 +491,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(DecodeArgs a) {
   }
 }
 
-// Direct-to-LDS, software-pipelined variant for bf16 caches.
+// Direct-to-LDS, software-pipelined prefill for bf16 caches on 32x32 products.
 //
 // Staging.  Each wave copies one of the tile's four cache blocks (its K and V
 // slabs) with direct-to-LDS buffer loads: one instruction moves 1 KB, 64 lanes
@@ -499,27 +505,25 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(DecodeArgs a) {
 //  - K (read as 16-byte A operands, 16 rows x one chunk per group of lanes):
 //    LDS chunk p of row r holds chunk p ^ (r mod 16) (D = 128), p ^ ((r / 2)
 //    mod 8) (D = 64);
-//  - V (read with the transposing 8-byte LDS read, 8 rows x 2 chunks per half
-//    wave): chunk p of row r holds chunk p ^ (2 (r mod 8) + (r / 8) mod 2)
-//    (D = 128), p ^ 2 ((r / 2) mod 4) (D = 64).
+//  - V (read with the transposing 8-byte LDS read, 8 rows x 64 bytes per
+//    instruction): chunk p of row r holds chunk p ^ 4 (r mod 4) (D = 128),
+//    p ^ 4 ((r / 2) mod 2) (D = 64).
 // K and V each have two tile buffers (64 KB in all at D = 128, so two
 // workgroups fit a compute unit).
 //
 // Pipeline.  K runs one tile ahead of V: during iteration kt the LDS holds K
 // of tile kt+1 and V of tile kt, and the loads of K of kt+2 and V of kt+1 --
 // issued at the top of the iteration into the buffers the previous iteration
-// finished with -- are in flight.  A wave holds the raw scores of tile kt
-// from the previous iteration and computes: the lazy reference-max check of
-// tile kt (a rescale is rare) and its causal mask, then the score MFMAs of
+// finished with -- are in flight.  A wave holds the scores of tile kt, masked
+// and with their max taken in the previous iteration, and computes: the lazy
+// reference-max check of tile kt (a rescale is rare), then the score MFMAs of
 // tile kt+1 interleaved with exp2 and the bf16 packing of tile kt's weights,
-// then the p.V MFMAs and row sums of tile kt beside the row maxima of tile
-// kt+1.  One barrier per tile, after each wave has waited for its own loads.
-// The arithmetic of every (query, key) pair is that of prefill_mfma_kernel.
+// then the row sums (v_dot2c of the packed weights with ones) and p.V MFMAs of
+// tile kt, then the causal mask and row maxima of tile kt+1.  One barrier per
+// tile, after each wave has waited for its own loads.  The arithmetic of every
+// (query, key) pair is that of prefill_mfma_kernel.
 template <int D> __device__ __forceinline__ int k_swizzle(int row) {
   return D == 128 ? (row & 15) : ((row >> 1) & 7);
-}
-template <int D> __device__ __forceinline__ int v_swizzle(int row) {
-  return D == 128 ? (((row & 7) << 1) | ((row >> 3) & 1)) : (((row >> 1) & 3) << 1);
 }
 // V rows for the 32x32 products' transposed reads (8 rows x 64 bytes per
 // instruction): chunk p of row `row` is stored at chunk p ^ v32_swizzle(row).
@@ -556,380 +560,21 @@ __device__ __forceinline__ void plain_barrier() {
   __asm__ __volatile__("" ::: "memory");
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW, 2) void prefill_dma_kernel(DecodeArgs a) {
-  static_assert(NW == 4, "one wave per cache block of a 64-key tile");
-  constexpr int RW = 32;                // query rows per wave
-  constexpr int KS = D / 32;            // k-steps of the score MFMA
-  constexpr int DT = D / 16;            // d-tiles of the output
-  constexpr int QB = RW / 16;           // 16-row query blocks per wave
-  constexpr int QT = NW * RW;           // query rows per workgroup
-  constexpr int NT = 64 * NW;           // threads per workgroup
-  constexpr int RB = D * 2;             // bytes per K or V row
-  constexpr int TILE = kKeys * RB;      // bytes per K or V tile
-  constexpr int SLAB = kBlock * RB;     // bytes per (block, kv head) slab
-  constexpr int NLD = SLAB / 1024;      // 1 KB loads per slab
-  constexpr int RPL = 1024 / RB;        // rows per 1 KB load
-  // four separate LDS objects, so that the compiler's wait for loads into one
-  // buffer is not imposed on reads of the other
-  __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t vbuf0[TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t vbuf1[TILE];
-  __shared__ int sh_bad;
-
-  PrefillItem it;
-  if (!prefill_item(a, QT, it)) return;
-  const int s = it.s, h = it.h, qtile = it.qtile, split = it.split;
-  const int nsplit_max = a.partition_blocks > 0 ? a.max_partitions : 1;
-  const int qt_count = (a.max_query_len + QT - 1) / QT;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = wave_uniform(tid >> 6);
-  const int r = lane & 15;
-  const int g = lane >> 4;
-  const int hq = a.num_heads;
-  const int kvh = h / a.group;
-
-  const int q0 = a.query_start_loc[s];
-  const int q1 = a.query_start_loc[s + 1];
-  if (q0 < 0 || q1 < q0 || q1 > a.num_items) return;
-  const int chunk = q1 - q0;
-  const int len = a.context_lens[s];
-  const int qr0 = qtile * QT;
-  if (qr0 >= chunk) return;
-  const bool bad = chunk > len || chunk > a.max_query_len || len > a.max_blocks_per_seq * kBlock ||
-                   (a.partition_blocks > 0 && len > a.max_context_len);
-  const int prefix = len - chunk;
-  bf16_t* out = static_cast<bf16_t*>(a.out);
-
-  if (bad) {
-    if (split != 0) return;
-    for (int base = qr0; base < chunk; base += qt_count * QT)
-      for (int i = tid; i < QT * D; i += NT) {
-        const int rr = base + i / D;
-        if (rr < chunk) out[((int64_t)(q0 + rr) * hq + h) * D + i % D] = 0x7FC0;
-      }
-    return;
-  }
-  const int qw0 = qr0 + w * RW;
-  const int wave_rows = max(0, min(RW, chunk - qw0));
-  const int wave_first_pos = prefix + qw0;
-  const int wave_last_pos = prefix + qw0 + wave_rows - 1;
-
-  const int qlast = min(chunk, qr0 + QT) - 1;
-  const int kend = prefix + qlast + 1;
-  const int ntiles = (kend + kKeys - 1) / kKeys;
-  const int nblk = (kend + kBlock - 1) / kBlock;
-  const int split_tiles = a.partition_blocks > 0 ? a.partition_blocks / 4 : ntiles;
-  const int nsplit = a.partition_blocks > 0 ? (ntiles + split_tiles - 1) / split_tiles : 1;
-  if (split >= nsplit) return;   // the whole workgroup: no barrier is left waiting
-  const int kt0 = split * split_tiles;
-  const int kt1 = min(ntiles, kt0 + split_tiles);
-  // tiles this wave sees any key of: kt0 .. wave_end-1; from mask_from on, a
-  // tile holds keys past some of its rows (the causal diagonal, and the
-  // zero-filled rows past kend), masked before the tile's max is taken
-  const int wave_end = wave_rows > 0 ? max(kt0, min(kt1, wave_last_pos / kKeys + 1)) : kt0;
-  const int mask_from = (wave_first_pos + 1) / kKeys;
-  if (tid == 0) sh_bad = 0;
-  plain_barrier();   // before any staging can set it
-
-  u32x4 qop[QB][KS];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qi = qw0 + 16 * qb + r;
-    const bf16_t* qsrc = static_cast<const bf16_t*>(a.query) + ((int64_t)(q0 + qi) * hq + h) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qop[qb][ks] = qi < chunk ? *reinterpret_cast<const u32x4*>(qsrc + 8 * (4 * ks + g))
-                               : u32x4{0u, 0u, 0u, 0u};
-  }
-
-  const float sl2 = a.scale_log2;
-  const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-  const uint8_t* kpool = static_cast<const uint8_t*>(a.k_cache);
-  const uint8_t* vpool = static_cast<const uint8_t*>(a.v_cache);
-
-  // Byte offsets inside a slab that lane `lane` loads for load j: its LDS row
-  // (tile row 16 w + RPL j + lane / (RB / 16)) and the swizzled chunk there.
-  int koff[NLD], voff[NLD];
-#pragma unroll
-  for (int j = 0; j < NLD; ++j) {
-    const int row = RPL * j + lane / (RB / 16);    // row in the slab = tile row mod 16
-    const int p = lane % (RB / 16);
-    koff[j] = row * RB + 16 * (p ^ k_swizzle<D>(row));
-    voff[j] = row * RB + 16 * (p ^ v_swizzle<D>(row));
-  }
-  // This wave's block of tile kt: its id, read through the constant address
-  // space (the table is not written during the call) so that it is a scalar
-  // load, counted apart from the vector loads into the tile buffers.
-  typedef __attribute__((address_space(4))) const int32_t const_i32;
-  const_i32* ctable = (const_i32*)table;
-  const auto block_id = [&](int kt) { return ctable[min(kt * 4 + w, a.max_blocks_per_seq - 1)]; };
-  // This wave's slab of tile kt (block id `id`): its byte offset in a pool and
-  // its live bytes (0: past the keys, or an id outside the pool, which
-  // poisons the workgroup's rows).  The K and V slabs of a tile share it.
-  struct Slab {
-    int64_t off;
-    int bytes;
-  };
-  const uint32_t pool_ids = (uint32_t)min<int64_t>(a.num_blocks, 0x80000000ll);
-  const int64_t id_stride = (int64_t)a.num_kv_heads * SLAB;
-  const int64_t head_off = (int64_t)kvh * SLAB;
-  int bad_id = 0;        // this wave staged a block id outside the pool
-  const auto describe = [&](int kt, int id) {
-    const int gb = kt * 4 + w;
-    const int rows = gb < nblk ? min(kBlock, kend - gb * kBlock) : 0;
-    const bool in_pool = (uint32_t)id < pool_ids;
-    bad_id |= (int)(rows > 0) & (int)!in_pool;
-    const bool live = rows > 0 && in_pool;
-    return Slab{live ? id * id_stride + head_off : 0, live ? rows * RB : 0};
-  };
-  const auto stage = [&](uint8_t* dst_base, const uint8_t* pool, const int (&off)[NLD],
-                         const Slab& sl) {
-    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pool + sl.off), 0,
-                                                      sl.bytes, kBufferWord3);
-#pragma unroll
-    for (int j = 0; j < NLD; ++j) load_lds_1k(rs, dst_base + w * SLAB + j * 1024, off[j]);
-  };
-  // every load of this wave has landed and no LDS read is outstanding; then
-  // meet the other waves
-  const auto sync_tiles = [&]() {
-    __builtin_amdgcn_s_waitcnt(0);
-    plain_barrier();
-  };
-
-  f32x4 o[QB][DT];
-  f32x4 lacc[QB];
-  float mref[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    mref[qb] = kNoMax;
-    lacc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < DT; ++t) o[qb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // S^T = K Q^T from a K buffer: lane holds S[row 16qb + r][key 16nt + 4g + i]
-  const auto scores = [&](const uint8_t* kb, f32x4 (&sc)[QB][4]) {
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int row = 16 * nt + r;
-      u32x4 ka[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        ka[ks] = *reinterpret_cast<const u32x4*>(
-            kb + row * RB + 16 * ((4 * ks + g) ^ k_swizzle<D>(row)));
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        sc[qb][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sc[qb][nt] = mfma_16x16x32(ka[ks], qop[qb][ks], sc[qb][nt]);
-      }
-    }
-  };
-  // max of a tile's scores per row block, in base 2 (masked keys are -inf):
-  // a tree of 8 three-way maxes over the lane's 16 scores, depth 3
-  const auto row_max = [&](const f32x4 (&sc)[QB][4], float (&lm)[QB]) {
-    float m1[QB][5];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const f32x4* v = sc[qb];
-      m1[qb][0] = max3f(v[0][0], v[0][1], v[0][2]);
-      m1[qb][1] = max3f(v[0][3], v[1][0], v[1][1]);
-      m1[qb][2] = max3f(v[1][2], v[1][3], v[2][0]);
-      m1[qb][3] = max3f(v[2][1], v[2][2], v[2][3]);
-      m1[qb][4] = max3f(v[3][0], v[3][1], v[3][2]);
-    }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float a = max3f(m1[qb][0], m1[qb][1], m1[qb][2]);
-      const float b = max3f(m1[qb][3], m1[qb][4], sc[qb][3][3]);
-      lm[qb] = max3f(a, b, b) * sl2;
-    }
-  };
-  // causal mask of tile kt: keys past a row's position get -inf
-  const auto mask = [&](f32x4 (&sc)[QB][4], int kt) {
-    const int tile_first = kt * kKeys;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int qpos = wave_first_pos + 16 * qb + r;
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sc[qb][nt][i] = (tile_first + 16 * nt + 4 * g + i <= qpos) ? sc[qb][nt][i] : -INFINITY;
-    }
-  };
-  // lazy reference-max check against a tile's visible max (rare rescale)
-  const auto rescale = [&](const float (&lm)[QB]) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      if (__ballot(lm[qb] > mref[qb] + kSlack) != 0) {
-        float rmax = fmaxf(lm[qb], __shfl_xor(lm[qb], 16, 64));
-        rmax = fmaxf(rmax, __shfl_xor(rmax, 32, 64));
-        const float mn = rmax > mref[qb] + kSlack ? rmax : mref[qb];
-        const float alpha = __builtin_amdgcn_exp2f(mref[qb] - mn);
-        lacc[qb] *= alpha;
-#pragma unroll
-        for (int t = 0; t < DT; ++t) o[qb][t] *= alpha;
-        mref[qb] = mn;
-      }
-    }
-  };
-  const auto weights = [&](const f32x4 (&sc)[QB][4], u32x4 (&pk)[2][QB]) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float nmr = -mref[qb];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        uint32_t wv[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const f32x4& sv = sc[qb][2 * kk + x / 2];
-          const int i0 = 2 * (x % 2);
-          wv[x] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sv[i0], sl2, nmr)),
-                              __builtin_amdgcn_exp2f(fmaf(sv[i0 + 1], sl2, nmr)));
-        }
-        pk[kk][qb] = u32x4{wv[0], wv[1], wv[2], wv[3]};
-      }
-    }
-  };
-  // row sums (all-ones A operand) and O^T += V^T P^T from a V buffer
-  const auto accumulate = [&](const uint8_t* vb, const u32x4 (&pk)[2][QB]) {
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) lacc[qb] = mfma_16x16x32(kOnes, pk[kk][qb], lacc[qb]);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int vrow = 32 * kk + 4 * g + ((lane & 15) >> 2);
-      const int vb8 = 8 * (lane & 3);          // byte of the 32-byte column group
-      u32x4 va[DT];
-#pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        const int b = 32 * t + vb8;
-        const u32x2 lo = lds_read_tr16(
-            vb, vrow * RB + 16 * ((b >> 4) ^ v_swizzle<D>(vrow)) + (b & 15));
-        const u32x2 hi = lds_read_tr16(
-            vb, (vrow + 16) * RB + 16 * ((b >> 4) ^ v_swizzle<D>(vrow + 16)) + (b & 15));
-        va[t] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-      }
-#pragma unroll
-      for (int t = 0; t < DT; ++t)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) o[qb][t] = mfma_16x16x32(va[t], pk[kk][qb], o[qb][t]);
-    }
-  };
-
-  const auto in_range = [&](int kt) { return kt < kt1 ? kt : ntiles; };
-
-  // prologue: K of kt0 and kt0+1, V of kt0; the scores of tile kt0
-  f32x4 sa[QB][4], sb[QB][4];
-  float lm[QB] = {};
-  int id_k = block_id(in_range(kt0 + 2));   // K of kt+2, staged in iteration kt
-  Slab slab_v;                              // V of kt+1: the slab its K was staged from
-  {
-    const Slab s0 = describe(kt0, block_id(kt0));
-    slab_v = describe(in_range(kt0 + 1), block_id(in_range(kt0 + 1)));
-    stage(kbuf0, kpool, koff, s0);
-    stage(vbuf0, vpool, voff, s0);
-    stage(kbuf1, kpool, koff, slab_v);
-    sync_tiles();
-    if (kt0 < wave_end) {
-      scores(kbuf0, sa);
-      if (kt0 >= mask_from) mask(sa, kt0);
-      row_max(sa, lm);
-    }
-    sync_tiles();
-  }
-
-  // iteration kt, with P = (kt - kt0) mod 2: K of kt+1 is in kbuf(1-P), V of kt
-  // in vbuf(P); K of kt+2 goes to kbuf(P), V of kt+1 to vbuf(1-P)
-  const auto iteration = [&](auto parity, int kt, f32x4 (&cur)[QB][4], f32x4 (&nxt)[QB][4]) {
-    constexpr int P = decltype(parity)::value;
-    uint8_t* const k_now = P ? kbuf0 : kbuf1;    // K of kt+1
-    uint8_t* const k_next = P ? kbuf1 : kbuf0;   // K of kt+2
-    uint8_t* const v_now = P ? vbuf1 : vbuf0;    // V of kt
-    uint8_t* const v_next = P ? vbuf0 : vbuf1;   // V of kt+1
-    const Slab slab_k = describe(in_range(kt + 2), id_k);
-    stage(k_next, kpool, koff, slab_k);
-    stage(v_next, vpool, voff, slab_v);
-    slab_v = slab_k;
-    id_k = block_id(in_range(kt + 3));
-    if (kt < wave_end) {
-      // cur holds tile kt's scores, masked where needed, and lm their max
-      rescale(lm);
-      // The next tile's scores are computed even past the wave's last tile
-      // (then from zeros or keys it does not see, never used), so that each
-      // phase is one straight block whose matrix and vector work can be
-      // interleaved.
-      u32x4 pk[2][QB];
-      scores(k_now, nxt);
-      weights(cur, pk);
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);     // K operand reads
-#pragma unroll
-        for (int j = 0; j < QB * KS; ++j) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);    // vector / transcendental
-        }
-      }
-      accumulate(v_now, pk);
-      // the next tile's max over the keys its rows see
-      if (__builtin_expect(kt + 1 >= mask_from && kt + 1 < wave_end, 0)) mask(nxt, kt + 1);
-      row_max(nxt, lm);
-    }
-    sync_tiles();
-  };
-  for (int kt = kt0; kt < kt1; kt += 2) {
-    iteration(std::integral_constant<int, 0>(), kt, sa, sb);
-    if (kt + 1 >= kt1) break;
-    iteration(std::integral_constant<int, 1>(), kt + 1, sb, sa);
-  }
-
-  // a wave that staged an id outside the pool poisons the workgroup's rows
-  if (bad_id) sh_bad = 1;
-  sync_tiles();
-  const bool poisoned = sh_bad != 0;
-  if (nsplit > 1) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float l = lacc[qb][0];
-      const int qi = qw0 + 16 * qb + r;
-      if (qi >= chunk) continue;
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      const int64_t row = ((int64_t)(q0 + qi) * hq + h) * nsplit_max + split;
-      float* dst = a.part_o + row * D;
-      const float nan = __builtin_nanf("");
-#pragma unroll
-      for (int t = 0; t < DT; ++t)
-        *reinterpret_cast<f32x4*>(dst + 16 * t + 4 * g) =
-            poisoned ? f32x4{nan, nan, nan, nan} : o[qb][t] * inv;
-      if (g == 0)
-        a.part_lse[row] = poisoned ? nan : l > 0.f ? (mref[qb] + log2f(l)) * kLn2 : -INFINITY;
-    }
-    return;
-  }
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float l = lacc[qb][0];
-    const int qi = qw0 + 16 * qb + r;
-    if (qi >= chunk) continue;
-    const float inv = 1.f / l;
-    bf16_t* dst = out + ((int64_t)(q0 + qi) * hq + h) * D;
-#pragma unroll
-    for (int t = 0; t < DT; ++t) {
-      const uint32_t lo = poisoned ? 0x7FC07FC0u : pack_bf16x2(o[qb][t][0] * inv, o[qb][t][1] * inv);
-      const uint32_t hi = poisoned ? 0x7FC07FC0u : pack_bf16x2(o[qb][t][2] * inv, o[qb][t][3] * inv);
-      *reinterpret_cast<u32x2*>(dst + 16 * t + 4 * g) = u32x2{lo, hi};
-    }
-  }
-}
-
-
-// The same pipeline on v_mfma_f32_32x32x16_bf16.
+// The products.  v_mfma_f32_32x32x16_bf16 (32 x 32 results, 16-deep k-steps)
+// runs at nearly the part's bf16 peak in a loop of independent products, where
+// the 16x16x32 form reaches little more than half of it.  Lane l = 32 hh + r
+// supplies row r of the A operand and column r of the B operand, k-slots
+// 8 hh .. 8 hh + 7 of each k-step, and holds result rows 8 i + 4 hh + j
+// (j < 4) of column r in result register 4 i + j.  A wave owns 32 query rows,
+// the columns of both products:
+//  - scores S^T = K Q^T: A is 32 keys of the K tile (16-byte swizzled reads),
+//    B is the wave's Q, held in registers for the whole walk;
+//  - O^T += V^T P^T: step (kb, p) takes keys 32 kb + 16 p + {4 hh + (0..3),
+//    8 + 4 hh + (0..3)} in lane (hh, r), exactly that lane's own scores
+//    8 p .. 8 p + 7 of key block kb, so the weights need no data movement; A
+//    is 32 dims of those keys from two transposing 8-byte LDS reads.
+// A row's 64 scores of a tile sit in two lanes (r and r + 32), 32 each; its
+// max and sum combine the two with one cross-lane step.
 
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_x32_kernel(DecodeArgs a) {
@@ -1392,26 +1037,16 @@ hipError_t launch_prefill(const DecodeArgs& a, int head_dim, hipStream_t stream)
   const int64_t nwg = kXcds * ((quads + kXcds - 1) / kXcds) * members * kEngines;
   if (nwg > INT32_MAX) return hipErrorInvalidValue;
   dim3 grid((unsigned)nwg);
-#ifndef PA_PREFILL_DMA
-#define PA_PREFILL_DMA 1
-#endif
-#ifndef PA_PREFILL_X32
-#define PA_PREFILL_X32 1
-#endif
-  if (PA_PREFILL_X32 && std::is_same<KV, bf16_t>::value) {
+  if constexpr (std::is_same<KV, bf16_t>::value) {
     if (head_dim == 64)
       hipLaunchKernelGGL((prefill_x32_kernel<64, NW>), grid, dim3(64 * NW), 0, stream, a);
     else
       hipLaunchKernelGGL((prefill_x32_kernel<128, NW>), grid, dim3(64 * NW), 0, stream, a);
-  } else if (PA_PREFILL_DMA && std::is_same<KV, bf16_t>::value) {
-    if (head_dim == 64)
-      hipLaunchKernelGGL((prefill_dma_kernel<64, NW>), grid, dim3(64 * NW), 0, stream, a);
-    else
-      hipLaunchKernelGGL((prefill_dma_kernel<128, NW>), grid, dim3(64 * NW), 0, stream, a);
-  } else if (head_dim == 64) {
-    hipLaunchKernelGGL((prefill_mfma_kernel<KV, 64, RW, NW>), grid, dim3(64 * NW), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((prefill_mfma_kernel<KV, 128, RW, NW>), grid, dim3(64 * NW), 0, stream, a);
+    if (head_dim == 64)
+      hipLaunchKernelGGL((prefill_mfma_kernel<KV, 64, RW, NW>), grid, dim3(64 * NW), 0, stream, a);
+    else
+      hipLaunchKernelGGL((prefill_mfma_kernel<KV, 128, RW, NW>), grid, dim3(64 * NW), 0, stream, a);
   }
   if (a.partition_blocks > 0 && nsplit_max > 1) {
     const hipError_t e = hipGetLastError();
