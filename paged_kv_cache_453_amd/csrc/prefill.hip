@@ -538,9 +538,11 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(const u32x4& a, const u32x4& b, 
 
 // One direct-to-LDS load: 64 lanes x 16 bytes from buffer `rs` at the lanes'
 // byte offsets `voff`, written to the 1 KB of LDS at `lds` (lane i at lds + 16 i).
+// POLICY: cache-policy bits, 0 or 2 (nontemporal: the lines are evicted first).
+template <int POLICY>
 __device__ __forceinline__ void load_lds_1k(__amdgpu_buffer_rsrc_t rs, uint8_t* lds, int voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16,
-                                           voff, 0, 0, 0);
+                                           voff, 0, 0, POLICY);
 }
 
 // max(a, b, c) in one instruction, with fmaxf's rule for NaN operands (they
@@ -576,7 +578,9 @@ __device__ __forceinline__ void plain_barrier() {
 // A row's 64 scores of a tile sit in two lanes (r and r + 32), 32 each; its
 // max and sum combine the two with one cross-lane step.
 
-template <int D, int NW>
+// STREAM: K/V tiles loaded with the nontemporal hint, for launches in which no
+// other workgroup reads them (see the launcher).
+template <int D, int NW, bool STREAM>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_x32_kernel(DecodeArgs a) {
   static_assert(NW == 4, "one wave per cache block of a 64-key tile");
   constexpr int RW = 32;                // query rows per wave: the 32 columns of the products
@@ -709,7 +713,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_x32_kernel(DecodeArgs a) {
     const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pool + sl.off), 0,
                                                       sl.bytes, kBufferWord3);
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) load_lds_1k(rs, dst_base + w * SLAB + j * 1024, off[j]);
+    for (int j = 0; j < NLD; ++j)
+      load_lds_1k<STREAM ? 2 : 0>(rs, dst_base + w * SLAB + j * 1024, off[j]);
   };
   // every load of this wave has landed and no LDS read is outstanding; then
   // meet the other waves
@@ -1038,10 +1043,25 @@ hipError_t launch_prefill(const DecodeArgs& a, int head_dim, hipStream_t stream)
   if (nwg > INT32_MAX) return hipErrorInvalidValue;
   dim3 grid((unsigned)nwg);
   if constexpr (std::is_same<KV, bf16_t>::value) {
-    if (head_dim == 64)
-      hipLaunchKernelGGL((prefill_x32_kernel<64, NW>), grid, dim3(64 * NW), 0, stream, a);
-    else
-      hipLaunchKernelGGL((prefill_x32_kernel<128, NW>), grid, dim3(64 * NW), 0, stream, a);
+    // With one query tile per sequence and one query head per kv head, each
+    // workgroup stages K/V that no other workgroup of the launch reads (unless
+    // sequences share prefix blocks): they are streamed past the caches, as
+    // decode streams its K/V (long prefixes split over the keys: 304 -> 281 us).
+    // Otherwise the query tiles and the heads of a kv head re-read them from
+    // the L2, where the hint would evict them early (prefix-cache prefill, 256
+    // query rows over a shared prefix: 413 -> 478 us with it).
+    const bool stream_kv = members == nsplit_max && a.group == 1;
+    if (head_dim == 64) {
+      if (stream_kv)
+        hipLaunchKernelGGL((prefill_x32_kernel<64, NW, true>), grid, dim3(64 * NW), 0, stream, a);
+      else
+        hipLaunchKernelGGL((prefill_x32_kernel<64, NW, false>), grid, dim3(64 * NW), 0, stream, a);
+    } else {
+      if (stream_kv)
+        hipLaunchKernelGGL((prefill_x32_kernel<128, NW, true>), grid, dim3(64 * NW), 0, stream, a);
+      else
+        hipLaunchKernelGGL((prefill_x32_kernel<128, NW, false>), grid, dim3(64 * NW), 0, stream, a);
+    }
   } else {
     if (head_dim == 64)
       hipLaunchKernelGGL((prefill_mfma_kernel<KV, 64, RW, NW>), grid, dim3(64 * NW), 0, stream, a);
