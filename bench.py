@@ -22,7 +22,7 @@ shuffled pool) with split-K partitions and their merge.
             one scale per pool: quantising scatter (llama13b), chunked prefill
             (mixed), decode, merge; KV bytes count one byte per element
   prefill_long  4 chunks of 128 tokens over 16384-token paged prefixes (40
-            heads): the split prefill (runs of 3072 keys) against one workgroup
+            heads): the split prefill (runs of 5504 keys) against one workgroup
             per query tile; with one 128-row query tile per (sequence, kv head)
             the K/V stream bounds it, so its roofline is HBM (K/V bytes read
             once), the TFLOP/s metric beside it
@@ -712,9 +712,11 @@ def bench_prefill_long(args, torch, dev, lib, timer) -> int:
     from workloads.device import to_device
 
     nseq, prefix, chunk, h, d = 4, 16384, 128, 40, 128
-    # runs of 3072 keys: 6 per query tile, 960 workgroups, just under two rounds
-    # of the part's 512 workgroup slots (the fastest of 1536-4096)
-    split = args.prefill_split or 3072
+    # runs of 5504 keys: 3 even runs per query tile (86 tiles each), 480
+    # workgroups, one round of the part's 512 workgroup slots; with the K/V
+    # streamed past the caches this beats 6 runs of 3072 (235 vs 278 us) and
+    # the other sizes of 1536-5632
+    split = args.prefill_split or 5504
     w = make_prefill("prefill-long", 453, "bf16", [prefix] * nseq, [chunk] * nseq, h, h, d,
                      nseq * ((prefix + chunk) // 16 + 1))
     dw = to_device(w, device=dev)
@@ -898,7 +900,7 @@ def main(argv=None):
                     help="keys per run of the split prefill (pa_prefill_chunk_split): "
                          "mixed_gqa defaults to 2048, the other mixed workloads to 0 = "
                          "pa_prefill_chunk, one workgroup per query tile; prefill_long "
-                         "defaults to 3072")
+                         "defaults to 5504")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode call and its merge (for counter runs); prints "
                          "a short JSON line")
