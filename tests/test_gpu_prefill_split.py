@@ -135,11 +135,14 @@ def test_split_contract(gpu):
 
 
 @pytest.mark.slow
-def test_long_prefix_split_launch(gpu):
-    """The launch bench.py --workload prefill_long times: runs of 3072 keys over
-    a 16384-token prefix with a 128-token chunk (one sequence, 8 heads, so the
-    oracle finishes in seconds)."""
-    say("split prefill: 128-token chunk over a 16384-token prefix, runs of 3072 keys")
+@pytest.mark.parametrize("split", [3072, 5504])
+def test_long_prefix_split_launch(gpu, split):
+    """The launch bench.py --workload prefill_long times: three even runs of
+    5504 keys (and six of 3072) over a 16384-token prefix with a 128-token
+    chunk (one sequence, 8 heads, so the oracle finishes in seconds).  One
+    query tile per sequence and one query head per kv head: the launch that
+    streams its K/V with the nontemporal hint."""
+    say(f"split prefill: 128-token chunk over a 16384-token prefix, runs of {split} keys")
     w = make_prefill("split-long", 89, "bf16", [16384], [128], 8, 8, 128, 1040)
-    out = run_split(w, 3072)
-    assert_close(as_f64(out), oracle_prefill(w), "bf16", "long prefix split")
+    out = run_split(w, split)
+    assert_close(as_f64(out), oracle_prefill(w), "bf16", f"long prefix split {split}")
