@@ -108,10 +108,13 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* base, int off) {
 //    so every 4 consecutive ids of a die are one (query tile, key run) of the 4
 //    heads of a quad: the 4 engines get equal work in lockstep and none waits
 //    on another's long workgroup;
-//  * quads are dealt to the dies round-robin, and all (query tile, key run)
-//    workgroups of a quad run on its die, longer query tiles first: the K/V
-//    tiles the quad stages are fetched from HBM about once per die instead of
-//    once per query tile (and once for the 4 heads when they share a kv head).
+//  * quads are dealt to the dies in rounds of kXcds, every other round in
+//    reverse order (die 0 takes the first and the last quad of the first two
+//    rounds), so that the dies' shares of unequal sequences even out; all
+//    (query tile, key run) workgroups of a quad run on its die, longer query
+//    tiles first: the K/V tiles the quad stages are fetched from HBM about
+//    once per die instead of once per query tile (and once for the 4 heads
+//    when they share a kv head).
 //  * the quads are taken sequence by sequence, the sequences in decreasing
 //    order of their causal work (pairs of a query and a key it sees), so the
 //    longest workgroups start first on every die instead of whenever their
@@ -152,7 +155,7 @@ __device__ __forceinline__ bool prefill_item(const DecodeArgs& a, int QT, Prefil
   const int round = k / (X * kEngines);
   const int rem = k - round * (X * kEngines);
   const int member = rem / kEngines;
-  const int quad = round * kXcds + xcd;
+  const int quad = round * kXcds + ((round & 1) ? kXcds - 1 - xcd : xcd);
   if (quad >= a.num_seqs * quads_per_seq) return false;
   const int rank = quad / quads_per_seq;
   it.s = seq_by_work(a, rank);
