@@ -111,6 +111,15 @@ COUNTED = {
                     ("decode_mfma.hip", "decode_groups.h", "pa_device.h")],
         "bench": "python3 bench.py --workload gqa --decode-only --steps 3 --warmup 1",
         "dir": "pmc_gqa", "out": "gqa"},
+    # the long-prefix split prefill: the key-run launch (told apart from the
+    # unsplit comparison launch of the same kernel by its grid) and the merge
+    "prefill_long": {
+        "json": os.path.join(ROOT, "profiles", "prefill_long_counters.json"),
+        "kernel": [("void pa::prefill_x32_kernel<128, 4, true>", 122880),
+                   "void pa::prefill_merge_kernel<128, 128>"],
+        "sources": [os.path.join(_CSRC, f) for f in ("prefill.hip", "pa_device.h")],
+        "bench": "python3 bench.py --workload prefill_long --steps 3 --warmup 1 --no-cpu-baseline",
+        "dir": "pmc_pl", "out": "pl"},
     "copy": {
         "json": os.path.join(ROOT, "profiles", "copy_blocks_13b_counters.json"),
         "kernel": "void pa::move_blocks_kernel<unsigned int __vector(4), pa::DeviceMapping>",
@@ -296,11 +305,15 @@ def other_configs(args, torch, dev, lib):
     return out
 
 
-def _counter_rows(path: str, kernel_prefix: str):
+def _counter_rows(path: str, kernel):
+    """Counter values of the dispatches of `kernel`: a name prefix, or a
+    (name prefix, grid size in threads) pair."""
     import csv
+    prefix, grid = kernel if isinstance(kernel, tuple) else (kernel, None)
     with open(path) as f:
         return [float(r["Counter_Value"]) for r in csv.DictReader(f)
-                if r["Kernel_Name"].startswith(kernel_prefix)]
+                if r["Kernel_Name"].startswith(prefix)
+                and (grid is None or int(r["Grid_Size"]) == grid)]
 
 
 def digest_counters(kind: str, fetch_csv: str, write_csv: str, copy_fetch_csv: str,
@@ -328,7 +341,9 @@ def digest_counters(kind: str, fetch_csv: str, write_csv: str, copy_fetch_csv: s
     w_scale = copy_bytes / (w_copy * 1024)
     hbm = f_k * 1024 * f_scale + w_k * 1024 * w_scale
     d, o = spec["dir"], spec["out"]
-    out = {"kernel": k, "source_sha256_16": source_digest(kind),
+    out = {"kernel": k if isinstance(k, str) else
+           [x if isinstance(x, str) else f"{x[0]} (grid {x[1]})" for x in ks],
+           "source_sha256_16": source_digest(kind),
            "fetch_kib_per_launch": round(f_k, 1), "write_kib_per_launch": round(w_k, 1),
            "copy_bytes": copy_bytes, "copy_fetch_kib": round(f_copy, 1),
            "copy_write_kib": round(w_copy, 1), "fetch_scale": round(f_scale, 4),
@@ -765,7 +780,7 @@ def bench_prefill_long(args, torch, dev, lib, timer) -> int:
         "speedup_over_unsplit": round(ms["unsplit"] / ms["split"], 3),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic("prefill_long") if split == 5504 else None,
                      "kernel": f"prefill_x32_kernel<128,4> in runs of {split} keys + "
                                "prefill_merge_kernel (one pa_prefill_chunk_split call)",
                      "algorithmic_bytes_per_launch": int(kv_bytes),
