@@ -106,7 +106,7 @@ COUNTED = {
     # the GQA long-context batch on the matrix-core decode
     "decode_gqa": {
         "json": os.path.join(ROOT, "profiles", "decode_gqa_counters.json"),
-        "kernel": "void pa::decode_gqa_mfma_kernel<unsigned short, false, false>",
+        "kernel": "void pa::decode_gqa_mfma_kernel<unsigned short, false, false, true>",
         "sources": [os.path.join(_CSRC, f) for f in
                     ("decode_mfma.hip", "decode_groups.h", "pa_device.h")],
         "bench": "python3 bench.py --workload gqa --decode-only --steps 3 --warmup 1",

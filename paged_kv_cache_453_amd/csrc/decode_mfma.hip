@@ -19,7 +19,10 @@
 // state, and partitions meet in the split-K merge.  Single-wave workgroups
 // measured faster than workgroups of 2, 4 or 8 kv heads (476 / 495 / 503 /
 // 534 us on the Llama-3-8B-shaped batch, 254 / 274 / 284 / 295 us over an FP8
-// cache).
+// cache).  A split-K call with no grouped pass (and at most 64 sequences)
+// runs the same waves persistently instead: as many as stay resident walk the
+// ids and hold their partials in LDS until their walk is done (see the
+// kernel), 487 -> 449 us on that batch.
 //
 // Operand layouts (v_mfma_f32_16x16x32_bf16 for scores, v_mfma_f32_16x16x16_bf16
 // for p.V).  In both, lane l = 16 g + r supplies row/column r and reduction
@@ -59,6 +62,8 @@
 #include <type_traits>
 
 #include "decode_groups.h"
+#include <atomic>
+
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -253,18 +258,95 @@ __device__ __forceinline__ void consume_mfma_slab(MfmaSlab& sl, const u32x4 (&qb
 // KV: the cache element type (bf16, or fp8 codes).  HINT: the caller passed
 // shared_prefix_blocks, so batches of shared blocks take the caching load path;
 // without it only the streaming path is compiled.
-template <typename KV, bool HINT, bool GROUPED>
+template <typename KV, bool HINT, bool GROUPED, bool PERSIST>
 __global__ __launch_bounds__(64 * kHeadsPerWG) void decode_gqa_mfma_kernel(DecodeArgs a) {
+  static_assert(!(PERSIST && GROUPED), "persistent waves walk the regular pass only");
   __shared__ __attribute__((aligned(16))) uint8_t sh_k[kHeadsPerWG][kKTileBytes];
   const int hgroups = (a.num_kv_heads + kHeadsPerWG - 1) / kHeadsPerWG;
-  const int item = blockIdx.x / hgroups;
-  const int kvh = (blockIdx.x - item * hgroups) * kHeadsPerWG + wave_uniform(threadIdx.x >> 6);
+  // PERSIST (the regular pass of a split-K call without a grouped pass, at
+  // most 64 sequences): a grid of resident waves walks the (sequence,
+  // partition, kv head group) ids that have work, numbered densely --
+  // sequence by sequence, its partitions, its head groups -- and dealt to the
+  // waves in turn, so that every wave gets the same count.  Lane l holds
+  // sequence l's partition count and, after a scan, the partitions before it.
+  int cum_excl = 0;
+  int64_t total = 1;
+  if constexpr (PERSIST) {
+    const int l = threadIdx.x & (kWave - 1);
+    int np_l = 0;
+    if (l < a.num_items) {
+      const int ctx = a.context_lens[l];
+      const bool bad_l = ctx < 0 || ctx > a.max_blocks_per_seq * kBlock || ctx > a.max_context_len;
+      const int nb = bad_l ? 0 : (ctx + kBlock - 1) / kBlock;
+      np_l = max(1, (nb + a.partition_blocks - 1) / a.partition_blocks);
+    }
+    int c = np_l;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(c, o, kWave);
+      if (l >= o) c += y;
+    }
+    cum_excl = c - np_l;
+    total = (int64_t)__shfl(c, a.num_items - 1, kWave) * hgroups;
+  }
+  // A persistent wave keeps its ids' split-K partials in LDS (up to 4 ids) and
+  // writes them, whole rows per instruction, when its slots are full or its
+  // ids are done.  Written at the end of each id, the partials cost the K/V
+  // stream about 10% (21 MB among 2.8 GB at the GQA batch's 512-token
+  // partitions), far more than their bytes, however they were laid out;
+  // staged, most of them reach HBM after the stream.  Slot s holds the rows of
+  // query heads kvh * G + hr at part_o rows sh_meta[s] + hr * max_partitions.
+  constexpr int kStageFloats = PERSIST ? 2048 : 1;   // 8 KB per wave
+  __shared__ float sh_stage[kHeadsPerWG][kStageFloats];
+  __shared__ float sh_slse[kHeadsPerWG][PERSIST ? 64 : 1];
+  __shared__ int64_t sh_meta[kHeadsPerWG][PERSIST ? 16 : 1];
+  const int slot_floats = a.group * kD;
+  const int slots = PERSIST ? min(4, kStageFloats / slot_floats) : 0;   // 1..4 for groups 4..16
+  int used = 0;   // wave-uniform
+  const auto flush_all = [&]() {
+    if constexpr (PERSIST) {
+      const int fl = threadIdx.x & (kWave - 1);
+      const int wv = wave_uniform(threadIdx.x >> 6);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int sl = 0; sl < used; ++sl) {
+        const int64_t base = sh_meta[wv][sl];
+        const float* src = &sh_stage[wv][sl * slot_floats];
+        for (int idx = 4 * fl; idx < slot_floats; idx += 4 * kWave) {
+          const int64_t row = base + (int64_t)(idx / kD) * a.max_partitions;
+          *reinterpret_cast<f32x4*>(a.part_o + row * kD + idx % kD) =
+              *reinterpret_cast<const f32x4*>(src + idx);
+        }
+        if (fl < a.group)
+          a.part_lse[base + (int64_t)fl * a.max_partitions] = sh_slse[wv][sl * 16 + fl];
+      }
+      __builtin_amdgcn_wave_barrier();
+      used = 0;
+    }
+  };
+  for (int64_t v = PERSIST ? (int64_t)blockIdx.x : 0; v < total; v += PERSIST ? gridDim.x : 1) {
+  int item, by, hg;
+  if constexpr (PERSIST) {
+    const int t = (int)(v / hgroups);
+    hg = (int)(v - (int64_t)t * hgroups);
+    const int sl = threadIdx.x & (kWave - 1);
+    const uint64_t below = __ballot(sl < a.num_items && cum_excl <= t);
+    item = 63 - __builtin_clzll(below);
+    by = t - __shfl(cum_excl, item, kWave);
+  } else {
+    item = blockIdx.x / hgroups;
+    hg = blockIdx.x - item * hgroups;
+    by = blockIdx.y;
+  }
+  const int kvh = hg * kHeadsPerWG + wave_uniform(threadIdx.x >> 6);
   // the regular pass of a grouped call takes the partitions last first (its
   // leading ones are mostly grouped: their empty workgroups then fill the tail)
-  const int part = (!GROUPED && a.prefix_group != nullptr) ? gridDim.y - 1 - blockIdx.y
-                                                           : blockIdx.y;
-  if (kvh >= a.num_kv_heads) return;
-  const int lane = threadIdx.x & (kWave - 1);
+  const int part = (!GROUPED && !PERSIST && a.prefix_group != nullptr) ? gridDim.y - 1 - by : by;
+  if (kvh >= a.num_kv_heads) continue;
+  int tix = threadIdx.x;
+  if constexpr (PERSIST) __asm__ volatile("" : "+v"(tix));   // recomputed per id, not held
+  const int lane = tix & (kWave - 1);
   const int r = lane & 15;
   const int g = lane >> 4;
   const int G = a.group;
@@ -282,11 +364,11 @@ __global__ __launch_bounds__(64 * kHeadsPerWG) void decode_gqa_mfma_kernel(Decod
   if constexpr (GROUPED) {
     const int M = a.group_members;
     const int lead = a.prefix_group[item];
-    if (lead < 0 || lead > item || (item - lead) % M != 0) return;
+    if (lead < 0 || lead > item || (item - lead) % M != 0) continue;
     for (int m = 0; m < M && item + m < a.num_seqs; ++m)
       if (a.prefix_group[item + m] == lead && part < grouped_parts(a, item + m))
         active |= 1u << m;
-    if (active == 0) return;
+    if (active == 0) continue;
     jb = part * a.partition_blocks;
     je = jb + a.partition_blocks;
     tok_end = je * kBlock;
@@ -298,8 +380,8 @@ __global__ __launch_bounds__(64 * kHeadsPerWG) void decode_gqa_mfma_kernel(Decod
     const int nblk = bad ? 0 : (ctx + kBlock - 1) / kBlock;
     const bool split = a.partition_blocks > 0;
     nparts = split ? (nblk + a.partition_blocks - 1) / a.partition_blocks : 1;
-    if (part >= (nparts > 0 ? nparts : 1)) return;
-    if (part < grouped_parts(a, item)) return;   // the grouped pass wrote it
+    if (part >= (nparts > 0 ? nparts : 1)) continue;
+    if (part < grouped_parts(a, item)) continue;   // the grouped pass wrote it
 
     // Degenerate sequences (only partition 0 gets here): no context gives zeros,
     // a violated contract gives NaN, in the partials too if the merge will read
@@ -317,12 +399,12 @@ __global__ __launch_bounds__(64 * kHeadsPerWG) void decode_gqa_mfma_kernel(Decod
             a.part_o[row * kD + i % kD] = fill;
             if (i % kD == 0) a.part_lse[row] = fill;
           }
-          return;
+          continue;
         }
       }
       for (int i = lane; i < G * kD; i += kWave)
         out[((int64_t)item * hq + kvh * G) * kD + i] = f32_to_bf16(fill);
-      return;
+      continue;
     }
     jb = split ? part * a.partition_blocks : 0;
     je = split ? min(nblk, jb + a.partition_blocks) : nblk;
@@ -441,7 +523,10 @@ __global__ __launch_bounds__(64 * kHeadsPerWG) void decode_gqa_mfma_kernel(Decod
       np = (nb + a.partition_blocks - 1) / a.partition_blocks;
     }
   }
-  if (colseq < 0) return;
+  if constexpr (PERSIST) {
+    if (np > 1 && used >= slots) flush_all();
+  }
+  if (colseq >= 0) {
   float inv = 1.f / lsum;
   if constexpr (std::is_same<KV, fp8_t>::value) inv = a.v_scale / lsum;
   const int h = colh;
@@ -458,7 +543,8 @@ __global__ __launch_bounds__(64 * kHeadsPerWG) void decode_gqa_mfma_kernel(Decod
     }
   } else {
     const int64_t row = ((int64_t)colseq * hq + h) * a.max_partitions + part;
-    float* dst = a.part_o + row * kD;
+    float* dst = PERSIST ? &sh_stage[wave_uniform(threadIdx.x >> 6)][used * slot_floats + r * kD]
+                         : a.part_o + row * kD;
     const float nan = __builtin_nanf("");
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -471,8 +557,23 @@ __global__ __launch_bounds__(64 * kHeadsPerWG) void decode_gqa_mfma_kernel(Decod
       *reinterpret_cast<f32x4*>(dst + 8 * (4 * g + i)) = lo;
       *reinterpret_cast<f32x4*>(dst + 8 * (4 * g + i) + 4) = hi;
     }
-    if (g == 0) a.part_lse[row] = poisoned ? nan : (st.m + log2f(lsum)) * kLn2;
+    const float lse = poisoned ? nan : (st.m + log2f(lsum)) * kLn2;
+    if (g == 0) {
+      if constexpr (PERSIST) sh_slse[wave_uniform(threadIdx.x >> 6)][used * 16 + r] = lse;
+      else a.part_lse[row] = lse;
+    }
   }
+  }
+  if constexpr (PERSIST) {
+    if (np > 1) {
+      if ((threadIdx.x & (kWave - 1)) == 0)
+        sh_meta[wave_uniform(threadIdx.x >> 6)][used] =
+            ((int64_t)item * hq + kvh * G) * a.max_partitions + part;
+      ++used;
+    }
+  }
+  }
+  flush_all();
 }
 
 // Query columns of the products: a grouped-pass wave stacks the query heads
@@ -491,14 +592,54 @@ hipError_t launch_gqa_mfma(const DecodeArgs& a, hipStream_t stream) {
   if (b.group_members == 0) b.prefix_group = nullptr;
   if (b.prefix_group != nullptr) {
     if (b.partition_blocks <= 0 || b.shared_prefix_blocks == nullptr) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((decode_gqa_mfma_kernel<KV, false, true>), grid, block, 0, stream, b);
+    hipLaunchKernelGGL((decode_gqa_mfma_kernel<KV, false, true, false>), grid, block, 0, stream, b);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  // (bf16 caches: over FP8 codes the same walk measured slower, 257 -> 294 us
+  // on the GQA batch, and the launch stays one wave per id)
+  if constexpr (std::is_same<KV, bf16_t>::value) {
+    if (b.prefix_group == nullptr && b.partition_blocks > 0 && b.num_items <= kWave &&
+        b.group >= 4 && b.group <= 16) {
+      // split-K without a grouped pass: as many waves as stay resident walk
+      // the ids and keep their partials until their walk ends (the count comes
+      // from the occupancy the compiled kernel allows, once per device)
+      static std::atomic<int> resident_cache[2][64];
+      int dev = 0;
+      if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+      const int hint = b.shared_prefix_blocks != nullptr ? 1 : 0;
+      int resident = resident_cache[hint][dev].load(std::memory_order_relaxed);
+      if (resident <= 0) {
+        int per_cu = 0, cus = 0;
+        const hipError_t e1 = hint ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                                         &per_cu, decode_gqa_mfma_kernel<KV, true, false, true>,
+                                         64 * kHeadsPerWG, 0)
+                                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                                         &per_cu, decode_gqa_mfma_kernel<KV, false, false, true>,
+                                         64 * kHeadsPerWG, 0);
+        const hipError_t e2 =
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        const bool known = e1 == hipSuccess && e2 == hipSuccess && per_cu > 0 && cus > 0;
+        resident = known ? per_cu * cus : 2048;
+        resident = resident / 8 * 8;
+        if (resident < 8) resident = 8;
+        resident_cache[hint][dev].store(resident, std::memory_order_relaxed);
+      }
+      const int64_t ids = (int64_t)grid.x * grid.y;
+      const dim3 pgrid((unsigned)(ids < resident ? ids : resident));
+      if (hint)
+        hipLaunchKernelGGL((decode_gqa_mfma_kernel<KV, true, false, true>), pgrid, block, 0,
+                           stream, b);
+      else
+        hipLaunchKernelGGL((decode_gqa_mfma_kernel<KV, false, false, true>), pgrid, block, 0,
+                           stream, b);
+      return hipGetLastError();
+    }
+  }
   if (b.shared_prefix_blocks != nullptr)
-    hipLaunchKernelGGL((decode_gqa_mfma_kernel<KV, true, false>), grid, block, 0, stream, b);
+    hipLaunchKernelGGL((decode_gqa_mfma_kernel<KV, true, false, false>), grid, block, 0, stream, b);
   else
-    hipLaunchKernelGGL((decode_gqa_mfma_kernel<KV, false, false>), grid, block, 0, stream, b);
+    hipLaunchKernelGGL((decode_gqa_mfma_kernel<KV, false, false, false>), grid, block, 0, stream, b);
   return hipGetLastError();
 }
 
