@@ -7,7 +7,7 @@ lognormal context lengths with median 1024 clipped to [16, 4096], 65536-block
 shuffled pool) with split-K partitions and their merge.
 
 --workload selects the other shapes the hot path is measured on:
-  llama7b   decode of 64 sequences, 32 = 32 heads, lengths U[128, 2048], 512-token
+  llama7b   decode of 64 sequences, 32 = 32 heads, lengths U[128, 2048], 2048-token
             split-K partitions + merge
   gqa       decode of 32 sequences, 32 query heads over 8 kv heads, lengths
             U[8192, 32768], 512-token split-K partitions + merge
@@ -71,11 +71,12 @@ _CSRC = os.path.join(ROOT, "paged_kv_cache_453_amd", "csrc")
 # the kernel name prefix in the rocprofv3 CSVs, the sources the kernel is built
 # from, and the bench command the counter runs profiled
 _DECODE_SOURCES = [os.path.join(_CSRC, f) for f in
-                   ("decode_valu.h", "decode_groups.h", "decode_valu_bf16.hip", "pa_device.h")]
+                   ("decode_valu.h", "decode_groups.h", "decode_valu_bf16.hip", "pa_device.h",
+                    "decode.hip", "pa_launch.h")]
 COUNTED = {
     "decode": {
         "json": os.path.join(ROOT, "profiles", "decode_llama13b_counters.json"),
-        "kernel": "void pa::decode_valu_kernel<unsigned short, unsigned short, 128, 1, false, false>",
+        "kernel": "void pa::decode_valu_dealt_kernel<unsigned short, unsigned short, 128, 1>",
         "sources": _DECODE_SOURCES,
         "bench": "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
         "dir": "pmc", "out": "bench"},
@@ -99,7 +100,7 @@ COUNTED = {
     # the Llama-2-7B-shaped batch (the headline kernel, other lengths and partitions)
     "decode_7b": {
         "json": os.path.join(ROOT, "profiles", "decode_llama7b_counters.json"),
-        "kernel": "void pa::decode_valu_kernel<unsigned short, unsigned short, 128, 1, false, false>",
+        "kernel": "void pa::decode_valu_dealt_kernel<unsigned short, unsigned short, 128, 1>",
         "sources": _DECODE_SOURCES,
         "bench": "python3 bench.py --workload llama7b --decode-only --steps 3 --warmup 1",
         "dir": "pmc_7b", "out": "l7b"},
@@ -278,7 +279,7 @@ def other_configs(args, torch, dev, lib):
     the Llama-2-7B-shaped batch, the GQA long-context batch (512-token split-K
     partitions as configured) and the mixed prefill + decode step."""
     out = {}
-    for name, ps in (("llama7b", 512), ("gqa", 512), ("mixed", 2048)):
+    for name, ps in (("llama7b", 2048), ("gqa", 512), ("mixed", 2048)):
         r = bench_attention(args, torch, dev, lib, name, partition_size=ps, with_cpu=False)
         torch.cuda.empty_cache()
         rf = r["roofline"]
@@ -904,9 +905,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", choices=WORKLOADS, default="llama13b")
     ap.add_argument("--partition-size", type=int, default=None,
-                    help="split-K partition length in tokens (default: 2048 for llama13b "
-                         "and mixed, 512 for gqa as its configuration states and for llama7b, "
-                         "whose lengths of 128-2048 leave a long tail at 2048)")
+                    help="split-K partition length in tokens (default: 512 for gqa as its "
+                         "configuration states, 2048 for the others)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="default workload only: skip the Llama-2-7B, GQA and mixed "
@@ -989,7 +989,7 @@ def bench_attention(args, torch, dev, lib, name: str, partition_size=None, steps
     fp8 = name.endswith("_fp8")
     base = name[:-len("_fp8")] if fp8 else name
     if ps is None:
-        ps = 512 if base in ("gqa", "llama7b") else 2048
+        ps = 512 if base == "gqa" else 2048
 
     log(f"bench: generating the {name} workload")
     t0 = time.time()
@@ -1156,6 +1156,10 @@ def bench_attention(args, torch, dev, lib, name: str, partition_size=None, steps
     kv_name = "fp8" if fp8 else "bf16"
     dec_kernel = (f"decode_gqa_mfma_kernel<{kv_name}>" if group >= 4 else
                   f"decode_valu_kernel<bf16,{kv_name},{w.head_dim},{group}>")
+    if group <= 4 and ps > 0 and base in ("llama13b", "llama7b"):
+        # a plain split-K decode: the schedule launch, then the dealt kernel
+        dec_kernel = (f"decode_valu_dealt_kernel<bf16,{kv_name},{w.head_dim},{group}> "
+                      "(after decode_schedule_kernel, one pa_decode call)")
     if grouped and group >= 4:
         dec_kernel = (f"decode_gqa_mfma_kernel<{kv_name},grouped> + "
                       f"decode_gqa_mfma_kernel<{kv_name}> (one pa_decode_shared_prefix call)")

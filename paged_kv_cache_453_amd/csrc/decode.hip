@@ -81,6 +81,128 @@ __global__ __launch_bounds__(64 * kReduceWaves) void splitk_reduce_kernel(Reduce
   }
 }
 
+// Schedule of the dealt split-K decode (decode_valu_dealt_kernel).
+//
+// Order: the (sequence, partition) pairs that have a work unit, sorted by the
+// partition's length in blocks, longest first -- a counting sort in one
+// workgroup; lengths of kSchedBuckets - 1 blocks and more share the first
+// bucket, and pairs of equal length come in any order (the order decides which
+// workgroup computes a unit, never its result).  Listed are partition 0 of
+// every sequence (which writes the zeros or NaN of a sequence without context
+// or with a length outside the contract) and the further partitions of a
+// sequence within the contract.  Unit t is kv head t % num_kv_heads of pair
+// t / num_kv_heads.
+//
+// Deal: the launch hands workgroup b to XCD b % 8, and each XCD runs its own
+// workgroups in order of b.  With one unit per workgroup in plain order every
+// XCD gets an eighth of the work, but under a full read stream the
+// odd-numbered XCDs of this part take about 10% longer per block than the even
+// ones (per-workgroup timestamps, with the kv heads rotated across XCDs as
+// well), so the even ones finish early and idle.  Here every run of
+// kDealPeriod units gives kDealEven to each even XCD and kDealOdd to each odd
+// one, spread evenly over the run (largest remainder), and XCD x's j-th
+// workgroup (b = 8 j + x) takes its j-th unit.
+constexpr int kSchedThreads = 1024;
+constexpr int kSchedBuckets = kSchedThreads;
+
+// pos[x][k]: the position in a period of XCD x's k-th unit.
+struct XcdDeal {
+  int n[kXcds];
+  unsigned char pos[kXcds][kDealPeriod];
+};
+
+static_assert(kDealPeriod <= 256, "positions fit a byte");
+
+XcdDeal make_deal() {
+  XcdDeal d = {};
+  int cnt[kXcds] = {};
+  for (int x = 0; x < kXcds; ++x) d.n[x] = (x & 1) ? kDealOdd : kDealEven;
+  for (int p = 0; p < kDealPeriod; ++p) {
+    int best = 0, lead = 0;   // the XCD furthest behind its share after p + 1 units
+    for (int x = 0; x < kXcds; ++x) {
+      const int v = d.n[x] * (p + 1) - kDealPeriod * cnt[x];
+      if (x == 0 || v > lead) {
+        lead = v;
+        best = x;
+      }
+    }
+    d.pos[best][cnt[best]++] = (unsigned char)p;
+  }
+  return d;
+}
+
+__device__ __forceinline__ int sched_partitions(const DecodeArgs& a, int s, int& nblk) {
+  const int ctx = a.context_lens[s];
+  const bool bad = ctx < 0 || ctx > a.max_context_len || ctx > a.max_blocks_per_seq * kBlock;
+  nblk = bad ? 0 : (ctx + kBlock - 1) / kBlock;
+  const int np = (nblk + a.partition_blocks - 1) / a.partition_blocks;
+  return np > 1 ? np : 1;
+}
+
+__device__ __forceinline__ int sched_bucket(const DecodeArgs& a, int nblk, int p) {
+  const int len = min(nblk - p * a.partition_blocks, a.partition_blocks);
+  return kSchedBuckets - 1 - min(len, kSchedBuckets - 1);
+}
+
+__global__ __launch_bounds__(kSchedThreads) void decode_schedule_kernel(DecodeArgs a, XcdDeal d,
+                                                                        int blocks) {
+  __shared__ int slot[kSchedBuckets];
+  __shared__ int wave_total[kSchedThreads / kWave];
+  const int tid = threadIdx.x;
+  slot[tid] = 0;
+  __syncthreads();
+  for (int s = tid; s < a.num_seqs; s += kSchedThreads) {
+    int nblk;
+    const int np = sched_partitions(a, s, nblk);
+    for (int p = 0; p < np; ++p) atomicAdd(&slot[sched_bucket(a, nblk, p)], 1);
+  }
+  __syncthreads();
+  // exclusive prefix sum of the bucket counts: within each wave, then across
+  const int lane = tid & (kWave - 1);
+  const int w = tid / kWave;
+  const int count = slot[tid];
+  int incl = count;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
+  }
+  if (lane == kWave - 1) wave_total[w] = incl;
+  __syncthreads();
+  int before = 0, npairs = 0;
+  for (int x = 0; x < kSchedThreads / kWave; ++x) {
+    before += x < w ? wave_total[x] : 0;
+    npairs += wave_total[x];
+  }
+  slot[tid] = before + incl - count;   // first position of bucket tid
+  if (tid == 0) a.sched[kSchedPairs] = npairs;
+  __syncthreads();
+  int* const pairs = a.sched + kSchedHeader;
+  for (int s = tid; s < a.num_seqs; s += kSchedThreads) {
+    int nblk;
+    const int np = sched_partitions(a, s, nblk);
+    for (int p = 0; p < np; ++p)
+      pairs[atomicAdd(&slot[sched_bucket(a, nblk, p)], 1)] = s * a.max_partitions + p;
+  }
+  // the deal: workgroup b's unit, or -1 past the last
+  const int units = npairs * a.num_kv_heads;
+  int* const unit_of = pairs + a.num_seqs * a.max_partitions;
+  for (int b = tid; b < blocks; b += kSchedThreads) {
+    const int x = b % kXcds;
+    const int j = b / kXcds;
+    const int t = (j / d.n[x]) * kDealPeriod + d.pos[x][j % d.n[x]];
+    unit_of[b] = t < units ? t : -1;
+  }
+}
+
+hipError_t launch_decode_schedule(const DecodeArgs& a, hipStream_t stream) {
+  static const XcdDeal deal = make_deal();
+  const int64_t blocks = deal_blocks((int64_t)a.num_items * a.max_partitions * a.num_kv_heads);
+  hipLaunchKernelGGL(decode_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, a, deal,
+                     (int)blocks);
+  return hipGetLastError();
+}
+
 // Grouped-query decode with at least this many query heads per kv head runs on
 // the matrix cores (bf16, head_dim 128); smaller groups stay on the vector ALUs.
 constexpr int kMfmaMinGroup = 4;

@@ -21,7 +21,9 @@
 // per-token prefill path).  A partition is a run of consecutive blocks; the
 // waves of a workgroup take its blocks round-robin.  All query heads that share
 // the kv head (a GQA group) are handled by the same workgroup, so each K/V
-// block is read from HBM exactly once per step.
+// block is read from HBM exactly once per step.  A plain split-K decode takes
+// the same units from a schedule instead (decode_valu_dealt_kernel): longest
+// partitions first, dealt to the XCDs by how fast each drains them.
 //
 // Lane layout inside a wave for one 16-token block slab (16 x head_dim values,
 // contiguous in memory): every lane issues 16-byte loads; LPR = head_dim*elem/16
@@ -333,6 +335,20 @@ __device__ __forceinline__ bool locate_item(const DecodeArgs& a, int item, ItemI
   return true;
 }
 
+// LDS of one workgroup: each wave's merged state, for the merge of the waves.
+template <int GP, int D>
+struct ValuShared {
+  float acc[kWavesPerGroup][GP][D];
+  float m[kWavesPerGroup][GP];
+  float l[kWavesPerGroup][GP];
+  int bad[kWavesPerGroup];
+  uint32_t mismatch[kWavesPerGroup];
+};
+
+// One work unit: kv head kvh of item `item`, partition `part` (the whole
+// context without split-K).  Every thread of the workgroup calls it with the
+// same unit; it returns early, all threads together, for units without work.
+//
 // HINT: the caller passed shared_prefix_blocks, so batches of shared blocks
 // take the caching load path; without it only the streaming path is compiled.
 // GROUPED: the grouped pass.  Workgroup (s, kv head, partition) works only if
@@ -342,7 +358,9 @@ __device__ __forceinline__ bool locate_item(const DecodeArgs& a, int item, ItemI
 // kvh*G + g % G of member s + g / G, and a member whose table names other
 // blocks there gets NaN (it broke the grouping contract).
 template <typename T, typename KV, int D, int GP, bool HINT, bool GROUPED>
-__global__ __launch_bounds__(64 * kWavesPerGroup) void decode_valu_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_valu_unit(const DecodeArgs& a, const int item,
+                                                 const int kvh, const int part,
+                                                 ValuShared<GP, D>& sh) {
   constexpr int E = ElemTraits<KV>::kPerLoad;  // cache elements per 16-byte load
   constexpr int LPR = D / E;                   // lanes per token row
   constexpr int RPL = kWave / LPR;             // token rows per wave-wide load
@@ -351,23 +369,6 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_valu_kernel(Decode
   static_assert(LPR >= 2 && LPR <= 32 && NLD >= 1, "layout");
   static_assert(!GROUPED || (GP <= 32 && !HINT), "grouped pass");
 
-  __shared__ float sh_acc[NW][GP][D];
-  __shared__ float sh_m[NW][GP];
-  __shared__ float sh_l[NW][GP];
-  __shared__ int sh_bad[NW];
-  __shared__ uint32_t sh_mismatch[NW];
-
-  // blockIdx.x = item * num_kv_heads + kv head: workgroups launched together
-  // read the adjacent head slabs of the same physical blocks, which keeps the
-  // HBM accesses of concurrently running waves close together.
-  const int item = blockIdx.x / a.num_kv_heads;
-  const int kvh = blockIdx.x - item * a.num_kv_heads;
-  // The regular pass of a grouped call takes the partitions last first: its
-  // leading partitions are mostly the grouped ones it skips, and dispatched
-  // last their empty workgroups fill the launch's tail instead of holding
-  // slots the live ones need.  Otherwise the first (longest) partitions go first.
-  const int part = (!GROUPED && a.prefix_group != nullptr) ? gridDim.y - 1 - blockIdx.y
-                                                           : blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = wave_uniform(threadIdx.x >> 6);
   const int r = lane / LPR;
@@ -552,20 +553,20 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_valu_kernel(Decode
   }
   __syncthreads();
   if (lane == 0) {
-    sh_bad[w] = __builtin_amdgcn_readfirstlane((int)bad_block);
-    sh_mismatch[w] = mismatch;
+    sh.bad[w] = __builtin_amdgcn_readfirstlane((int)bad_block);
+    sh.mismatch[w] = mismatch;
   }
   if (r == 0) {
 #pragma unroll
     for (int g = 0; g < GP; ++g)
 #pragma unroll
-      for (int e = 0; e < E; ++e) sh_acc[w][g][c * E + e] = acc[g][e];
+      for (int e = 0; e < E; ++e) sh.acc[w][g][c * E + e] = acc[g][e];
   }
   if (lane == 0) {
 #pragma unroll
     for (int g = 0; g < GP; ++g) {
-      sh_m[w][g] = m[g];
-      sh_l[w][g] = l[g];
+      sh.m[w][g] = m[g];
+      sh.l[w][g] = l[g];
     }
   }
   __syncthreads();
@@ -575,8 +576,8 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_valu_kernel(Decode
   uint32_t mism = 0;
 #pragma unroll
   for (int x = 0; x < NW; ++x) {
-    poisoned |= sh_bad[x] != 0;
-    mism |= sh_mismatch[x];
+    poisoned |= sh.bad[x] != 0;
+    mism |= sh.mismatch[x];
   }
   const int nslots = GROUPED ? a.group_members * G : G;
   for (int i = threadIdx.x; i < nslots * D; i += blockDim.x) {
@@ -595,13 +596,13 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_valu_kernel(Decode
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int x = 0; x < NW; ++x) mx = fmaxf(mx, sh_m[x][g]);
+    for (int x = 0; x < NW; ++x) mx = fmaxf(mx, sh.m[x][g]);
     float lsum = 0.f, o = 0.f;
 #pragma unroll
     for (int x = 0; x < NW; ++x) {
-      const float f = (sh_m[x][g] == -INFINITY) ? 0.f : exp2f(sh_m[x][g] - mx);
-      lsum = fmaf(sh_l[x][g], f, lsum);
-      o = fmaf(sh_acc[x][g][d], f, o);
+      const float f = (sh.m[x][g] == -INFINITY) ? 0.f : exp2f(sh.m[x][g] - mx);
+      lsum = fmaf(sh.l[x][g], f, lsum);
+      o = fmaf(sh.acc[x][g][d], f, o);
     }
     o = bad ? __builtin_nanf("") : o / lsum;
     if constexpr (std::is_same<KV, fp8_t>::value) o *= a.v_scale;
@@ -613,6 +614,45 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_valu_kernel(Decode
       if (d == 0) a.part_lse[row] = bad ? __builtin_nanf("") : (mx + log2f(lsum)) * kLn2;
     }
   }
+}
+
+// One workgroup per unit.  blockIdx.x = item * num_kv_heads + kv head:
+// workgroups launched together read the adjacent head slabs of the same
+// physical blocks, which keeps the HBM accesses of concurrently running waves
+// close together.  The regular pass of a grouped call takes the partitions
+// last first: its leading partitions are mostly the grouped ones it skips, and
+// dispatched last their empty workgroups fill the launch's tail instead of
+// holding slots the live ones need.  Otherwise the first (longest) partitions
+// go first.
+template <typename T, typename KV, int D, int GP, bool HINT, bool GROUPED>
+__global__ __launch_bounds__(64 * kWavesPerGroup) void decode_valu_kernel(DecodeArgs a) {
+  __shared__ ValuShared<GP, D> sh;
+  const int item = blockIdx.x / a.num_kv_heads;
+  const int kvh = blockIdx.x - item * a.num_kv_heads;
+  const int part = (!GROUPED && a.prefix_group != nullptr) ? gridDim.y - 1 - blockIdx.y
+                                                           : blockIdx.y;
+  decode_valu_unit<T, KV, D, GP, HINT, GROUPED>(a, item, kvh, part, sh);
+}
+
+// Split-K decode over a dealt schedule: workgroup b takes the unit that
+// decode_schedule_kernel, launched just before, wrote for it (none: -1).  The
+// units are the (sequence, partition) pairs longest first, each followed by its
+// kv heads, so every XCD starts its long units first and ends on short ones,
+// and they are dealt to the XCDs in proportion to how fast each drains them
+// (see decode_deal in decode.hip): within an XCD the hardware hands the next
+// workgroup to the first free slot.
+template <typename T, typename KV, int D, int GP>
+__global__ __launch_bounds__(64 * kWavesPerGroup) void decode_valu_dealt_kernel(DecodeArgs a) {
+  __shared__ ValuShared<GP, D> sh;
+  const int* const pairs = a.sched + kSchedHeader;
+  const int t = pairs[(int64_t)a.num_items * a.max_partitions + blockIdx.x];
+  if (t < 0) return;
+  const int nkv = a.num_kv_heads;
+  const int u = t / nkv;
+  const int pair = pairs[u];
+  const int item = pair / a.max_partitions;
+  decode_valu_unit<T, KV, D, GP, false, false>(a, item, t - u * nkv,
+                                               pair - item * a.max_partitions, sh);
 }
 
 // Query heads per kv head the vector-ALU kernel takes for an FP8 cache: its
@@ -652,6 +692,23 @@ inline void launch_decode_grouped(const DecodeArgs& a, dim3 grid, hipStream_t st
     hipLaunchKernelGGL((decode_valu_kernel<T, KV, D, 4, false, true>), grid, block, 0, stream, a);
 }
 
+// The dealt split-K decode: decode_schedule_kernel, then one workgroup per
+// slot of the deal.
+template <typename T, typename KV, int D>
+inline hipError_t launch_decode_dealt(const DecodeArgs& a, hipStream_t stream) {
+  const hipError_t e = launch_decode_schedule(a, stream);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)deal_blocks((int64_t)a.num_items * a.max_partitions * a.num_kv_heads));
+  const dim3 block(64 * kWavesPerGroup);
+  if (a.group <= 1)
+    hipLaunchKernelGGL((decode_valu_dealt_kernel<T, KV, D, 1>), grid, block, 0, stream, a);
+  else if (a.group <= 2)
+    hipLaunchKernelGGL((decode_valu_dealt_kernel<T, KV, D, 2>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_valu_dealt_kernel<T, KV, D, 4>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
 template <typename T, typename KV, int D>
 inline hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   if (std::is_same<KV, fp8_t>::value && a.group > kFp8ValuMaxGroup) return hipErrorInvalidValue;
@@ -668,6 +725,13 @@ inline hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  // A plain split-K decode with up to four query heads per kv head runs over
+  // the dealt schedule (while its units stay well inside an int).
+  if (b.prefix_group == nullptr && b.shared_prefix_blocks == nullptr &&
+      b.query_start_loc == nullptr && b.partition_blocks > 0 && b.sched != nullptr &&
+      b.group <= 4 &&
+      (int64_t)b.num_items * b.max_partitions * b.num_kv_heads < (int64_t(1) << 30))
+    return launch_decode_dealt<T, KV, D>(b, stream);
   if (b.shared_prefix_blocks != nullptr)
     launch_decode_group<T, KV, D, true>(b, grid, stream);
   else

@@ -110,6 +110,7 @@ int decode_impl(void* out, const void* query, const void* key_cache, const void*
   const size_t rows = (size_t)num_seqs * num_heads * nparts;
   a.part_o = partition_size > 0 ? static_cast<float*>(workspace) : nullptr;
   a.part_lse = partition_size > 0 ? static_cast<float*>(workspace) + rows * head_dim : nullptr;
+  a.sched = partition_size > 0 ? reinterpret_cast<int*>(a.part_lse + rows) : nullptr;
   a.num_seqs = num_seqs;
   a.num_items = num_seqs;
   a.num_heads = num_heads;
@@ -236,9 +237,10 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int 
   if (partition_size <= 0 || num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 ||
       max_context_len < 0)
     return 0;
-  const size_t rows = (size_t)num_seqs * (size_t)num_heads *
-                      (size_t)max_partitions(max_context_len, partition_size);
-  return rows * (size_t)head_dim * sizeof(float) + rows * sizeof(float);
+  const size_t nparts = (size_t)max_partitions(max_context_len, partition_size);
+  const size_t rows = (size_t)num_seqs * (size_t)num_heads * nparts;
+  const size_t sched = (size_t)pa::sched_ints(num_seqs, (int64_t)nparts, num_heads);
+  return rows * (size_t)head_dim * sizeof(float) + rows * sizeof(float) + sched * sizeof(int);
 }
 
 int pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,

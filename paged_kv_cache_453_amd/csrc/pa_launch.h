@@ -45,6 +45,8 @@ struct DecodeArgs {
   int group_members;
   float* part_o;
   float* part_lse;
+  // Split-K decode only: the schedule of the dealt decode (null: none).
+  int* sched;
   int num_seqs;
   int num_items;          // grid z: sequences (decode) or query tokens (prefill)
   int num_heads;
@@ -59,6 +61,35 @@ struct DecodeArgs {
   float scale_log2;       // softmax scale * log2(e) (times the K scale for FP8 caches)
   float v_scale;          // FP8 caches: the V scale, applied to the output
 };
+
+// The split-K schedule of the dealt decode (decode_schedule_kernel), in ints:
+// the number of (sequence, partition) pairs with work; from kSchedHeader on,
+// num_seqs * max_partitions slots holding those pairs (sequence *
+// max_partitions + partition), longest partition first; then the unit of
+// every workgroup of the decode launch (-1: none).
+constexpr int kSchedPairs = 0;
+constexpr int kSchedHeader = 64;
+
+// The deal of units to XCDs: of every kDealPeriod consecutive units (in the
+// schedule's order), kDealEven go to each even-numbered XCD and kDealOdd to
+// each odd-numbered one.  Workgroup ids reach the XCDs round-robin (id % 8).
+constexpr int kXcds = 8;   // accelerator dies (XCDs): workgroup ids go to them round-robin
+constexpr int kDealEven = 17;
+constexpr int kDealOdd = 15;
+constexpr int kDealPeriod = 4 * (kDealEven + kDealOdd);
+
+// Workgroups of a dealt launch over `units` units: every XCD's slots for the
+// periods they span, at the larger share.
+inline int64_t deal_blocks(int64_t units) {
+  return kXcds * ((units + kDealPeriod - 1) / kDealPeriod) *
+         (kDealEven > kDealOdd ? kDealEven : kDealOdd);
+}
+
+// Ints of the schedule for num_seqs sequences, nparts partitions and at most
+// num_heads kv heads.
+inline int64_t sched_ints(int64_t num_seqs, int64_t nparts, int64_t num_heads) {
+  return kSchedHeader + num_seqs * nparts + deal_blocks(num_seqs * nparts * num_heads);
+}
 
 // Query slots (sharing members x query heads per kv head) of one grouped-pass
 // workgroup: its registers hold that many accumulators, and 4 keeps two waves
@@ -108,6 +139,8 @@ constexpr int kSwapPairsPerLaunch = 256;
 
 hipError_t launch_reshape_and_cache(const ScatterArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t stream);
+// Writes a.sched for the dealt split-K decode (one workgroup).
+hipError_t launch_decode_schedule(const DecodeArgs& a, hipStream_t stream);
 // pa_decode's scalar and pointer checks (no HIP call): PA_OK or the status pa_decode returns.
 int check_decode_args(const void* out, const void* query, const void* key_cache,
                       const void* value_cache, const int32_t* block_tables,

@@ -66,7 +66,6 @@ namespace pa {
 namespace {
 
 constexpr int kKeys = 64;             // keys per tile (4 blocks)
-constexpr int kXcds = 8;              // accelerator dies: workgroup ids go to them round-robin
 constexpr int kEngines = 4;           // shader engines per die: a die's workgroups go to them in turn
 constexpr int kBufferWord3 = 0x00020000;   // raw 32-bit buffer resource, no format conversion
 constexpr float kSlack = 8.f;         // base-2 headroom of the lazy rescale

@@ -65,5 +65,56 @@ def test_any_partition_length_gives_the_same_answer(gpu, ps):
 
 def test_workspace_size_formula(gpu):
     L = lib()
-    assert L.pa_decode_workspace_bytes(32, 32, 128, 32768, 512) == 32 * 32 * 64 * (128 + 1) * 4
+    sched = 64 + 32 * 64 + 8 * 17 * (32 * 32 * 64 // 128)   # header, pairs, dealt workgroups
+    assert L.pa_decode_workspace_bytes(32, 32, 128, 32768, 512) == 32 * 32 * 64 * (128 + 1) * 4 + sched * 4
     assert L.pa_decode_workspace_bytes(4, 8, 64, 100, 0) == 0
+
+
+def _decode_into(dw, ps, ws):
+    """pa_decode + merge of dw into its output, with the given workspace."""
+    import torch
+    L = lib()
+    g, w = dw.decode, dw.w
+    L.pa_decode(g.out, g.query, dw.k_cache, dw.v_cache, g.block_tables, g.context_lens, w.scale,
+                g.max_context_len, ps, ws)
+    L.pa_decode_splitk_reduce(g.out, ws, g.context_lens, g.max_context_len, ps)
+    torch.cuda.synchronize()
+
+
+def test_dealt_schedule_with_fewer_units_than_xcds(gpu):
+    """One sequence, one kv head, two 16-token partitions: two units for a launch
+    of eight XCDs' slots, so most workgroups find no unit and must do nothing."""
+    import torch
+    w = make_decode("deal2", 71, "f32", np.array([20]), 1, 1, 64, 8, with_scatter=False)
+    dw = to_device(w)
+    nbytes = lib().pa_decode_workspace_bytes(1, 1, 64, 20, 16)
+    ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    _decode_into(dw, 16, ws)
+    assert_close(as_f64(dw.decode.out), oracle_decode(w), "f32", "2 units")
+
+
+def test_dealt_schedule_long_partitions_then_smaller_batch(gpu):
+    """Partitions of 1100 blocks (past the length sort's last bucket, 1023 blocks)
+    over lengths from 1 to 40000 tokens, an empty sequence among them; then a
+    smaller batch through the same workspace, whose schedule is rewritten whole."""
+    import torch
+    ps = 1100 * 16
+    lens = np.array([40000, 2 * ps + 5, 0, 1, ps + 1, 30000, 16, 1234])
+    w = make_decode("deal_long", 72, "f32", lens, 4, 2, 64, 8192, with_scatter=False)
+    dw = to_device(w)
+    g = dw.decode
+    nbytes = lib().pa_decode_workspace_bytes(len(lens), 4, 64, g.max_context_len, ps)
+    ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    _decode_into(dw, ps, ws)
+    out = as_f64(g.out)
+    live = [i for i, n in enumerate(lens) if n > 0]
+    assert_close(out[live], oracle_decode(w, seqs=live), "f32", "long partitions")
+    assert (out[2] == 0).all()
+    say(f"long partitions: {len(live)} sequences within tolerance, the empty one zero")
+
+    small = make_decode("deal_small", 73, "f32", np.array([3000, 17, 17600]), 4, 2, 64, 2048,
+                        with_scatter=False)
+    ds = to_device(small)
+    assert lib().pa_decode_workspace_bytes(3, 4, 64, ds.decode.max_context_len, ps) <= nbytes
+    _decode_into(ds, ps, ws)
+    assert_close(as_f64(ds.decode.out), oracle_decode(small), "f32", "smaller batch, same workspace")
