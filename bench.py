@@ -76,7 +76,9 @@ _DECODE_SOURCES = [os.path.join(_CSRC, f) for f in
 COUNTED = {
     "decode": {
         "json": os.path.join(ROOT, "profiles", "decode_llama13b_counters.json"),
-        "kernel": "void pa::decode_valu_dealt_kernel<unsigned short, unsigned short, 128, 1>",
+        # told apart by its grid from the Llama-2-7B-shaped launch of the same kernel
+        "kernel": [("void pa::decode_valu_dealt_kernel<unsigned short, unsigned short, 128, 1>",
+                    5570560)],
         "sources": _DECODE_SOURCES,
         "bench": "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
         "dir": "pmc", "out": "bench"},
@@ -100,7 +102,8 @@ COUNTED = {
     # the Llama-2-7B-shaped batch (the headline kernel, other lengths and partitions)
     "decode_7b": {
         "json": os.path.join(ROOT, "profiles", "decode_llama7b_counters.json"),
-        "kernel": "void pa::decode_valu_dealt_kernel<unsigned short, unsigned short, 128, 1>",
+        "kernel": [("void pa::decode_valu_dealt_kernel<unsigned short, unsigned short, 128, 1>",
+                    557056)],
         "sources": _DECODE_SOURCES,
         "bench": "python3 bench.py --workload llama7b --decode-only --steps 3 --warmup 1",
         "dir": "pmc_7b", "out": "l7b"},

@@ -110,9 +110,9 @@ int pa_reshape_and_cache(const void* key, const void* value, void* key_cache, vo
  * with P = ceil(max_context_len / partition_size), o_part first, lse_part right
  * after it.  lse is the natural-log log-sum-exp of the partition's scaled scores;
  * o_part is that partition's normalised output.  After lse_part comes the
- * library's own schedule of the call's work units, 4 * (64 + num_seqs * P +
- * 136 * ceil(num_seqs * num_heads * P / 128)) bytes; pa_decode rewrites it
- * whole on every call and pa_decode_splitk_reduce does not read it.
+ * library's own schedule of the call's work units, 4 * (64 + num_seqs * P)
+ * bytes; pa_decode rewrites it on every call and pa_decode_splitk_reduce does
+ * not read it.
  */
 size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int max_context_len,
                                  int partition_size);

@@ -93,43 +93,19 @@ __global__ __launch_bounds__(64 * kReduceWaves) void splitk_reduce_kernel(Reduce
 // sequence within the contract.  Unit t is kv head t % num_kv_heads of pair
 // t / num_kv_heads.
 //
-// Deal: the launch hands workgroup b to XCD b % 8, and each XCD runs its own
-// workgroups in order of b.  With one unit per workgroup in plain order every
-// XCD gets an eighth of the work, but under a full read stream the
-// odd-numbered XCDs of this part take about 10% longer per block than the even
-// ones (per-workgroup timestamps, with the kv heads rotated across XCDs as
-// well), so the even ones finish early and idle.  Here every run of
-// kDealPeriod units gives kDealEven to each even XCD and kDealOdd to each odd
-// one, spread evenly over the run (largest remainder), and XCD x's j-th
-// workgroup (b = 8 j + x) takes its j-th unit.
+// The deal (dealt_unit): the launch hands workgroup b to XCD b % 8, and each
+// XCD runs its own workgroups in order of b.  With one unit per workgroup in
+// plain order every XCD gets an eighth of the work, but under a full read
+// stream the odd-numbered XCDs of this part take about 10% longer per block
+// than the even ones (per-workgroup timestamps, also with the kv heads
+// rotated across XCDs), so the even ones finish early and idle.  The deal gives
+// each even XCD 7 units of every 52 and each odd one 6: of the shares tried
+// (1 : 1, 17 : 15, 7 : 6, 17 : 14, 18 : 14) 7 : 6 and 17 : 14 drained the
+// Llama-2-13B-shaped batch fastest, about 4% ahead of one workgroup per unit in
+// plain order.
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedBuckets = kSchedThreads;
-
-// pos[x][k]: the position in a period of XCD x's k-th unit.
-struct XcdDeal {
-  int n[kXcds];
-  unsigned char pos[kXcds][kDealPeriod];
-};
-
-static_assert(kDealPeriod <= 256, "positions fit a byte");
-
-XcdDeal make_deal() {
-  XcdDeal d = {};
-  int cnt[kXcds] = {};
-  for (int x = 0; x < kXcds; ++x) d.n[x] = (x & 1) ? kDealOdd : kDealEven;
-  for (int p = 0; p < kDealPeriod; ++p) {
-    int best = 0, lead = 0;   // the XCD furthest behind its share after p + 1 units
-    for (int x = 0; x < kXcds; ++x) {
-      const int v = d.n[x] * (p + 1) - kDealPeriod * cnt[x];
-      if (x == 0 || v > lead) {
-        lead = v;
-        best = x;
-      }
-    }
-    d.pos[best][cnt[best]++] = (unsigned char)p;
-  }
-  return d;
-}
+constexpr int kSchedCached = 4096;   // sequences whose block counts stay in LDS between passes
 
 __device__ __forceinline__ int sched_partitions(const DecodeArgs& a, int s, int& nblk) {
   const int ctx = a.context_lens[s];
@@ -144,16 +120,17 @@ __device__ __forceinline__ int sched_bucket(const DecodeArgs& a, int nblk, int p
   return kSchedBuckets - 1 - min(len, kSchedBuckets - 1);
 }
 
-__global__ __launch_bounds__(kSchedThreads) void decode_schedule_kernel(DecodeArgs a, XcdDeal d,
-                                                                        int blocks) {
+__global__ __launch_bounds__(kSchedThreads) void decode_schedule_kernel(DecodeArgs a) {
   __shared__ int slot[kSchedBuckets];
   __shared__ int wave_total[kSchedThreads / kWave];
+  __shared__ int2 cached[kSchedCached];   // (partitions, blocks) of the first sequences
   const int tid = threadIdx.x;
   slot[tid] = 0;
   __syncthreads();
   for (int s = tid; s < a.num_seqs; s += kSchedThreads) {
     int nblk;
     const int np = sched_partitions(a, s, nblk);
+    if (s < kSchedCached) cached[s] = make_int2(np, nblk);
     for (int p = 0; p < np; ++p) atomicAdd(&slot[sched_bucket(a, nblk, p)], 1);
   }
   __syncthreads();
@@ -179,27 +156,20 @@ __global__ __launch_bounds__(kSchedThreads) void decode_schedule_kernel(DecodeAr
   __syncthreads();
   int* const pairs = a.sched + kSchedHeader;
   for (int s = tid; s < a.num_seqs; s += kSchedThreads) {
-    int nblk;
-    const int np = sched_partitions(a, s, nblk);
+    int nblk, np;
+    if (s < kSchedCached) {
+      np = cached[s].x;
+      nblk = cached[s].y;
+    } else {
+      np = sched_partitions(a, s, nblk);
+    }
     for (int p = 0; p < np; ++p)
       pairs[atomicAdd(&slot[sched_bucket(a, nblk, p)], 1)] = s * a.max_partitions + p;
-  }
-  // the deal: workgroup b's unit, or -1 past the last
-  const int units = npairs * a.num_kv_heads;
-  int* const unit_of = pairs + a.num_seqs * a.max_partitions;
-  for (int b = tid; b < blocks; b += kSchedThreads) {
-    const int x = b % kXcds;
-    const int j = b / kXcds;
-    const int t = (j / d.n[x]) * kDealPeriod + d.pos[x][j % d.n[x]];
-    unit_of[b] = t < units ? t : -1;
   }
 }
 
 hipError_t launch_decode_schedule(const DecodeArgs& a, hipStream_t stream) {
-  static const XcdDeal deal = make_deal();
-  const int64_t blocks = deal_blocks((int64_t)a.num_items * a.max_partitions * a.num_kv_heads);
-  hipLaunchKernelGGL(decode_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, a, deal,
-                     (int)blocks);
+  hipLaunchKernelGGL(decode_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, a);
   return hipGetLastError();
 }
 

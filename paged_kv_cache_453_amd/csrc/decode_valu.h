@@ -634,20 +634,20 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_valu_kernel(Decode
   decode_valu_unit<T, KV, D, GP, HINT, GROUPED>(a, item, kvh, part, sh);
 }
 
-// Split-K decode over a dealt schedule: workgroup b takes the unit that
-// decode_schedule_kernel, launched just before, wrote for it (none: -1).  The
-// units are the (sequence, partition) pairs longest first, each followed by its
-// kv heads, so every XCD starts its long units first and ends on short ones,
-// and they are dealt to the XCDs in proportion to how fast each drains them
-// (see decode_deal in decode.hip): within an XCD the hardware hands the next
-// workgroup to the first free slot.
+// Split-K decode over a dealt schedule.  The units are the (sequence,
+// partition) pairs that decode_schedule_kernel, launched just before, sorted
+// longest first, each followed by its kv heads; workgroup b takes unit
+// dealt_unit(b).  So every XCD starts on long units and ends on short ones,
+// and the even-numbered XCDs, which drain blocks faster, take more of them
+// (decode_schedule_kernel's notes give the measurements); within an XCD the
+// hardware hands the next workgroup to the first free slot.
 template <typename T, typename KV, int D, int GP>
 __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_valu_dealt_kernel(DecodeArgs a) {
   __shared__ ValuShared<GP, D> sh;
-  const int* const pairs = a.sched + kSchedHeader;
-  const int t = pairs[(int64_t)a.num_items * a.max_partitions + blockIdx.x];
-  if (t < 0) return;
   const int nkv = a.num_kv_heads;
+  const int t = dealt_unit(blockIdx.x);
+  if (t >= a.sched[kSchedPairs] * nkv) return;
+  const int* const pairs = a.sched + kSchedHeader;
   const int u = t / nkv;
   const int pair = pairs[u];
   const int item = pair / a.max_partitions;

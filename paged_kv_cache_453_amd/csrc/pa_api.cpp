@@ -239,7 +239,7 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int 
     return 0;
   const size_t nparts = (size_t)max_partitions(max_context_len, partition_size);
   const size_t rows = (size_t)num_seqs * (size_t)num_heads * nparts;
-  const size_t sched = (size_t)pa::sched_ints(num_seqs, (int64_t)nparts, num_heads);
+  const size_t sched = (size_t)pa::sched_ints(num_seqs, (int64_t)nparts);
   return rows * (size_t)head_dim * sizeof(float) + rows * sizeof(float) + sched * sizeof(int);
 }
 

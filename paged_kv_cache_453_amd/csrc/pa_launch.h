@@ -65,30 +65,39 @@ struct DecodeArgs {
 // The split-K schedule of the dealt decode (decode_schedule_kernel), in ints:
 // the number of (sequence, partition) pairs with work; from kSchedHeader on,
 // num_seqs * max_partitions slots holding those pairs (sequence *
-// max_partitions + partition), longest partition first; then the unit of
-// every workgroup of the decode launch (-1: none).
+// max_partitions + partition), longest partition first.
 constexpr int kSchedPairs = 0;
 constexpr int kSchedHeader = 64;
 
-// The deal of units to XCDs: of every kDealPeriod consecutive units (in the
-// schedule's order), kDealEven go to each even-numbered XCD and kDealOdd to
-// each odd-numbered one.  Workgroup ids reach the XCDs round-robin (id % 8).
-constexpr int kXcds = 8;   // accelerator dies (XCDs): workgroup ids go to them round-robin
-constexpr int kDealEven = 17;
-constexpr int kDealOdd = 15;
-constexpr int kDealPeriod = 4 * (kDealEven + kDealOdd);
-
-// Workgroups of a dealt launch over `units` units: every XCD's slots for the
-// periods they span, at the larger share.
-inline int64_t deal_blocks(int64_t units) {
-  return kXcds * ((units + kDealPeriod - 1) / kDealPeriod) *
-         (kDealEven > kDealOdd ? kDealEven : kDealOdd);
+inline int64_t sched_ints(int64_t num_seqs, int64_t nparts) {
+  return kSchedHeader + num_seqs * nparts;
 }
 
-// Ints of the schedule for num_seqs sequences, nparts partitions and at most
-// num_heads kv heads.
-inline int64_t sched_ints(int64_t num_seqs, int64_t nparts, int64_t num_heads) {
-  return kSchedHeader + num_seqs * nparts + deal_blocks(num_seqs * nparts * num_heads);
+// The deal of the dealt decode's units (in the schedule's order) to the XCDs:
+// every period of kDealPeriod units gives kDealRounds to each XCD in turn,
+// then kDealExtra more to each even-numbered one.  Workgroup ids reach the
+// XCDs round-robin (XCD b % 8), and each XCD runs its workgroups in order of
+// b / 8, so workgroup b takes XCD b % 8's (b / 8)-th unit.
+constexpr int kXcds = 8;   // accelerator dies (XCDs): workgroup ids go to them round-robin
+constexpr int kDealRounds = 6;
+constexpr int kDealExtra = 1;
+constexpr int kDealPeriod = kXcds * kDealRounds + (kXcds / 2) * kDealExtra;
+
+__host__ __device__ inline int dealt_unit(int b) {
+  const int x = b % kXcds;
+  const int j = b / kXcds;
+  const int n = (x & 1) ? kDealRounds : kDealRounds + kDealExtra;
+  const int q = j / n;
+  const int k = j - q * n;
+  const int p = k < kDealRounds ? k * kXcds + x
+                                : kXcds * kDealRounds + (k - kDealRounds) * (kXcds / 2) + x / 2;
+  return q * kDealPeriod + p;
+}
+
+// Workgroups of a dealt launch that covers `units` units: every XCD's slots
+// for the periods they span, at the larger share.
+inline int64_t deal_blocks(int64_t units) {
+  return kXcds * ((units + kDealPeriod - 1) / kDealPeriod) * (kDealRounds + kDealExtra);
 }
 
 // Query slots (sharing members x query heads per kv head) of one grouped-pass

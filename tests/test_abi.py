@@ -81,11 +81,10 @@ def test_decode_validation(lib):
 
 
 def test_workspace_bytes(lib):
-    # partials [S, Hq, P, D] and lse [S, Hq, P] in fp32, then the schedule: 64 ints,
-    # S * P pairs and one int per workgroup of the dealt launch (17 per XCD and
-    # 128-unit period over S * Hq * P units)
+    # partials [S, Hq, P, D] and lse [S, Hq, P] in fp32, then the schedule: 64 ints
+    # and S * P (sequence, partition) pairs
     def sched(S, P, H):
-        return 64 + S * P + 8 * 17 * -(-(S * P * H) // 128)
+        return 64 + S * P
     assert lib.pa_decode_workspace_bytes(32, 32, 128, 32768, 512) == 32 * 32 * 64 * 129 * 4 + sched(32, 64, 32) * 4
     assert lib.pa_decode_workspace_bytes(2, 2, 64, 17, 16) == 2 * 2 * 2 * 65 * 4 + sched(2, 2, 2) * 4
     assert lib.pa_decode_workspace_bytes(2, 2, 64, 17, 0) == 0

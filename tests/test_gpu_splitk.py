@@ -65,7 +65,7 @@ def test_any_partition_length_gives_the_same_answer(gpu, ps):
 
 def test_workspace_size_formula(gpu):
     L = lib()
-    sched = 64 + 32 * 64 + 8 * 17 * (32 * 32 * 64 // 128)   # header, pairs, dealt workgroups
+    sched = 64 + 32 * 64   # the schedule: header and (sequence, partition) pairs
     assert L.pa_decode_workspace_bytes(32, 32, 128, 32768, 512) == 32 * 32 * 64 * (128 + 1) * 4 + sched * 4
     assert L.pa_decode_workspace_bytes(4, 8, 64, 100, 0) == 0
 
