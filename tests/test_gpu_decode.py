@@ -121,11 +121,12 @@ def test_shared_prefix_bitwise_identical_to_private_copies(gpu):
     assert_close(as_f64(a), oracle_decode(w), "bf16", "shared prefix decode")
 
 
+@pytest.mark.parametrize("ps", [0, 16])   # 16: the split-K call, over the dealt schedule
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_single_token_context_returns_v_exactly(gpu, dtype):
+def test_single_token_context_returns_v_exactly(gpu, dtype, ps):
     import torch
     w = make_decode("one", 3, dtype, np.array([1, 1, 1]), 4, 2, 128, 8, with_scatter=False)
-    dw = run(w)
+    dw = run(w, ps)
     for s in range(3):
         blk = int(w.decode.block_tables[s, 0])
         for h in range(4):
