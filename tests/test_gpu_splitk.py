@@ -118,3 +118,22 @@ def test_dealt_schedule_long_partitions_then_smaller_batch(gpu):
     assert lib().pa_decode_workspace_bytes(3, 4, 64, ds.decode.max_context_len, ps) <= nbytes
     _decode_into(ds, ps, ws)
     assert_close(as_f64(ds.decode.out), oracle_decode(small), "f32", "smaller batch, same workspace")
+
+
+def test_dealt_schedule_with_many_sequences(gpu):
+    """5000 sequences of 0-40 tokens in 16-token partitions: the schedule's
+    threads take several sequences each, and those past the first 4096 are
+    re-read rather than cached in LDS between its two passes."""
+    import torch
+    rng = np.random.default_rng(74)
+    lens = rng.integers(0, 41, size=5000)
+    w = make_decode("deal_many", 74, "f32", lens, 2, 1, 64, 16384, with_scatter=False)
+    dw = to_device(w)
+    g = dw.decode
+    nbytes = lib().pa_decode_workspace_bytes(len(lens), 2, 64, g.max_context_len, 16)
+    ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    _decode_into(dw, 16, ws)
+    out = as_f64(g.out)
+    live = np.nonzero(lens > 0)[0]
+    assert_close(out[live], oracle_decode(w, seqs=live), "f32", "5000 sequences")
+    assert (out[lens == 0] == 0).all()
